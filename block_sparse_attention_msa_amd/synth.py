@@ -1,0 +1,318 @@
+"""Seeded synthetic inputs for the MSA decode path.
+
+This module only *makes* inputs: random tensors, the quantisers that pack them
+into the stored formats, and the paged layout.  It contains none of the
+method's arithmetic (no decoding, scoring, pooling, selection or attention),
+so both the HIP path and the CPU oracle can consume its bytes without sharing
+any of the computation under test.
+
+Stored formats (the layouts the library reads):
+  q      bf16  [rows][Hq][128]          rows = num_seqs * q_len, request-major
+  iq     bf16  [rows][Hkv][128]         one index query per GQA group
+  idx_k  FP8 E4M3 (uint8) or bf16  [P][128 tokens][128]
+  k, v   NVFP4: uint8 [P][Hkv][128 tokens][64]   (element 2i in the low nibble)
+         + E4M3 scales uint8 [P][Hkv][128 tokens][8]  (one per 16 elements)
+         + one fp32 tensor scale each;
+         bf16: [P][Hkv][128 tokens][128]
+  block_table int32 [num_seqs][max_blocks_per_seq]; seq_lens int32 [num_seqs]
+
+NVFP4 quantiser (harness only; results do not depend on it because both sides
+decode the stored bytes): tensor scale gs = amax / (6 * 448); per group of 16,
+s = E4M3(amax16 / (6 * gs)) round-to-nearest-even; code = the E2M1 value
+nearest to x / (s * gs), ties to even, saturating at +-6.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+BLOCK = 128
+DIM = 128
+E4M3_MAX = 448.0
+# E2M1 magnitude grid, code index == magnitude code (OCP FP4)
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) & 0x7FFFFFFFFFFFFFFF)
+    return g
+
+
+def quant_e4m3(x: torch.Tensor) -> torch.Tensor:
+    """float -> OCP E4M3 bytes, round-to-nearest-even; clamps to +-448 first
+    because torch turns out-of-range values into NaN instead of saturating."""
+    return x.float().clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def quant_e2m1_codes(y: torch.Tensor) -> torch.Tensor:
+    """float (already divided by its scale) -> 4-bit E2M1 codes (uint8, one per
+    element), nearest value with ties to the even code, saturating at +-6."""
+    mids = torch.tensor(_E2M1_MIDS, device=y.device, dtype=torch.float32)
+    a = y.abs().float().clamp(max=6.0)
+    idx = torch.bucketize(a, mids, right=False)  # mids[idx-1] < a <= mids[idx]
+    # a tie sits exactly on mids[idx]; bucketize put it low, which is right when
+    # the lower neighbour has the even code (idx even) and wrong otherwise.
+    on_mid = (idx < len(_E2M1_MIDS)) & (a == mids[idx.clamp(max=len(_E2M1_MIDS) - 1)])
+    idx = idx + (on_mid & (idx % 2 == 1)).to(idx.dtype)
+    sign = ((y < 0) & (idx > 0)).to(torch.uint8)
+    return (sign << 3) | idx.to(torch.uint8)
+
+
+def nvfp4_tensor_scale(amax: float) -> float:
+    return float(amax) / (6.0 * E4M3_MAX) if amax > 0 else 1.0
+
+
+def quant_nvfp4(x: torch.Tensor, gs: float):
+    """x [..., 128] float -> (packed uint8 [..., 64], scales uint8 [..., 8])."""
+    shp = x.shape
+    xg = x.float().reshape(*shp[:-1], DIM // 16, 16)
+    amax16 = xg.abs().amax(dim=-1)
+    sc = quant_e4m3(amax16 / (6.0 * gs))                       # [..., 8] bytes
+    sc_val = sc.view(torch.float8_e4m3fn).float()              # exact decode of the stored scale
+    denom = (sc_val * gs).unsqueeze(-1)
+    y = torch.where(denom > 0, xg / torch.where(denom > 0, denom, torch.ones_like(denom)), torch.zeros_like(xg))
+    codes = quant_e2m1_codes(y).reshape(*shp[:-1], DIM)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), sc.contiguous()
+
+
+@dataclass
+class Workload:
+    """One batch of synthetic inputs, resident on `device`."""
+    name: str
+    num_seqs: int
+    q_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    max_blocks_per_seq: int
+    num_pages: int
+    kv_dtype: str            # "bf16" | "nvfp4"
+    idx_dtype: str           # "bf16" | "fp8"
+    sm_scale: float
+    k_scale: float
+    v_scale: float
+    idx_scale: float
+    q: torch.Tensor
+    iq: torch.Tensor
+    idx_k: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    k_sf: Optional[torch.Tensor]
+    v_sf: Optional[torch.Tensor]
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return self.num_seqs * self.q_len
+
+    def host_arrays(self) -> dict:
+        """numpy copies of exactly the bytes the device path reads."""
+        def u16(t):
+            return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+        def raw(t):
+            if t is None:
+                return None
+            if t.dtype == torch.bfloat16:
+                return u16(t)
+            return t.detach().contiguous().cpu().numpy()
+
+        return dict(q=u16(self.q), iq=u16(self.iq), idx_k=raw(self.idx_k), k=raw(self.k), v=raw(self.v),
+                    k_sf=raw(self.k_sf), v_sf=raw(self.v_sf),
+                    block_table=self.block_table.cpu().numpy().astype(np.int32),
+                    seq_lens=self.seq_lens.cpu().numpy().astype(np.int32))
+
+    def nbytes_algorithmic(self) -> dict:
+        """Bytes the method must move per layer-step (decode, q_len == 1):
+        every visible token's index key, K+V of the selected tokens only,
+        the used block-table entries, q, iq and the fp32 output."""
+        lens = [int(x) for x in self.seq_lens.cpu().tolist()]
+        b_idx = DIM * (1 if self.idx_dtype == "fp8" else 2)
+        b_kv_tok = DIM * (0.5 + 1.0 / 16) if self.kv_dtype == "nvfp4" else DIM * 2.0
+        scan = sum(lens) * b_idx
+        gather = 0.0
+        table = 0
+        for L in lens:
+            if L <= 0:
+                continue
+            nb = (L - 1) // BLOCK + 1
+            kept = min(nb, 16)
+            gather += self.num_kv_heads * kept * BLOCK * b_kv_tok * 2   # K and V
+            table += nb * 4
+        qio = self.rows * (self.num_q_heads + self.num_kv_heads) * DIM * 2
+        out = self.rows * self.num_q_heads * DIM * 4
+        return dict(scan=scan, gather=gather, table=table, q_iq=qio, out=out,
+                    total=scan + gather + table + qio + out)
+
+
+def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: str = "nvfp4",
+                  idx_dtype: str = "fp8", max_blocks_per_seq: Optional[int] = None, layout: str = "identity",
+                  spare_pages: int = 0, plant: int = 0, zipf: Optional[float] = None, zipf_amp: float = 4.0,
+                  idx_dist: str = "normal", shared_bias_iq: bool = False, seed: int = 0,
+                  device="cpu", num_q_heads: int = 16, num_kv_heads: int = 4,
+                  sm_scale: Optional[float] = None, idx_scale: float = 1.0,
+                  kv_chunk_pages: int = 1024) -> Workload:
+    """Seeded synthetic workload.
+
+    seq_lens: visible tokens per sequence (including the q_len new tokens);
+    0 marks a padded row.  layout "identity" gives sequence b the consecutive
+    pages of its blocks; "paged" scatters all pages through the pool with one
+    random permutation (the block table is then a random int32 map).
+    plant n: for each (sequence, group), n distinct non-recent blocks get
+    2.0 * (unit index-query direction) added to every index key.
+    zipf s: for each (sequence, group) a random permutation ranks the
+    non-recent blocks 1..nb-1 and block of rank k gets zipf_amp * k^-s times the
+    unit direction added.  idx_dist: "normal" N(0,1) or "uniform" U(-1,1).
+    shared_bias_iq: (q_len > 1) index queries are u_{b,g} + N(0,1), with u the
+    bias direction shared by the chunk.
+    Index-key rows past a sequence's end are filled with a poison value that
+    scores high, so an unmasked tail would show up in the selection.
+    """
+    dev = torch.device(device)
+    seq_lens = [int(x) for x in seq_lens]
+    S = len(seq_lens)
+    G, Hq = num_kv_heads, num_q_heads
+    nbs = [((L - 1) // BLOCK + 1) if L > 0 else 0 for L in seq_lens]
+    mbps = max_blocks_per_seq if max_blocks_per_seq is not None else max([1] + nbs)
+    assert all(nb <= mbps for nb in nbs)
+    assert all(L == 0 or L >= q_len for L in seq_lens)
+    P = sum(nbs) + spare_pages
+    P = max(P, 1)
+    rows = S * q_len
+
+    # ---- page map
+    perm = torch.arange(P, dtype=torch.int64)
+    if layout == "paged":
+        perm = torch.randperm(P, generator=_gen("cpu", seed * 7919 + 1))
+    elif layout != "identity":
+        raise ValueError(layout)
+    bt = torch.zeros(S, mbps, dtype=torch.int32)
+    off = 0
+    for b, nb in enumerate(nbs):
+        bt[b, :nb] = perm[off:off + nb].to(torch.int32)
+        off += nb
+
+    # ---- queries
+    gq = _gen(dev, seed * 7919 + 2)
+    q = torch.randn(rows, Hq, DIM, generator=gq, device=dev).to(torch.bfloat16)
+    if shared_bias_iq:
+        u = torch.randn(S, 1, G, DIM, generator=gq, device=dev)
+        iqf = u + torch.randn(S, q_len, G, DIM, generator=gq, device=dev)
+        iq = iqf.reshape(rows, G, DIM).to(torch.bfloat16)
+        direction = (u[:, 0] / u[:, 0].norm(dim=-1, keepdim=True))            # [S][G][D]
+    else:
+        iq = torch.randn(rows, G, DIM, generator=gq, device=dev).to(torch.bfloat16)
+        iq_last = iq.view(S, q_len, G, DIM)[:, -1].float().double()
+        direction = (iq_last / iq_last.norm(dim=-1, keepdim=True)).float()     # [S][G][D]
+
+    # ---- index keys, per sequence in logical order, scattered to pages
+    bidx = 1 if idx_dtype == "fp8" else 2
+    idx_pool = torch.zeros(P, BLOCK, DIM * bidx, dtype=torch.uint8, device=dev)
+    gi = _gen(dev, seed * 7919 + 3)
+    gsel = _gen("cpu", seed * 7919 + 4)
+    planted = {}
+    for b in range(S):
+        nb, L = nbs[b], seq_lens[b]
+        if nb == 0:
+            continue
+        if idx_dist == "normal":
+            keys = torch.randn(nb, BLOCK, DIM, generator=gi, device=dev)
+        elif idx_dist == "uniform":
+            keys = torch.rand(nb, BLOCK, DIM, generator=gi, device=dev) * 2.0 - 1.0
+        else:
+            raise ValueError(idx_dist)
+        r_last = nb - 1
+        bias = torch.zeros(nb, DIM, device=dev)
+        for g in range(G):
+            dvec = direction[b, g].to(dev)
+            if plant and r_last > 0:
+                n = min(plant, r_last)
+                picks = torch.randperm(r_last, generator=gsel)[:n]
+                planted[(b, g)] = sorted(int(x) for x in picks)
+                bias[picks.to(dev)] += 2.0 * dvec
+            if zipf is not None and r_last > 0:
+                ranks = torch.randperm(r_last, generator=gsel).to(torch.float64) + 1.0  # block j -> rank
+                w = (zipf_amp * ranks.pow(-zipf)).to(torch.float32).to(dev)
+                bias[:r_last] += w[:, None] * dvec[None, :]
+        keys += bias[:, None, :]
+        tail = L - (nb - 1) * BLOCK
+        if tail < BLOCK:
+            keys[nb - 1, tail:] = 3.0 * direction[b].sum(dim=0).to(dev)  # poison past the end
+        if idx_dtype == "fp8":
+            kb = quant_e4m3(keys)
+        else:
+            kb = keys.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(nb, BLOCK, DIM * 2)
+        idx_pool[bt[b, :nb].long().to(dev)] = kb
+    if idx_dtype == "bf16":
+        idx_pool = idx_pool.view(torch.bfloat16).reshape(P, BLOCK, DIM)
+
+    # ---- K / V pools (i.i.d. N(0,1), generated page-chunk by page-chunk)
+    def kv_pool(seed_k):
+        if kv_dtype == "bf16":
+            gk = _gen(dev, seed_k)
+            out = torch.empty(P, G, BLOCK, DIM, dtype=torch.bfloat16, device=dev)
+            for c0 in range(0, P, kv_chunk_pages):
+                c1 = min(P, c0 + kv_chunk_pages)
+                out[c0:c1] = torch.randn(c1 - c0, G, BLOCK, DIM, generator=gk, device=dev).to(torch.bfloat16)
+            return out, None, 1.0
+        # pass 1: amax, pass 2: quantise the same stream
+        amax = 0.0
+        gk = _gen(dev, seed_k)
+        for c0 in range(0, P, kv_chunk_pages):
+            c1 = min(P, c0 + kv_chunk_pages)
+            amax = max(amax, float(torch.randn(c1 - c0, G, BLOCK, DIM, generator=gk, device=dev).abs().max()))
+        gs = nvfp4_tensor_scale(amax)
+        packed = torch.empty(P, G, BLOCK, DIM // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(P, G, BLOCK, DIM // 16, dtype=torch.uint8, device=dev)
+        gk = _gen(dev, seed_k)
+        for c0 in range(0, P, kv_chunk_pages):
+            c1 = min(P, c0 + kv_chunk_pages)
+            x = torch.randn(c1 - c0, G, BLOCK, DIM, generator=gk, device=dev)
+            packed[c0:c1], scales[c0:c1] = quant_nvfp4(x, gs)
+        return packed, scales, gs
+
+    k, k_sf, k_scale = kv_pool(seed * 7919 + 5)
+    v, v_sf, v_scale = kv_pool(seed * 7919 + 6)
+
+    return Workload(name=name, num_seqs=S, q_len=q_len, num_q_heads=Hq, num_kv_heads=G,
+                    max_blocks_per_seq=mbps, num_pages=P, kv_dtype=kv_dtype, idx_dtype=idx_dtype,
+                    sm_scale=sm_scale if sm_scale is not None else 1.0 / math.sqrt(DIM),
+                    k_scale=float(k_scale), v_scale=float(v_scale), idx_scale=float(idx_scale),
+                    q=q, iq=iq, idx_k=idx_pool, k=k, v=v, k_sf=k_sf, v_sf=v_sf,
+                    block_table=bt.to(dev), seq_lens=torch.tensor(seq_lens, dtype=torch.int32, device=dev),
+                    meta=dict(seed=seed, layout=layout, plant=plant, zipf=zipf, idx_dist=idx_dist,
+                              planted=planted))
+
+
+# The five workloads the method is evaluated on.  Every config uses 4 KV heads
+# (= 4 GQA groups = 4 index queries per token), 16 query heads, head and index
+# dim 128 and 128-token blocks.
+CONFIGS = {
+    # batch 1, 4,096 tokens, everything bf16, 3 planted blocks per group
+    "tiny_b1_4k_bf16": dict(seq_lens=[4096], kv_dtype="bf16", idx_dtype="bf16", plant=3,
+                            layout="identity", seed=0),
+    # batch 8, 32K tokens, NVFP4 K/V, FP8 index keys, 6 planted blocks per group
+    "decode_b8_32k": dict(seq_lens=[32768] * 8, plant=6, layout="identity", seed=1),
+    # batch 32, 128K tokens each, paged pool with a random block table,
+    # Zipf(1.1) block-score bias
+    "paged_b32_128k": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", seed=2),
+    # batch 4, 512K tokens, U(-1,1) index keys, 8 planted blocks per group, paged
+    "paged_b4_512k": dict(seq_lens=[524288] * 4, idx_dist="uniform", plant=8, layout="paged", seed=3),
+    # batch 2 x 256 new query tokens appended causally to a 128K paged context
+    "verify_b2_q256_128k": dict(seq_lens=[131072 + 256] * 2, q_len=256, zipf=1.1, layout="paged",
+                                shared_bias_iq=True, seed=4),
+}
+
+
+def make_config(name: str, device="cpu", **over) -> Workload:
+    kw = dict(CONFIGS[name])
+    kw.update(over)
+    return make_workload(name=name, device=device, **kw)
