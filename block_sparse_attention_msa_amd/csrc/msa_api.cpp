@@ -1,0 +1,242 @@
+// msa_api.cpp - C ABI of the MSA decode path: host-side validation, workspace
+// layout and launch orchestration.  Every argument is checked before the first
+// HIP call, so invalid calls return without touching the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/msa.h"
+#include "msa_kernels.hpp"
+
+static_assert(MSA_MAX_BLOCKS_PER_SEQ == msa::kMaxBlocksPerSeq, "block limit mismatch");
+static_assert(MSA_BLOCK_SIZE == msa::kBlock && MSA_HEAD_DIM == msa::kDim && MSA_INDEX_DIM == msa::kDim,
+              "geometry mismatch");
+static_assert(MSA_TOPK == msa::kTopK && MSA_NUM_KV_HEADS == msa::kGroups &&
+                  MSA_NUM_Q_HEADS == msa::kGroups * msa::kHeadsPerGroup,
+              "head geometry mismatch");
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+msa_status fail(msa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+msa_status ok() {
+  g_last_error[0] = '\0';
+  return MSA_OK;
+}
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.f; }
+
+msa_status check_shape(const msa_shape* s) {
+  if (!s) return fail(MSA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->num_seqs < 0) return fail(MSA_ERR_INVALID_ARGUMENT, "num_seqs = %d < 0", s->num_seqs);
+  if (s->q_len < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "q_len = %d < 1", s->q_len);
+  if (s->num_kv_heads != MSA_NUM_KV_HEADS)
+    return fail(MSA_ERR_UNSUPPORTED, "num_kv_heads = %d (only %d supported)", s->num_kv_heads, MSA_NUM_KV_HEADS);
+  if (s->num_q_heads != MSA_NUM_Q_HEADS)
+    return fail(MSA_ERR_UNSUPPORTED, "num_q_heads = %d (only %d supported)", s->num_q_heads, MSA_NUM_Q_HEADS);
+  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > MSA_MAX_BLOCKS_PER_SEQ)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq = %d outside [1, %d]", s->max_blocks_per_seq,
+                MSA_MAX_BLOCKS_PER_SEQ);
+  if (s->num_pages < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages = %d < 1", s->num_pages);
+  if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_NVFP4)
+    return fail(MSA_ERR_UNSUPPORTED, "kv_dtype = %d", s->kv_dtype);
+  if (s->idx_dtype != MSA_IDX_BF16 && s->idx_dtype != MSA_IDX_FP8_E4M3)
+    return fail(MSA_ERR_UNSUPPORTED, "idx_dtype = %d", s->idx_dtype);
+  if (!finite_pos(s->sm_scale) || !finite_pos(s->k_scale) || !finite_pos(s->v_scale) || !finite_pos(s->idx_scale))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "scales must be finite and > 0 (sm %g, k %g, v %g, idx %g)",
+                (double)s->sm_scale, (double)s->k_scale, (double)s->v_scale, (double)s->idx_scale);
+  if ((long long)s->q_len > (long long)s->max_blocks_per_seq * MSA_BLOCK_SIZE)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "q_len = %d exceeds the sequence capacity", s->q_len);
+  if ((long long)s->num_seqs * s->q_len > 65535)
+    return fail(MSA_ERR_UNSUPPORTED, "num_seqs * q_len = %lld rows > 65535", (long long)s->num_seqs * s->q_len);
+  return MSA_OK;
+}
+
+msa_status check_cache(const msa_shape* s, const msa_cache* c, bool need_idx, bool need_kv) {
+  if (!c) return fail(MSA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!c->block_table || !c->seq_lens) return fail(MSA_ERR_INVALID_ARGUMENT, "block_table / seq_lens is NULL");
+  if (need_idx && !c->idx_k) return fail(MSA_ERR_INVALID_ARGUMENT, "idx_k is NULL");
+  if (need_kv) {
+    if (!c->k || !c->v) return fail(MSA_ERR_INVALID_ARGUMENT, "k / v is NULL");
+    if (s->kv_dtype == MSA_KV_NVFP4 && (!c->k_sf || !c->v_sf))
+      return fail(MSA_ERR_INVALID_ARGUMENT, "k_sf / v_sf is NULL for NVFP4 K/V");
+  }
+  return MSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t rows_of(const msa_shape* s) { return (size_t)s->num_seqs * (size_t)s->q_len; }
+size_t scores_bytes(const msa_shape* s) { return rows_of(s) * MSA_NUM_KV_HEADS * (size_t)s->max_blocks_per_seq * 4; }
+size_t sel_bytes(const msa_shape* s) { return rows_of(s) * MSA_NUM_KV_HEADS * MSA_TOPK * 4; }
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+msa::AttnArgs attn_args(const msa_shape* s, const msa_cache* c, const void* q, const int32_t* sel, float* out,
+                        void* partials) {
+  msa::AttnArgs a;
+  a.k = c->k;
+  a.v = c->v;
+  a.k_sf = c->k_sf;
+  a.v_sf = c->v_sf;
+  a.block_table = c->block_table;
+  a.seq_lens = c->seq_lens;
+  a.q = static_cast<const uint16_t*>(q);
+  a.sel = sel;
+  a.partials = static_cast<float*>(partials);
+  a.out = out;
+  a.rows = (int)rows_of(s);
+  a.q_len = s->q_len;
+  a.mbps = s->max_blocks_per_seq;
+  a.qk_scale_log2 = (float)((double)s->sm_scale * (double)s->k_scale * 1.4426950408889634);
+  a.v_scale = s->v_scale;
+  a.kv_nvfp4 = s->kv_dtype == MSA_KV_NVFP4;
+  return a;
+}
+
+msa::ScanArgs scan_args(const msa_shape* s, const msa_cache* c, const void* idx_q, float* block_scores) {
+  msa::ScanArgs a;
+  a.idx_pool = c->idx_k;
+  a.block_table = c->block_table;
+  a.seq_lens = c->seq_lens;
+  a.iq = static_cast<const uint16_t*>(idx_q);
+  a.block_scores = block_scores;
+  a.num_seqs = s->num_seqs;
+  a.mbps = s->max_blocks_per_seq;
+  a.idx_scale = s->idx_scale;
+  a.idx_fp8 = s->idx_dtype == MSA_IDX_FP8_E4M3;
+  return a;
+}
+
+msa_status check_aligned(const void* p, size_t a, const char* what) {
+  if (((uintptr_t)p) % a) return fail(MSA_ERR_INVALID_ARGUMENT, "%s must be %zu-byte aligned", what, a);
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t msa_attn_workspace_size(const msa_shape* shape) {
+  if (check_shape(shape) != MSA_OK) return 0;
+  return align256(msa::attn_partials_bytes((int)rows_of(shape)));
+}
+
+size_t msa_workspace_size(const msa_shape* shape) {
+  if (check_shape(shape) != MSA_OK) return 0;
+  return align256(scores_bytes(shape)) + align256(sel_bytes(shape)) +
+         align256(msa::attn_partials_bytes((int)rows_of(shape)));
+}
+
+msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, const void* idx_q, float* block_scores,
+                             hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(shape, cache, true, false)) != MSA_OK) return st;
+  if (!idx_q || !block_scores) return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q / block_scores is NULL");
+  if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
+  if ((st = check_aligned(idx_q, 16, "idx_q")) != MSA_OK) return st;
+  if (shape->q_len != 1)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_indexer_score: q_len = %d (the index scan handles decode, q_len 1)",
+                shape->q_len);
+  if (shape->num_seqs == 0) return ok();
+  return hip_status(msa::launch_scan_decode(scan_args(shape, cache, idx_q, block_scores), stream), "index scan");
+}
+
+msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const float* block_scores,
+                          int32_t* sel_blocks, hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!seq_lens || !block_scores || !sel_blocks)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "seq_lens / block_scores / sel_blocks is NULL");
+  if (shape->num_seqs == 0) return ok();
+  msa::TopkArgs a{seq_lens, block_scores, sel_blocks, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};
+  return hip_status(msa::launch_block_topk(a, stream), "block top-k");
+}
+
+msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache, const void* q,
+                                  const int32_t* sel_blocks, float* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(shape, cache, false, true)) != MSA_OK) return st;
+  if (!q || !sel_blocks || !out) return fail(MSA_ERR_INVALID_ARGUMENT, "q / sel_blocks / out is NULL");
+  if ((st = check_aligned(q, 16, "q")) != MSA_OK) return st;
+  if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
+  if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
+  const size_t need = msa_attn_workspace_size(shape);
+  if (shape->num_seqs > 0) {
+    if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((st = check_aligned(workspace, 256, "workspace")) != MSA_OK) return st;
+    if (workspace_bytes < need)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  }
+  if (shape->num_seqs == 0) return ok();
+  return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, sel_blocks, out, workspace), stream),
+                    "sparse attention");
+}
+
+msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
+                      int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(shape, cache, true, true)) != MSA_OK) return st;
+  if (!q || !idx_q || !out) return fail(MSA_ERR_INVALID_ARGUMENT, "q / idx_q / out is NULL");
+  if ((st = check_aligned(q, 16, "q")) != MSA_OK) return st;
+  if ((st = check_aligned(idx_q, 16, "idx_q")) != MSA_OK) return st;
+  if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
+  if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
+  if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
+  if (shape->q_len != 1)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_decode: q_len = %d (multi-query path not available)", shape->q_len);
+  const size_t need = msa_workspace_size(shape);
+  if (shape->num_seqs > 0) {
+    if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((st = check_aligned(workspace, 256, "workspace")) != MSA_OK) return st;
+    if (workspace_bytes < need)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  }
+  if (shape->num_seqs == 0) return ok();
+
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align256(scores_bytes(shape));
+  int32_t* sel = reinterpret_cast<int32_t*>(ws);
+  ws += align256(sel_bytes(shape));
+  void* partials = ws;
+  if (sel_blocks) sel = sel_blocks;
+
+  hipError_t e = msa::launch_scan_decode(scan_args(shape, cache, idx_q, scores), stream);
+  if (e != hipSuccess) return hip_status(e, "index scan");
+  msa::TopkArgs ta{cache->seq_lens, scores, sel, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};
+  e = msa::launch_block_topk(ta, stream);
+  if (e != hipSuccess) return hip_status(e, "block top-k");
+  e = msa::launch_sparse_attn(attn_args(shape, cache, q, sel, out, partials), stream);
+  return hip_status(e, "sparse attention");
+}
+
+const char* msa_status_string(msa_status status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARGUMENT: return "MSA_ERR_INVALID_ARGUMENT";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

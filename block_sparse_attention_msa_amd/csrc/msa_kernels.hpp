@@ -1,0 +1,68 @@
+// msa_kernels.hpp - internal launchers of the MSA kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;               // tokens per KV block / page
+constexpr int kDim = 128;                 // head dim == index dim
+constexpr int kTopK = 16;                 // kept blocks per (row, group)
+constexpr int kGroups = 4;                // KV heads == GQA groups
+constexpr int kHeadsPerGroup = 4;         // query heads per group
+constexpr int kMaxBlocksPerSeq = 16384;   // 2M tokens per sequence
+
+struct ScanArgs {
+  const void* idx_pool;        // [P][128][128] FP8 or bf16
+  const int32_t* block_table;  // [S][mbps]
+  const int32_t* seq_lens;     // [S]
+  const uint16_t* iq;          // bf16 [S][4][128]
+  float* block_scores;         // [S][4][mbps]
+  int num_seqs;
+  int mbps;
+  float idx_scale;
+  bool idx_fp8;
+};
+// Decode (one query row per sequence) index scan + block max-pool.
+hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+  const int32_t* seq_lens;
+  const float* block_scores;   // [rows][4][mbps]
+  int32_t* sel;                // [rows][4][16]
+  int rows;
+  int q_len;
+  int mbps;
+};
+hipError_t launch_block_topk(const TopkArgs& a, hipStream_t stream);
+
+constexpr int kAttnSplits = 4;                   // workgroups per (row, group)
+constexpr int kPartialFloats = 4 * (128 + 2);    // per workgroup: 4 heads x (o[128], m, l)
+
+struct AttnArgs {
+  const void* k;
+  const void* v;
+  const uint8_t* k_sf;
+  const uint8_t* v_sf;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const uint16_t* q;           // bf16 [rows][16][128]
+  const int32_t* sel;          // [rows][4][16]
+  float* partials;             // [rows][4][kAttnSplits][kPartialFloats]
+  float* out;                  // [rows][16][128]
+  int rows;
+  int q_len;
+  int mbps;
+  float qk_scale_log2;         // sm_scale * k_scale * log2(e)
+  float v_scale;
+  bool kv_nvfp4;
+};
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+inline size_t attn_partials_bytes(int rows) {
+  return (size_t)rows * 4 * kAttnSplits * kPartialFloats * sizeof(float);
+}
+
+}  // namespace msa

@@ -1,0 +1,160 @@
+/*
+ * msa.h - C ABI of the MI355X (gfx950) MiniMax Sparse Attention decode path.
+ *
+ * The method (vLLM "Day-0 support for MiniMax-M3.1-Flash", section "MSA
+ * basics"; "MiniMax M3 x vLLM", sections "MSA mechanism details", "MiniMax
+ * sparse attention backend", "Decode execution" and "KV cache layout"):
+ * the KV cache is cut into 128-token blocks; a lightweight indexer scores
+ * every context key with one index query per GQA group against one shared
+ * 128-dim index-key head; the scores are max-pooled to one score per block;
+ * per group the most recent block plus the 15 best other blocks are kept
+ * (at most 16 x 128 = 2,048 keys); exact GQA attention then runs over only
+ * the kept keys.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls and never synchronises:
+ *    work is enqueued on `stream` and results are valid once the stream has
+ *    reached that point.  Launch grids depend only on the host-side shape, so
+ *    calls can be captured into HIP graphs.
+ *  - Host arguments are validated before any HIP call.  Failures return
+ *    MSA_ERR_INVALID_ARGUMENT / MSA_ERR_UNSUPPORTED / MSA_ERR_WORKSPACE_TOO_SMALL
+ *    with a message in msa_last_error(); nothing is launched then.  A launch
+ *    failure returns MSA_ERR_HIP.
+ *  - Device-resident values are preconditions, not checked: for every sequence
+ *    b, 0 <= seq_lens[b] <= max_blocks_per_seq * 128 and seq_lens[b] is 0 or
+ *    >= q_len; block_table[b][j] lies in [0, num_pages) for every block j that
+ *    holds a visible token.  A sequence with seq_lens[b] == 0 is a padded row:
+ *    its block scores are -inf, its selected ids -1 and its output 0.
+ *  - Query rows are flattened request-major: row = b * q_len + i, and row i of
+ *    sequence b sits at position seq_lens[b] - q_len + i (its own K/V and index
+ *    key are already in the cache, so it attends to itself).
+ *  - Block ids are LOGICAL block indices of the sequence (block j holds tokens
+ *    128 j .. 128 j + 127), never physical pages.
+ *
+ * Stored formats
+ *  - q      bf16 [rows][num_q_heads][128]; iq bf16 [rows][num_kv_heads][128].
+ *  - idx_k  index-key pool, one shared head: FP8 E4M3 (OCP, bias 7) bytes
+ *           [num_pages][128 tokens][128], or bf16 [num_pages][128][128];
+ *           value = stored x idx_scale.
+ *  - k, v   NVFP4: uint8 [num_pages][num_kv_heads][128 tokens][64], element 2i
+ *           in the low nibble of byte i (E2M1), plus k_sf / v_sf uint8 E4M3
+ *           [num_pages][num_kv_heads][128 tokens][8] (one scale per 16
+ *           consecutive elements); value = e2m1 x scale x k_scale (v_scale).
+ *           bf16: [num_pages][num_kv_heads][128][128], value = stored x k_scale.
+ *  - block_table int32 [num_seqs][max_blocks_per_seq]; seq_lens int32 [num_seqs].
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_BLOCK_SIZE 128    /* tokens per KV block (one page)              */
+#define MSA_HEAD_DIM 128      /* q / k / v head dimension                    */
+#define MSA_INDEX_DIM 128     /* index query / index key dimension           */
+#define MSA_TOPK 16           /* kept blocks per (query, group), recent incl. */
+#define MSA_NUM_KV_HEADS 4    /* GQA groups = KV heads = index queries/token */
+#define MSA_NUM_Q_HEADS 16    /* query heads (4 per group)                   */
+#define MSA_MAX_BLOCKS_PER_SEQ 16384 /* 2M tokens                            */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,
+  MSA_ERR_UNSUPPORTED = 2,
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4
+} msa_status;
+
+typedef enum { MSA_KV_BF16 = 0, MSA_KV_NVFP4 = 1 } msa_kv_dtype;
+typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1 } msa_idx_dtype;
+
+/* Host-side problem shape; read only during the call. */
+typedef struct {
+  int32_t num_seqs;           /* S >= 0 (0: nothing to do)                          */
+  int32_t q_len;              /* query tokens per sequence; 1 = decode              */
+  int32_t num_q_heads;        /* must be MSA_NUM_Q_HEADS                            */
+  int32_t num_kv_heads;       /* must be MSA_NUM_KV_HEADS                           */
+  int32_t max_blocks_per_seq; /* row stride of block_table, 1..MSA_MAX_BLOCKS_PER_SEQ */
+  int32_t num_pages;          /* pool size P >= 1                                   */
+  int32_t kv_dtype;           /* msa_kv_dtype                                       */
+  int32_t idx_dtype;          /* msa_idx_dtype                                      */
+  float sm_scale;             /* softmax logit scale (normally 1/sqrt(128)), > 0    */
+  float k_scale, v_scale;     /* K / V tensor scales, > 0                           */
+  float idx_scale;            /* index-key tensor scale, > 0                        */
+} msa_shape;
+
+/* Paged caches: device pointers, caller-owned, layouts as above. */
+typedef struct {
+  const void* k;
+  const void* v;
+  const uint8_t* k_sf;        /* NVFP4 only; NULL for bf16 */
+  const uint8_t* v_sf;        /* NVFP4 only; NULL for bf16 */
+  const void* idx_k;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+} msa_cache;
+
+/* Bytes of device workspace msa_decode needs for this shape (256-B aligned
+ * pointer expected).  msa_sparse_attn_decode needs msa_attn_workspace_size().
+ * Returns 0 for an invalid shape (see msa_last_error()). */
+size_t msa_workspace_size(const msa_shape* shape);
+size_t msa_attn_workspace_size(const msa_shape* shape);
+
+/* Steps 1-2 of the method ("MSA basics": index scores against the shared
+ * index-key head, max-pooled per 128-token block; "Decode indexer-score
+ * kernel" of the M3 post: a dedicated scan, not a padded dense GEMM).
+ *   idx_q        bf16 [rows][num_kv_heads][128]
+ *   block_scores fp32 [rows][num_kv_heads][max_blocks_per_seq], written in
+ *                full: for the row's visible blocks j <= pos/128,
+ *                idx_scale * max over tokens t <= pos of block j of
+ *                sum_d idx_q[row][g][d] * idx_k[t][d]; -inf elsewhere.
+ * fp32 accumulation; products are exact in fp32. */
+msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, const void* idx_q,
+                             float* block_scores, hipStream_t stream);
+
+/* Step 3 ("MSA basics": top-16 blocks with the most recent one always kept;
+ * "MSA mechanism details": init_blocks = 0, local_blocks = 1, a local block
+ * that also wins top-k is not counted twice).
+ *   seq_lens     int32 [num_seqs] (device)
+ *   block_scores fp32 [rows][num_kv_heads][max_blocks_per_seq] (device)
+ *   sel_blocks   int32 [rows][num_kv_heads][16]: with r = pos/128 the recent
+ *                block, all of 0..r if r < 16, else r plus the 15 blocks j < r
+ *                first under (score descending, index ascending); ascending,
+ *                padded with -1. */
+msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const float* block_scores,
+                          int32_t* sel_blocks, hipStream_t stream);
+
+/* Step 4 ("MSA basics": exact attention over the kept blocks only; "Prefill
+ * execution" step 4 of the M3 post: equal to dense attention restricted to
+ * the selected set; "Decode sparse GQA": split work, partial outputs merged).
+ *   q          bf16 [rows][num_q_heads][128]; head h uses KV head h / 4
+ *   sel_blocks int32 [rows][num_kv_heads][16] logical ids (-1 = none)
+ *   out        fp32 [rows][num_q_heads][128]
+ *   workspace  device buffer of >= msa_attn_workspace_size(shape) bytes
+ * Keys: tokens t <= pos of the listed blocks; logits sm_scale * q.k. */
+msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache, const void* q,
+                                  const int32_t* sel_blocks, float* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* The fused path: steps 1-4 in one call, no host synchronisation.
+ *   sel_blocks may be NULL (then kept inside the workspace).
+ *   workspace  >= msa_workspace_size(shape) bytes. */
+msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
+                      int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+const char* msa_status_string(msa_status status);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* msa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,136 @@
+"""The C-ABI boundary on the CPU: the library loads without a GPU, exports
+every function include/msa.h declares, and host-side validation returns its
+documented status codes before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_msa_amd import msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(msa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = msa.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def _shape(**kw):
+    d = dict(num_seqs=2, q_len=1, num_q_heads=16, num_kv_heads=4, max_blocks_per_seq=8, num_pages=16,
+             kv_dtype=msa.MSA_KV_NVFP4, idx_dtype=msa.MSA_IDX_FP8_E4M3, sm_scale=0.088, k_scale=1.0, v_scale=1.0,
+             idx_scale=1.0)
+    d.update(kw)
+    return msa.MsaShape(*[d[f] for f, _ in msa.MsaShape._fields_])
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def _cache(**kw):
+    d = dict(k=FAKE, v=FAKE, k_sf=FAKE, v_sf=FAKE, idx_k=FAKE, block_table=FAKE, seq_lens=FAKE)
+    d.update(kw)
+    return msa.MsaCache(*[d[f] for f, _ in msa.MsaCache._fields_])
+
+
+def _decode(shape, cache=None, q=FAKE, iq=FAKE, out=FAKE, sel=FAKE, ws=FAKE, nbytes=1 << 30):
+    L = msa.lib()
+    cache = cache or _cache()
+    return L.msa_decode(ctypes.byref(shape) if shape is not None else None, ctypes.byref(cache), q, iq, out, sel, ws,
+                        nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=8), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=2), msa.MSA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), msa.MSA_ERR_UNSUPPORTED),
+    (dict(idx_dtype=5), msa.MSA_ERR_UNSUPPORTED),
+    (dict(q_len=0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(num_seqs=-1), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(max_blocks_per_seq=0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(max_blocks_per_seq=16385), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(sm_scale=0.0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(k_scale=float("nan")), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(idx_scale=-1.0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(q_len=2000, max_blocks_per_seq=8), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(q_len=3), msa.MSA_ERR_UNSUPPORTED),  # multi-query decode entry not available yet
+])
+def test_shape_validation(kw, code):
+    assert _decode(_shape(**kw)) == code
+    assert msa.last_error() != ""
+    size = msa.lib().msa_workspace_size(ctypes.byref(_shape(**kw)))
+    if kw.get("q_len") == 3:
+        assert size > 0   # a valid shape; only the entry point lacks the multi-query path
+    else:
+        assert size == 0  # invalid shapes have no workspace size
+
+
+def test_null_and_pointer_validation():
+    L = msa.lib()
+    assert L.msa_decode(None, ctypes.byref(_cache()), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), q=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), iq=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), out=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), cache=_cache(k_sf=None)) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), cache=_cache(idx_k=None)) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), cache=_cache(block_table=None)) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), ws=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert _decode(_shape(), q=FAKE + 2) == msa.MSA_ERR_INVALID_ARGUMENT        # misaligned
+    assert _decode(_shape(), ws=FAKE + 16) == msa.MSA_ERR_INVALID_ARGUMENT      # workspace not 256-B aligned
+    # bf16 K/V needs no scale arrays; validation then proceeds to the workspace check
+    assert _decode(_shape(kv_dtype=msa.MSA_KV_BF16), cache=_cache(k_sf=None, v_sf=None), nbytes=0) == \
+        msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_size_and_too_small():
+    L = msa.lib()
+    s = _shape(num_seqs=32, max_blocks_per_seq=1024)
+    need = L.msa_workspace_size(ctypes.byref(s))
+    scores = 32 * 4 * 1024 * 4
+    assert need >= scores + 32 * 4 * 16 * 4 and need % 256 == 0
+    assert _decode(s, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in msa.last_error()
+    attn = L.msa_attn_workspace_size(ctypes.byref(s))
+    assert 0 < attn < need
+    assert L.msa_sparse_attn_decode(ctypes.byref(s), ctypes.byref(_cache()), FAKE, FAKE, FAKE, FAKE, attn - 1,
+                                    None) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_empty_batch_is_a_no_op():
+    """num_seqs == 0 returns MSA_OK without launching anything."""
+    L = msa.lib()
+    s = _shape(num_seqs=0)
+    assert _decode(s, ws=None, nbytes=0) == msa.MSA_OK
+    assert L.msa_indexer_score(ctypes.byref(s), ctypes.byref(_cache()), FAKE, FAKE, None) == msa.MSA_OK
+    assert L.msa_block_topk(ctypes.byref(s), FAKE, FAKE, FAKE, None) == msa.MSA_OK
+    assert msa.last_error() == ""
+
+
+def test_other_entry_points_validate():
+    L = msa.lib()
+    s = _shape()
+    assert L.msa_indexer_score(ctypes.byref(s), ctypes.byref(_cache()), None, FAKE, None) == \
+        msa.MSA_ERR_INVALID_ARGUMENT
+    assert L.msa_indexer_score(ctypes.byref(_shape(q_len=2)), ctypes.byref(_cache()), FAKE, FAKE, None) == \
+        msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_block_topk(ctypes.byref(s), None, FAKE, FAKE, None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert L.msa_sparse_attn_decode(ctypes.byref(s), ctypes.byref(_cache(v=None)), FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == msa.MSA_ERR_INVALID_ARGUMENT
+    for st in range(5):
+        assert msa.status_string(st).startswith("MSA_")

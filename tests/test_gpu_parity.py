@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small and ragged cases are compared on every row; the full-size workloads
+(batch 32 x 128K paged, batch 4 x 512K paged) are run in the same launch
+configuration the bench times and compared on sampled rows.  Rules (ids
+bit-exact except near ties, out within 2e-3 + 1e-2|ref|, block scores within
+the fp32 rounding bound) are in oracle/compare.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.compare import check_row
+from block_sparse_attention_msa_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _msa():
+    from block_sparse_attention_msa_amd import msa  # raises if libmsa.so is missing
+    return msa
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_all(w):
+    """Fused path plus the unfused trio; returns host arrays."""
+    msa = _msa()
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    dev = w.q.device
+    out, sel = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+    bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    sel2 = torch.empty_like(sel)
+    out2 = torch.empty_like(out)
+    msa.msa_indexer_score(shape, cache, w.iq, bs)
+    msa.msa_block_topk(shape, w.seq_lens, bs, sel2)
+    msa.msa_sparse_attn_decode(shape, cache, w.q, sel2, out2, msa.alloc_workspace(shape, dev, attn_only=True))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy(), out2.cpu().numpy(), sel2.cpu().numpy()
+
+
+def check_workload(w, rows=None, label=""):
+    _say(f"[parity] {label or w.name}: seqs={w.num_seqs} mbps={w.max_blocks_per_seq} kv={w.kv_dtype} idx={w.idx_dtype}")
+    out, sel, bs, out2, sel2 = run_all(w)
+    # the unfused trio runs the same kernels: identical results
+    assert np.array_equal(sel, sel2)
+    assert np.array_equal(out, out2)
+    P = oracle.Problem.from_workload(w)
+    rows = range(w.rows) if rows is None else rows
+    ties = 0
+    worst = 0.0
+    for row in rows:
+        info = check_row(P, row, out[row], sel[row], bs[row])
+        ties += info["near_ties"]
+        worst = max(worst, info["max_abs_err"])
+    _say(f"[parity] {label or w.name}: rows={len(list(rows))} near_ties={ties} max_abs_err={worst:.3g}")
+    return out, sel, bs
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def test_tiny_bf16_config(dev):
+    w = synth.make_config("tiny_b1_4k_bf16", device=dev)
+    _, sel, _ = check_workload(w)
+    for g in range(4):
+        assert set(w.meta["planted"][(0, g)]) <= set(sel[0, g].tolist())
+
+
+def test_decode_b8_32k_config(dev):
+    w = synth.make_config("decode_b8_32k", device=dev)
+    _, sel, _ = check_workload(w)
+    for b in range(8):
+        for g in range(4):
+            assert set(w.meta["planted"][(b, g)]) <= set(sel[b, g].tolist())
+
+
+def test_paged_b32_128k_config_sampled(dev):
+    w = synth.make_config("paged_b32_128k", device=dev)
+    check_workload(w, rows=[0, 9, 22, 31])
+
+
+def test_paged_b4_512k_config_sampled(dev):
+    w = synth.make_config("paged_b4_512k", device=dev)
+    _, sel, _ = check_workload(w, rows=[0, 3])
+    for b in (0, 3):
+        for g in range(4):
+            assert set(w.meta["planted"][(b, g)]) <= set(sel[b, g].tolist())
+
+
+@pytest.mark.parametrize("kv,idx", [("nvfp4", "fp8"), ("bf16", "bf16"), ("nvfp4", "bf16"), ("bf16", "fp8")])
+def test_ragged_lengths_all_dtypes(dev, kv, idx):
+    """Ragged contexts: 1 token, partial blocks, exactly 16 and 17 blocks,
+    a padded row, table wider than any sequence, paged layout."""
+    lens = [1, 127, 128, 129, 16 * 128, 16 * 128 + 1, 0, 5000, 37 * 128 - 3, 20000]
+    w = synth.make_workload(seq_lens=lens, kv_dtype=kv, idx_dtype=idx, plant=3, layout="paged", seed=21,
+                            max_blocks_per_seq=200, spare_pages=7, device=dev)
+    out, sel, bs = check_workload(w, label=f"ragged {kv}/{idx}")
+    assert (out[6] == 0).all() and (sel[6] == -1).all() and np.isneginf(bs[6]).all()
+
+
+def test_scales_not_one(dev):
+    w = synth.make_workload(seq_lens=[9000, 3333], plant=2, seed=22, idx_scale=0.37, sm_scale=0.05, device=dev)
+    w.k_scale *= 3.0
+    w.v_scale *= 0.25
+    check_workload(w, label="scales")
+
+
+def test_exhaustive_format_codes(dev):
+    """Every finite E4M3 index-key byte, every E2M1 nibble and every finite
+    E4M3 K/V scale byte appears; checks the hardware conversions end to end."""
+    w = synth.make_workload(seq_lens=[128 * 40, 128 * 23 + 77], seed=23, device=dev)
+    P = w.num_pages
+    codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8, device=dev)
+    n = w.idx_k.numel()
+    w.idx_k.view(-1).copy_(codes.repeat(n // codes.numel() + 1)[:n])
+    # shuffle the codes per token so every dim chunk sees all of them
+    perm = torch.randperm(w.idx_k.shape[1] * w.idx_k.shape[2], generator=torch.Generator().manual_seed(0))
+    w.idx_k.copy_(w.idx_k.view(P, -1)[:, perm.to(dev)].view_as(w.idx_k))
+    nib = torch.arange(256, dtype=torch.uint8, device=dev)          # all nibble pairs
+    for t in (w.k, w.v):
+        m = t.numel()
+        t.view(-1).copy_(nib.repeat(m // 256 + 1)[:m])
+    for t in (w.k_sf, w.v_sf):
+        m = t.numel()
+        t.view(-1).copy_(codes.repeat(m // codes.numel() + 1)[:m])
+    w.k_scale = w.v_scale = 1.0 / (448 * 6)
+    w.idx_scale = 1.0 / 64
+    check_workload(w, label="exhaustive codes")
+
+
+def test_selection_kernel_exact_on_ties(dev):
+    """msa_block_topk alone: integer-valued scores full of ties and -0/+0;
+    ids must equal the oracle's selection of the same fp32 values bit for bit."""
+    msa = _msa()
+    rng = np.random.default_rng(5)
+    lens = [128 * n for n in (17, 18, 64, 300, 1024, 4096, 16384)] + [128 * 200 + 5, 0]
+    S = len(lens)
+    mb = 16384
+    bs = rng.integers(-4, 4, size=(S, 4, mb)).astype(np.float32)
+    bs[1, 0, :] = 0.0
+    bs[1, 0, ::2] = -0.0
+    bs[2, 1, :] = 7.0                       # all equal: lowest ids win
+    bs[3, 2, :] = np.linspace(-1, 1, mb, dtype=np.float32)[::-1]
+    shape = msa.MsaShape(S, 1, 16, 4, mb, 1, 1, 1, 0.1, 1.0, 1.0, 1.0)
+    d_bs = torch.from_numpy(bs).to(dev)
+    d_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+    d_sel = torch.empty(S, 4, 16, dtype=torch.int32, device=dev)
+    msa.msa_block_topk(shape, d_len, d_bs, d_sel)
+    got = d_sel.cpu().numpy()
+    for b, L in enumerate(lens):
+        nbv = (L - 1) // 128 + 1 if L else 0
+        for g in range(4):
+            ref = oracle.select(bs[b, g].astype(np.float64), nbv)
+            assert np.array_equal(got[b, g], ref), (b, g, got[b, g], ref)
+
+
+def test_paged_permutation_invariance(dev):
+    """Physical page permutation leaves ids and outputs bitwise unchanged."""
+    w = synth.make_workload(seq_lens=[7000, 4100, 300], plant=3, seed=24, spare_pages=3, device=dev)
+    out0, sel0, _, _, _ = run_all(w)
+    perm = torch.randperm(w.num_pages, generator=torch.Generator().manual_seed(1)).to(dev)
+    for name in ("idx_k", "k", "v", "k_sf", "v_sf"):
+        t = getattr(w, name)
+        new = torch.empty_like(t)
+        new[perm] = t
+        setattr(w, name, new)
+    w.block_table = perm[w.block_table.long()].to(torch.int32)
+    out1, sel1, _, _, _ = run_all(w)
+    assert np.array_equal(sel0, sel1)
+    assert np.array_equal(out0, out1)
+
+
+def test_deterministic(dev):
+    w = synth.make_workload(seq_lens=[30000, 12000, 640], plant=4, seed=25, device=dev)
+    a = run_all(w)
+    b = run_all(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
