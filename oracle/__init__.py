@@ -84,6 +84,8 @@ class Problem:
         self.num_q_heads, self.num_kv_heads = int(num_q_heads), int(num_kv_heads)
         self.max_blocks_per_seq = int(max_blocks_per_seq)
         self.rows = self.num_seqs * self.q_len
+        self.sm_scale, self.k_scale = float(sm_scale), float(k_scale)
+        self.v_scale, self.idx_scale = float(v_scale), float(idx_scale)
         self._s = _Problem(self.num_seqs, self.q_len, self.num_q_heads, self.num_kv_heads, self.max_blocks_per_seq,
                            int(num_pages), 1 if kv_dtype == "nvfp4" else 0, 1 if idx_dtype == "fp8" else 0,
                            float(sm_scale), float(k_scale), float(v_scale), float(idx_scale),

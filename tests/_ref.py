@@ -62,6 +62,4 @@ def row_queries(P, row: int):
 
 def make_problem(w):
     import oracle
-    p = oracle.Problem.from_workload(w)
-    p.idx_scale, p.k_scale, p.v_scale, p.sm_scale = w.idx_scale, w.k_scale, w.v_scale, w.sm_scale
-    return p
+    return oracle.Problem.from_workload(w)
