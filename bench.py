@@ -76,6 +76,28 @@ def cpu_baseline(w, sample_seqs: int, t_gpu_us: float):
             "gpu_speedup": round(scaled_us / t_gpu_us, 1)}
 
 
+COPY_BYTES = 512 << 20
+
+
+def run_counter_pass(args, w, copies, shape, caches):
+    """Launches for hardware-counter runs: the index scan (steps x) and a plain
+    device copy of COPY_BYTES (steps x) whose FETCH_SIZE / WRITE_SIZE per
+    dispatch calibrate the counters against a known byte count."""
+    import torch
+    from block_sparse_attention_msa_amd import msa
+    dev = w.q.device
+    bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for i in range(args.steps):
+        c = copies[i % len(copies)]
+        msa.msa_indexer_score(shape, caches[i % len(copies)], c.iq, bs)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] counters pass: {args.steps} scan launches ({scan_bytes(w)} algorithmic B each), "
+        f"{args.steps} copies of {COPY_BYTES} B")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +107,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="input copies the steps rotate through")
     ap.add_argument("--cpu-sample-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
+                    help="counters: only the scan kernel and a plain 512 MiB copy of known size, for rocprofv3 --pmc")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -105,6 +129,9 @@ def main():
 
     shape = msa.MsaShape.from_workload(w)
     caches = [msa.MsaCache.from_workload(c) for c in copies]
+    if args.mode == "counters":
+        run_counter_pass(args, w, copies, shape, caches)
+        return
     ws = msa.alloc_workspace(shape, dev)
     out, sel = msa.alloc_outputs(w)
     stream = torch.cuda.current_stream()

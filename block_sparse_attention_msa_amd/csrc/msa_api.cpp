@@ -76,15 +76,14 @@ msa_status check_cache(const msa_shape* s, const msa_cache* c, bool need_idx, bo
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t rows_of(const msa_shape* s) { return (size_t)s->num_seqs * (size_t)s->q_len; }
 size_t scores_bytes(const msa_shape* s) { return rows_of(s) * MSA_NUM_KV_HEADS * (size_t)s->max_blocks_per_seq * 4; }
-size_t sel_bytes(const msa_shape* s) { return rows_of(s) * MSA_NUM_KV_HEADS * MSA_TOPK * 4; }
 
 msa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-msa::AttnArgs attn_args(const msa_shape* s, const msa_cache* c, const void* q, const int32_t* sel, float* out,
-                        void* partials) {
+msa::AttnArgs attn_args(const msa_shape* s, const msa_cache* c, const void* q, const float* block_scores,
+                        const int32_t* sel, int32_t* sel_out, float* out) {
   msa::AttnArgs a;
   a.k = c->k;
   a.v = c->v;
@@ -93,8 +92,9 @@ msa::AttnArgs attn_args(const msa_shape* s, const msa_cache* c, const void* q, c
   a.block_table = c->block_table;
   a.seq_lens = c->seq_lens;
   a.q = static_cast<const uint16_t*>(q);
+  a.block_scores = block_scores;
   a.sel = sel;
-  a.partials = static_cast<float*>(partials);
+  a.sel_out = sel_out;
   a.out = out;
   a.rows = (int)rows_of(s);
   a.q_len = s->q_len;
@@ -129,14 +129,13 @@ msa_status check_aligned(const void* p, size_t a, const char* what) {
 extern "C" {
 
 size_t msa_attn_workspace_size(const msa_shape* shape) {
-  if (check_shape(shape) != MSA_OK) return 0;
-  return align256(msa::attn_partials_bytes((int)rows_of(shape)));
+  (void)check_shape(shape);
+  return 0;  // the attention kernel merges its split work on chip
 }
 
 size_t msa_workspace_size(const msa_shape* shape) {
   if (check_shape(shape) != MSA_OK) return 0;
-  return align256(scores_bytes(shape)) + align256(sel_bytes(shape)) +
-         align256(msa::attn_partials_bytes((int)rows_of(shape)));
+  return align256(scores_bytes(shape));
 }
 
 msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, const void* idx_q, float* block_scores,
@@ -168,6 +167,8 @@ msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const
 msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache, const void* q,
                                   const int32_t* sel_blocks, float* out, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;  // no workspace is needed (msa_attn_workspace_size() == 0)
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;
   if ((st = check_cache(shape, cache, false, true)) != MSA_OK) return st;
@@ -175,15 +176,8 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
   if ((st = check_aligned(q, 16, "q")) != MSA_OK) return st;
   if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
-  const size_t need = msa_attn_workspace_size(shape);
-  if (shape->num_seqs > 0) {
-    if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
-    if ((st = check_aligned(workspace, 256, "workspace")) != MSA_OK) return st;
-    if (workspace_bytes < need)
-      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
-  }
   if (shape->num_seqs == 0) return ok();
-  return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, sel_blocks, out, workspace), stream),
+  return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, nullptr, sel_blocks, nullptr, out), stream),
                     "sparse attention");
 }
 
@@ -209,21 +203,13 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   }
   if (shape->num_seqs == 0) return ok();
 
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws);
-  ws += align256(scores_bytes(shape));
-  int32_t* sel = reinterpret_cast<int32_t*>(ws);
-  ws += align256(sel_bytes(shape));
-  void* partials = ws;
-  if (sel_blocks) sel = sel_blocks;
-
+  // 2 launches: index scan fused with the block max-pool, then selection
+  // fused with attention (each attention workgroup selects its (row, group)).
+  float* scores = static_cast<float*>(workspace);
   hipError_t e = msa::launch_scan_decode(scan_args(shape, cache, idx_q, scores), stream);
   if (e != hipSuccess) return hip_status(e, "index scan");
-  msa::TopkArgs ta{cache->seq_lens, scores, sel, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};
-  e = msa::launch_block_topk(ta, stream);
-  if (e != hipSuccess) return hip_status(e, "block top-k");
-  e = msa::launch_sparse_attn(attn_args(shape, cache, q, sel, out, partials), stream);
-  return hip_status(e, "sparse attention");
+  e = msa::launch_sparse_attn(attn_args(shape, cache, q, scores, nullptr, sel_blocks, out), stream);
+  return hip_status(e, "selection + sparse attention");
 }
 
 const char* msa_status_string(msa_status status) {

@@ -38,9 +38,6 @@ struct TopkArgs {
 };
 hipError_t launch_block_topk(const TopkArgs& a, hipStream_t stream);
 
-constexpr int kAttnSplits = 4;                   // workgroups per (row, group)
-constexpr int kPartialFloats = 4 * (128 + 2);    // per workgroup: 4 heads x (o[128], m, l)
-
 struct AttnArgs {
   const void* k;
   const void* v;
@@ -49,8 +46,9 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const uint16_t* q;           // bf16 [rows][16][128]
-  const int32_t* sel;          // [rows][4][16]
-  float* partials;             // [rows][4][kAttnSplits][kPartialFloats]
+  const float* block_scores;   // [rows][4][mbps]: select in-kernel (fused path), or nullptr
+  const int32_t* sel;          // [rows][4][16] ids when block_scores is nullptr
+  int32_t* sel_out;            // fused path: where to store the selection, or nullptr
   float* out;                  // [rows][16][128]
   int rows;
   int q_len;
@@ -59,10 +57,7 @@ struct AttnArgs {
   float v_scale;
   bool kv_nvfp4;
 };
+// Selection (fused path) + attention: one launch.
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
-
-inline size_t attn_partials_bytes(int rows) {
-  return (size_t)rows * 4 * kAttnSplits * kPartialFloats * sizeof(float);
-}
 
 }  // namespace msa

@@ -1,0 +1,202 @@
+// select_device.hpp - exact block selection of one (query row, group), run by
+// a whole workgroup; shared by the stand-alone selection kernel and the
+// fused attention kernel.
+//
+// Method ("MSA basics", vLLM MiniMax-M3.1-Flash post; "MSA mechanism details",
+// MiniMax M3 x vLLM post): keep the block holding the query position
+// (local_blocks = 1, init_blocks = 0) plus the best other visible blocks so
+// that 16 blocks are kept; a local block that also wins top-k is not counted
+// twice, so the others are the top 15 of the blocks before it.  Ties go to the
+// lower block index (total order: score descending, index ascending), which
+// makes the selection exact under any split of the candidates.
+//
+// Algorithm, NT threads:
+//  1. thread t takes blocks j = t + NT e (coalesced loads, all issued before
+//     use) as 64-bit keys (ordered score << 32 | ~j) and keeps its best;
+//  2. each wave sorts its 64 thread bests (bitonic, DPP lane moves where they
+//     exist); T_w = the wave's 15th best is a lower bound of the 15th best
+//     block overall, and so is T0 = max_w T_w;
+//  3. keys >= T0 (every true top-15 key among them; at most 15 threads' worth
+//     per wave) are compacted into LDS with ballots;
+//  4. wave 0 merges the candidates 49 at a time into a running top-15;
+//  5. the 15 ids plus the recent block are written in ascending order.
+#pragma once
+
+#include "msa_device.hpp"
+
+namespace msa {
+
+// Candidate bound: per wave at most 15 threads hold keys >= T0, each with at
+// most ceil(n / NT) keys; summed over NT/64 waves that is <= 15 * 16384 / 64.
+constexpr int kSelCandCap = (kTopK - 1) * (kMaxBlocksPerSeq / kWave) + kWave;
+
+template <int NT>
+struct SelectSmem {
+  uint64_t cand[kSelCandCap];
+  uint64_t wave_t0[NT / kWave];
+  int count;
+};
+
+__device__ __forceinline__ uint64_t block_key(float s, int j) {
+  uint32_t u = __builtin_bit_cast(uint32_t, s);
+  if (u == 0x80000000u) u = 0u;  // -0 ranks equal to +0
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)j);
+}
+__device__ __forceinline__ int key_block(uint64_t k) { return (int)(~(uint32_t)k); }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// value of lane ^ J (J a power of two < 64)
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  if constexpr (J == 1) {
+    return dpp_u32<0xB1>(x);                        // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return dpp_u32<0x4E>(x);                        // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t up = dpp_u32<0x104>(x);          // row_shl:4, lane i reads i+4
+    const uint32_t dn = dpp_u32<0x114>(x);          // row_shr:4, lane i reads i-4
+    return (lane & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return dpp_u32<0x128>(x);                       // row_ror:8 (= xor 8 in a row of 16)
+  } else {
+    return (uint32_t)__shfl_xor((int)x, J);
+  }
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t v, int lane) {
+  const uint32_t lo = xor_lane<J>((uint32_t)v, lane);
+  const uint32_t hi = xor_lane<J>((uint32_t)(v >> 32), lane);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  const bool lower = (lane & J) == 0;   // lower index of its pair
+  const bool desc = (lane & K) == 0;    // this run sorts descending
+  const bool take_max = lower == desc;
+  return take_max ? (o > v ? o : v) : (o < v ? o : v);
+}
+
+// Bitonic sort of one key per lane, descending: lane 0 ends with the largest.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
+  v = bitonic_step<2, 1>(v, lane);
+  v = bitonic_step<4, 2>(v, lane);
+  v = bitonic_step<4, 1>(v, lane);
+  v = bitonic_step<8, 4>(v, lane);
+  v = bitonic_step<8, 2>(v, lane);
+  v = bitonic_step<8, 1>(v, lane);
+  v = bitonic_step<16, 8>(v, lane);
+  v = bitonic_step<16, 4>(v, lane);
+  v = bitonic_step<16, 2>(v, lane);
+  v = bitonic_step<16, 1>(v, lane);
+  v = bitonic_step<32, 16>(v, lane);
+  v = bitonic_step<32, 8>(v, lane);
+  v = bitonic_step<32, 4>(v, lane);
+  v = bitonic_step<32, 2>(v, lane);
+  v = bitonic_step<32, 1>(v, lane);
+  v = bitonic_step<64, 32>(v, lane);
+  v = bitonic_step<64, 16>(v, lane);
+  v = bitonic_step<64, 8>(v, lane);
+  v = bitonic_step<64, 4>(v, lane);
+  v = bitonic_step<64, 2>(v, lane);
+  v = bitonic_step<64, 1>(v, lane);
+  return v;
+}
+
+// Appends the keys of this wave with take == true to cand[] (any order).
+__device__ __forceinline__ void sel_append(uint64_t k, bool take, int lane, uint64_t* cand, int* count) {
+  const uint64_t ballot = __ballot(take);
+  if (ballot == 0) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(count, __popcll(ballot));
+  base = __shfl(base, 0);
+  if (take) cand[base + __popcll(ballot & ((1ull << lane) - 1ull))] = k;
+}
+
+// Selection for one (row, group) by the whole workgroup of NT threads.
+// s: block scores of the row/group; r: the recent block (0 <= r < row length).
+// Writes 16 ids (ascending, -1 padded) to out[] (LDS or global) from wave 0,
+// then synchronises the workgroup so out[] is readable by every thread when
+// it is in LDS.  Every thread of the workgroup must call it.
+template <int NT>
+__device__ void select_blocks(const float* __restrict__ s, int r, SelectSmem<NT>& sm, int32_t* out) {
+  constexpr int kWaves = NT / kWave;
+  constexpr int kRegKeys = 4096 / NT;  // keys held in registers per thread
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  if (r + 1 <= kTopK) {  // every visible block is kept
+    if (tid < kTopK) out[tid] = tid <= r ? tid : -1;
+    __syncthreads();
+    return;
+  }
+  const int n = r;  // candidates: blocks 0 .. r-1 (n >= 16)
+
+  // 1. keys and the best key per thread (loads of in-range indices only)
+  float sv[kRegKeys];
+#pragma unroll
+  for (int e = 0; e < kRegKeys; ++e) sv[e] = s[min(tid + e * NT, n - 1)];
+  uint64_t keys[kRegKeys];
+  uint64_t best = 0;
+#pragma unroll
+  for (int e = 0; e < kRegKeys; ++e) {
+    const int j = tid + e * NT;
+    keys[e] = j < n ? block_key(sv[e], j) : 0;
+    best = keys[e] > best ? keys[e] : best;
+  }
+  for (int j = tid + kRegKeys * NT; j < n; j += NT) {
+    const uint64_t k = block_key(s[j], j);
+    best = k > best ? k : best;
+  }
+
+  // 2. T0 = max over waves of the wave's 15th best thread best (> 0: wave 0
+  //    has at least 16 threads holding keys)
+  const uint64_t sorted = wave_sort_desc(best, lane);
+  if (lane == kTopK - 2) sm.wave_t0[wave] = sorted;
+  if (tid == 0) sm.count = 0;
+  __syncthreads();
+  uint64_t t0 = sm.wave_t0[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
+
+  // 3. candidates >= T0 (absent keys are 0 and never qualify)
+#pragma unroll
+  for (int e = 0; e < kRegKeys; ++e) sel_append(keys[e], keys[e] >= t0, lane, sm.cand, &sm.count);
+  for (int j0 = kRegKeys * NT; j0 < n; j0 += NT) {
+    const int j = j0 + tid;
+    const uint64_t k = j < n ? block_key(s[j], j) : 0;
+    sel_append(k, k >= t0, lane, sm.cand, &sm.count);
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // 4. running top-15 in lanes 0..14, 49 new candidates per round
+    const int count = sm.count;
+    uint64_t top = 0;
+    for (int base = 0; base < count; base += kWave - (kTopK - 1)) {
+      uint64_t v = 0;
+      if (lane < kTopK - 1) {
+        v = top;
+      } else {
+        const int idx = base + lane - (kTopK - 1);
+        if (idx < count) v = sm.cand[idx];
+      }
+      top = wave_sort_desc(v, lane);
+    }
+    // 5. 15 winners ascending by block id, then the recent block
+    const int myj = lane < kTopK - 1 ? key_block(top) : 0x7fffffff;
+    int rank = 0;
+#pragma unroll
+    for (int m = 0; m < kTopK - 1; ++m) {
+      const int other = __shfl(myj, m);
+      rank += other < myj ? 1 : 0;
+    }
+    if (lane < kTopK - 1) out[rank] = myj;
+    if (lane == kTopK - 1) out[kTopK - 1] = r;
+  }
+  __syncthreads();
+}
+
+}  // namespace msa

@@ -164,11 +164,15 @@ def alloc_outputs(w):
     return out, sel
 
 
-def alloc_workspace(shape: MsaShape, device, attn_only: bool = False) -> torch.Tensor:
+def alloc_workspace(shape: MsaShape, device, attn_only: bool = False):
+    """Workspace for msa_decode (the fp32 block scores); None for the
+    stand-alone attention, which needs none."""
     n = msa_attn_workspace_size(shape) if attn_only else msa_workspace_size(shape)
-    if n == 0 and shape.num_seqs > 0:
-        raise MsaError(MSA_ERR_INVALID_ARGUMENT, "workspace size", last_error())
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    if n == 0:
+        if shape.num_seqs > 0 and not attn_only:
+            raise MsaError(MSA_ERR_INVALID_ARGUMENT, "workspace size", last_error())
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode(w, out=None, sel=None, workspace=None, stream=None):

@@ -101,9 +101,11 @@ typedef struct {
   const int32_t* seq_lens;
 } msa_cache;
 
-/* Bytes of device workspace msa_decode needs for this shape (256-B aligned
- * pointer expected).  msa_sparse_attn_decode needs msa_attn_workspace_size().
- * Returns 0 for an invalid shape (see msa_last_error()). */
+/* Bytes of device workspace msa_decode needs for this shape: the fp32 block
+ * scores [rows][num_kv_heads][max_blocks_per_seq], 256-B aligned.  Its
+ * contents need no initialisation.  Returns 0 for an invalid shape (see
+ * msa_last_error()).  msa_attn_workspace_size() is 0: the stand-alone
+ * attention merges its split work on chip and needs no workspace. */
 size_t msa_workspace_size(const msa_shape* shape);
 size_t msa_attn_workspace_size(const msa_shape* shape);
 
@@ -137,15 +139,18 @@ msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const
  *   q          bf16 [rows][num_q_heads][128]; head h uses KV head h / 4
  *   sel_blocks int32 [rows][num_kv_heads][16] logical ids (-1 = none)
  *   out        fp32 [rows][num_q_heads][128]
- *   workspace  device buffer of >= msa_attn_workspace_size(shape) bytes
- * Keys: tokens t <= pos of the listed blocks; logits sm_scale * q.k. */
+ *   workspace  unused (msa_attn_workspace_size() == 0); may be NULL
+ * Keys: tokens t <= pos of the listed blocks; logits sm_scale * q.k.  Ids
+ * outside [0, pos/128] contribute nothing; a row left with no keys outputs 0. */
 msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache, const void* q,
                                   const int32_t* sel_blocks, float* out, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
-/* The fused path: steps 1-4 in one call, no host synchronisation.
- *   sel_blocks may be NULL (then kept inside the workspace).
- *   workspace  >= msa_workspace_size(shape) bytes. */
+/* The fused path: steps 1-4 in one call (two launches: the index scan fused
+ * with the block max-pool, then the selection fused with the attention), no
+ * host synchronisation.
+ *   sel_blocks int32 [rows][num_kv_heads][16], or NULL if not wanted.
+ *   workspace  >= msa_workspace_size(shape) bytes, 256-B aligned. */
 msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
                       int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
