@@ -77,6 +77,29 @@ def cpu_baseline(w, sample_seqs: int, t_gpu_us: float):
 
 
 COPY_BYTES = 512 << 20
+SCAN_SOURCES = ("indexer_scan.hip", "msa_device.hpp", "msa_kernels.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_paged_b32_128k_traffic.json")
+
+
+def scan_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_msa_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def scan_traffic():
+    """HBM bytes per scan launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (each scaled by what the counter read for a plain copy of
+    known size), or None if the scan's sources changed since."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != scan_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def run_counter_pass(args, w, copies, shape, caches):
@@ -178,14 +201,7 @@ def main():
     log(f"[bench] step {us_step:.1f} us ({step_gbps:.0f} GB/s algorithmic, {nb['total'] / 1e6:.1f} MB), "
         f"scan {scan_us:.1f} us ({scan_gbps:.0f} GB/s, {sb / 1e6:.1f} MB), host wall {wall / args.steps * 1e6:.1f} us")
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "scan_paged_b32_128k_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            traffic = json.load(open(tfile)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
-
+    traffic = scan_traffic()
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()

@@ -1,4 +1,4 @@
-// block_topk.hip - stand-alone block selection: one 256-thread workgroup per
+// block_topk.hip - stand-alone block selection: one 1024-thread workgroup per
 // (query row, group) running the exact selection of select_device.hpp
 // (recent block + top 15 of the earlier blocks by score desc, index asc).
 #include "msa_device.hpp"
@@ -8,7 +8,7 @@
 namespace msa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 
 __global__ __launch_bounds__(kThreads) void block_topk_kernel(const int32_t* __restrict__ seq_lens,
                                                               const float* __restrict__ block_scores,

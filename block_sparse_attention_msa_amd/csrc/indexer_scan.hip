@@ -37,8 +37,10 @@ struct ScanGeom {
   static constexpr int kChunk = 16;                                // loads in flight per wave
 };
 
+constexpr int kScanWaves = 8;
+
 template <bool FP8>
-__global__ __launch_bounds__(256) void scan_decode_kernel(const uint8_t* __restrict__ idx_pool,
+__global__ __launch_bounds__(kScanWaves * kWave) void scan_decode_kernel(const uint8_t* __restrict__ idx_pool,
                                                           const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seq_lens,
                                                           const uint16_t* __restrict__ iq,
@@ -118,11 +120,11 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(const uint8_t* __restr
 }  // namespace
 
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
-  // Enough waves to cover the chip several times over, a few pages per wave.
+  // 8-wave workgroups, 1-2 pages per wave: measured best on the batch-32 x
+  // 128K workload (2 pages per wave: 82 us vs 84-88 us for 1, 4, 8 or 16).
   const long long total_blocks = (long long)a.num_seqs * a.mbps;
-  int bpw = (int)(total_blocks / 8192);
-  bpw = bpw < 1 ? 1 : (bpw > 8 ? 8 : bpw);
-  const int waves_per_wg = 4;
+  const int bpw = total_blocks >= 16384 ? 2 : 1;
+  constexpr int waves_per_wg = kScanWaves;
   dim3 grid((a.mbps + waves_per_wg * bpw - 1) / (waves_per_wg * bpw), a.num_seqs);
   dim3 block(waves_per_wg * kWave);
   if (a.idx_fp8)

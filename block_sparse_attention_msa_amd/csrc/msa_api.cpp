@@ -6,7 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/msa.h"
+#include "msa.h"
 #include "msa_kernels.hpp"
 
 static_assert(MSA_MAX_BLOCKS_PER_SEQ == msa::kMaxBlocksPerSeq, "block limit mismatch");

@@ -78,6 +78,10 @@ __device__ __forceinline__ float reduce4_permuted(float a0, float a1, float a2, 
   return a0;
 }
 
+// 2^x on the hardware exponential (v_exp_f32), for x <= 0 (softmax weights):
+// no range reduction needed; results below 2^-126 flush to 0.
+__device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wave_max_xor(float m, int from) {
   for (int off = from; off < kWave; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
   return m;

@@ -10,14 +10,15 @@
 // lower block index (total order: score descending, index ascending), which
 // makes the selection exact under any split of the candidates.
 //
-// Algorithm, NT threads:
-//  1. thread t takes blocks j = t + NT e (coalesced loads, all issued before
-//     use) as 64-bit keys (ordered score << 32 | ~j) and keeps its best;
-//  2. each wave sorts its 64 thread bests (bitonic, DPP lane moves where they
-//     exist); T_w = the wave's 15th best is a lower bound of the 15th best
+// Algorithm (one active wave per 1,024 candidate blocks, 16 keys per lane):
+//  1. wave w takes blocks j = 1024 w + lane + 64 e (e < 16; coalesced loads,
+//     all issued before use) as 64-bit keys (ordered score << 32 | ~j) and
+//     keeps each lane's best;
+//  2. each active wave sorts its 64 lane bests (bitonic, DPP lane moves where
+//     they exist); T_w = the wave's 15th best is a lower bound of the 15th best
 //     block overall, and so is T0 = max_w T_w;
-//  3. keys >= T0 (every true top-15 key among them; at most 15 threads' worth
-//     per wave) are compacted into LDS with ballots;
+//  3. keys >= T0 (every true top-15 key among them; at most 15 lanes x 16 keys
+//     per active wave) are compacted into LDS with ballots;
 //  4. wave 0 merges the candidates 49 at a time into a running top-15;
 //  5. the 15 ids plus the recent block are written in ascending order.
 #pragma once
@@ -26,9 +27,11 @@
 
 namespace msa {
 
-// Candidate bound: per wave at most 15 threads hold keys >= T0, each with at
-// most ceil(n / NT) keys; summed over NT/64 waves that is <= 15 * 16384 / 64.
-constexpr int kSelCandCap = (kTopK - 1) * (kMaxBlocksPerSeq / kWave) + kWave;
+constexpr int kSelKeysPerLane = 16;                               // keys per lane of an active wave
+constexpr int kSelBlocksPerWave = kWave * kSelKeysPerLane;         // 1,024
+// Candidate bound: per active wave at most 15 lanes hold keys >= T0, 16 keys
+// each; at most kMaxBlocksPerSeq / 1024 = 16 active waves.
+constexpr int kSelCandCap = (kTopK - 1) * kSelKeysPerLane * (kMaxBlocksPerSeq / kSelBlocksPerWave) + kWave;
 
 template <int NT>
 struct SelectSmem {
@@ -115,7 +118,8 @@ __device__ __forceinline__ void sel_append(uint64_t k, bool take, int lane, uint
   if (take) cand[base + __popcll(ballot & ((1ull << lane) - 1ull))] = k;
 }
 
-// Selection for one (row, group) by the whole workgroup of NT threads.
+// Selection for one (row, group) by a workgroup of NT threads (NT / 64 >= 16
+// waves, so every candidate fits the active waves' registers).
 // s: block scores of the row/group; r: the recent block (0 <= r < row length).
 // Writes 16 ids (ascending, -1 padded) to out[] (LDS or global) from wave 0,
 // then synchronises the workgroup so out[] is readable by every thread when
@@ -123,7 +127,7 @@ __device__ __forceinline__ void sel_append(uint64_t k, bool take, int lane, uint
 template <int NT>
 __device__ void select_blocks(const float* __restrict__ s, int r, SelectSmem<NT>& sm, int32_t* out) {
   constexpr int kWaves = NT / kWave;
-  constexpr int kRegKeys = 4096 / NT;  // keys held in registers per thread
+  static_assert(kWaves * kSelBlocksPerWave >= kMaxBlocksPerSeq, "too few waves for the largest row");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -133,41 +137,39 @@ __device__ void select_blocks(const float* __restrict__ s, int r, SelectSmem<NT>
     return;
   }
   const int n = r;  // candidates: blocks 0 .. r-1 (n >= 16)
+  const int active = (n + kSelBlocksPerWave - 1) / kSelBlocksPerWave;
+  const int j0 = wave * kSelBlocksPerWave + lane;
 
-  // 1. keys and the best key per thread (loads of in-range indices only)
-  float sv[kRegKeys];
-#pragma unroll
-  for (int e = 0; e < kRegKeys; ++e) sv[e] = s[min(tid + e * NT, n - 1)];
-  uint64_t keys[kRegKeys];
+  // 1. 16 keys per lane of the active waves, and each lane's best
+  uint64_t keys[kSelKeysPerLane];
   uint64_t best = 0;
+  if (wave < active) {
+    float sv[kSelKeysPerLane];
 #pragma unroll
-  for (int e = 0; e < kRegKeys; ++e) {
-    const int j = tid + e * NT;
-    keys[e] = j < n ? block_key(sv[e], j) : 0;
-    best = keys[e] > best ? keys[e] : best;
-  }
-  for (int j = tid + kRegKeys * NT; j < n; j += NT) {
-    const uint64_t k = block_key(s[j], j);
-    best = k > best ? k : best;
+    for (int e = 0; e < kSelKeysPerLane; ++e) sv[e] = s[min(j0 + e * kWave, n - 1)];
+#pragma unroll
+    for (int e = 0; e < kSelKeysPerLane; ++e) {
+      const int j = j0 + e * kWave;
+      keys[e] = j < n ? block_key(sv[e], j) : 0;
+      best = keys[e] > best ? keys[e] : best;
+    }
   }
 
-  // 2. T0 = max over waves of the wave's 15th best thread best (> 0: wave 0
-  //    has at least 16 threads holding keys)
-  const uint64_t sorted = wave_sort_desc(best, lane);
-  if (lane == kTopK - 2) sm.wave_t0[wave] = sorted;
+  // 2. T0 = max over active waves of the wave's 15th best lane best (wave 0
+  //    always has at least 16 lanes holding keys, so T0 > 0)
+  if (wave < active) {
+    const uint64_t sorted = wave_sort_desc(best, lane);
+    if (lane == kTopK - 2) sm.wave_t0[wave] = sorted;
+  }
   if (tid == 0) sm.count = 0;
   __syncthreads();
   uint64_t t0 = sm.wave_t0[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
+  for (int w = 1; w < active; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
 
   // 3. candidates >= T0 (absent keys are 0 and never qualify)
+  if (wave < active) {
 #pragma unroll
-  for (int e = 0; e < kRegKeys; ++e) sel_append(keys[e], keys[e] >= t0, lane, sm.cand, &sm.count);
-  for (int j0 = kRegKeys * NT; j0 < n; j0 += NT) {
-    const int j = j0 + tid;
-    const uint64_t k = j < n ? block_key(s[j], j) : 0;
-    sel_append(k, k >= t0, lane, sm.cand, &sm.count);
+    for (int e = 0; e < kSelKeysPerLane; ++e) sel_append(keys[e], keys[e] >= t0, lane, sm.cand, &sm.count);
   }
   __syncthreads();
 

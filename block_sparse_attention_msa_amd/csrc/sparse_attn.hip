@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     m_w = wave_max_xor(mx, Geo::kLanesPerToken);
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      const float p = exp2f(z[it] - m_w);
+      const float p = exp2_nonpos(z[it] - m_w);
       l_lane += p;
       if (owner) lds_p[wave][slot + it * Geo::kTokensPerIter][hh] = p;
     }
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
       for (int w = 0; w < kWaves; ++w) {
         const float mw = lds_ml[w][h][0];
         if (mw == -INFINITY) continue;
-        const float f = exp2f(mw - M);
+        const float f = exp2_nonpos(mw - M);
         float s = 0.f;
 #pragma unroll
         for (int sgi = 0; sgi < kSlotGroups; ++sgi) s += U.merge.o[w][sgi][h][d];
