@@ -119,6 +119,11 @@ msa::ScanArgs scan_args(const msa_shape* s, const msa_cache* c, const void* idx_
   return a;
 }
 
+// q_len == 1: the VALU decode scan; q_len > 1: the MFMA multi-query scan.
+hipError_t launch_scan(const msa_shape* s, const msa::ScanArgs& a, hipStream_t stream) {
+  return s->q_len == 1 ? msa::launch_scan_decode(a, stream) : msa::launch_scan_mq(a, s->q_len, stream);
+}
+
 msa_status check_aligned(const void* p, size_t a, const char* what) {
   if (((uintptr_t)p) % a) return fail(MSA_ERR_INVALID_ARGUMENT, "%s must be %zu-byte aligned", what, a);
   return MSA_OK;
@@ -146,11 +151,8 @@ msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, con
   if (!idx_q || !block_scores) return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q / block_scores is NULL");
   if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
   if ((st = check_aligned(idx_q, 16, "idx_q")) != MSA_OK) return st;
-  if (shape->q_len != 1)
-    return fail(MSA_ERR_UNSUPPORTED, "msa_indexer_score: q_len = %d (the index scan handles decode, q_len 1)",
-                shape->q_len);
   if (shape->num_seqs == 0) return ok();
-  return hip_status(msa::launch_scan_decode(scan_args(shape, cache, idx_q, block_scores), stream), "index scan");
+  return hip_status(launch_scan(shape, scan_args(shape, cache, idx_q, block_scores), stream), "index scan");
 }
 
 msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const float* block_scores,
@@ -192,8 +194,6 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
-  if (shape->q_len != 1)
-    return fail(MSA_ERR_UNSUPPORTED, "msa_decode: q_len = %d (multi-query path not available)", shape->q_len);
   const size_t need = msa_workspace_size(shape);
   if (shape->num_seqs > 0) {
     if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
@@ -206,7 +206,7 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   // 2 launches: index scan fused with the block max-pool, then selection
   // fused with attention (each attention workgroup selects its (row, group)).
   float* scores = static_cast<float*>(workspace);
-  hipError_t e = msa::launch_scan_decode(scan_args(shape, cache, idx_q, scores), stream);
+  hipError_t e = launch_scan(shape, scan_args(shape, cache, idx_q, scores), stream);
   if (e != hipSuccess) return hip_status(e, "index scan");
   e = msa::launch_sparse_attn(attn_args(shape, cache, q, scores, nullptr, sel_blocks, out), stream);
   return hip_status(e, "selection + sparse attention");

@@ -27,6 +27,8 @@ struct ScanArgs {
 };
 // Decode (one query row per sequence) index scan + block max-pool.
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream);
+// Multi-query (q_len > 1) index scores + causal block max-pool on MFMA.
+hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream);
 
 struct TopkArgs {
   const int32_t* seq_lens;

@@ -68,16 +68,11 @@ def _decode(shape, cache=None, q=FAKE, iq=FAKE, out=FAKE, sel=FAKE, ws=FAKE, nby
     (dict(k_scale=float("nan")), msa.MSA_ERR_INVALID_ARGUMENT),
     (dict(idx_scale=-1.0), msa.MSA_ERR_INVALID_ARGUMENT),
     (dict(q_len=2000, max_blocks_per_seq=8), msa.MSA_ERR_INVALID_ARGUMENT),
-    (dict(q_len=3), msa.MSA_ERR_UNSUPPORTED),  # multi-query decode entry not available yet
 ])
 def test_shape_validation(kw, code):
     assert _decode(_shape(**kw)) == code
     assert msa.last_error() != ""
-    size = msa.lib().msa_workspace_size(ctypes.byref(_shape(**kw)))
-    if kw.get("q_len") == 3:
-        assert size > 0   # a valid shape; only the entry point lacks the multi-query path
-    else:
-        assert size == 0  # invalid shapes have no workspace size
+    assert msa.lib().msa_workspace_size(ctypes.byref(_shape(**kw))) == 0  # invalid shapes have no size
 
 
 def test_null_and_pointer_validation():
@@ -125,8 +120,7 @@ def test_other_entry_points_validate():
     s = _shape()
     assert L.msa_indexer_score(ctypes.byref(s), ctypes.byref(_cache()), None, FAKE, None) == \
         msa.MSA_ERR_INVALID_ARGUMENT
-    assert L.msa_indexer_score(ctypes.byref(_shape(q_len=2)), ctypes.byref(_cache()), FAKE, FAKE, None) == \
-        msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_workspace_size(ctypes.byref(_shape(q_len=256))) == 2 * 256 * 4 * 8 * 4  # multi-query rows
     assert L.msa_block_topk(ctypes.byref(s), None, FAKE, FAKE, None) == msa.MSA_ERR_INVALID_ARGUMENT
     assert L.msa_sparse_attn_decode(ctypes.byref(s), ctypes.byref(_cache(v=None)), FAKE, FAKE, FAKE, FAKE, 1 << 30,
                                     None) == msa.MSA_ERR_INVALID_ARGUMENT

@@ -181,6 +181,26 @@ def test_paged_permutation_invariance(dev):
     assert np.array_equal(out0, out1)
 
 
+@pytest.mark.parametrize("kv,idx", [("nvfp4", "fp8"), ("bf16", "bf16")])
+@pytest.mark.parametrize("q_len", [2, 5, 9, 64])
+def test_multi_query_causal(dev, kv, idx, q_len):
+    """q_len > 1 (speculative verify / prefill chunk): every query row has its
+    own causal position, block scores, selection and attention; the scan runs
+    on MFMA.  Ragged lengths, a padded row, rows that do not fill an MFMA tile."""
+    lens = [q_len + 1, 127 + q_len, 2177, 0, 16 * 128 + q_len, 5000]
+    w = synth.make_workload(seq_lens=lens, q_len=q_len, kv_dtype=kv, idx_dtype=idx, plant=3, layout="paged",
+                            seed=30 + q_len, device=dev, max_blocks_per_seq=48)
+    out, sel, bs = check_workload(w, label=f"multi-query q_len={q_len} {kv}/{idx}")
+    pad = 3 * q_len
+    assert (out[pad:pad + q_len] == 0).all() and (sel[pad:pad + q_len] == -1).all()
+
+
+def test_verify_b2_q256_128k_config_sampled(dev):
+    """The multi-query verify chunk: 2 sequences x 256 new tokens on 128K."""
+    w = synth.make_config("verify_b2_q256_128k", device=dev)
+    check_workload(w, rows=[0, 1, 2, 130, 255, 256, 300, 511])
+
+
 def test_deterministic(dev):
     w = synth.make_workload(seq_lens=[30000, 12000, 640], plant=4, seed=25, device=dev)
     a = run_all(w)
