@@ -77,7 +77,7 @@ def cpu_baseline(w, sample_seqs: int, t_gpu_us: float):
 
 
 COPY_BYTES = 512 << 20
-SCAN_SOURCES = ("indexer_scan.hip", "msa_device.hpp", "msa_kernels.hpp")
+SCAN_SOURCES = ("indexer_scan.hip", "scan_device.hpp", "msa_device.hpp", "msa_kernels.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_paged_b32_128k_traffic.json")
 
 

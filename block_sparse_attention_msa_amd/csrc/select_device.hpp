@@ -146,7 +146,9 @@ __device__ void select_blocks(const float* __restrict__ s, int r, SelectSmem<NT>
   if (wave < active) {
     float sv[kSelKeysPerLane];
 #pragma unroll
-    for (int e = 0; e < kSelKeysPerLane; ++e) sv[e] = s[min(j0 + e * kWave, n - 1)];
+    for (int e = 0; e < kSelKeysPerLane; ++e) {
+      sv[e] = s[min(j0 + e * kWave, n - 1)];
+    }
 #pragma unroll
     for (int e = 0; e < kSelKeysPerLane; ++e) {
       const int j = j0 + e * kWave;

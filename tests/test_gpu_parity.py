@@ -201,6 +201,55 @@ def test_verify_b2_q256_128k_config_sampled(dev):
     check_workload(w, rows=[0, 1, 2, 130, 255, 256, 300, 511])
 
 
+def test_workspace_reuse_across_calls_and_shapes(dev):
+    """One workspace (uninitialised, larger than needed), consecutive decode
+    calls on different data and shapes: no call sees another's scores."""
+    msa = _msa()
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device=dev)
+    cases = [dict(seq_lens=[9000, 4000, 129], seed=40), dict(seq_lens=[9000, 4000, 129], seed=41),
+             dict(seq_lens=[3000, 0, 20000, 777, 128 * 17], seed=42), dict(seq_lens=[9000, 4000, 129], seed=40)]
+    for c in cases:
+        w = synth.make_workload(plant=3, layout="paged", device=dev, **c)
+        shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+        out, sel = msa.alloc_outputs(w)
+        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+        torch.cuda.synchronize()
+        P = oracle.Problem.from_workload(w)
+        o, s_ = out.cpu().numpy(), sel.cpu().numpy()
+        for row in range(w.rows):
+            check_row(P, row, o[row], s_[row])
+
+
+def test_graph_capture_replays(dev):
+    """msa_decode captured in a HIP graph: every replay (with eager work and
+    synchronisation in between) equals the eager result bit for bit."""
+    msa = _msa()
+    w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", seed=43, device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    out, sel = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+    torch.cuda.synchronize()
+    ref_out, ref_sel = out.clone(), sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), rep
+        assert torch.equal(sel, ref_sel), rep
+        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)  # eager call between replays
+        torch.cuda.synchronize()
+
+
 def test_deterministic(dev):
     w = synth.make_workload(seq_lens=[30000, 12000, 640], plant=4, seed=25, device=dev)
     a = run_all(w)
