@@ -1,6 +1,6 @@
 // attn_device.hpp - one workgroup of the exact GQA attention over the kept
-// blocks of one (query row, group, head pair), optionally preceded by the
-// exact block selection of that (row, group).
+// blocks of one (query row, group), all four query heads of the group,
+// optionally preceded by the exact block selection of that (row, group).
 //
 // Method ("MSA basics", vLLM MiniMax-M3.1-Flash post: the main attention runs
 // exactly, but only over the kept blocks, and every query head of a GQA group
@@ -9,49 +9,42 @@
 // restricted to the selected set, computed with an online softmax over split
 // work whose partial outputs are merged).
 //
-// One 1024-thread workgroup per (row, group, head pair).  Each of the 16 waves
-// takes one of the 16 kept blocks, and the waves' partial (o, m, l) are merged
-// by log-sum-exp in LDS, so every head's softmax completes inside one
-// workgroup and the output is written directly (no cross-workgroup merge).
-// Full K/V is read only for the kept blocks, straight from the paged pool.
+// One 1024-thread workgroup per (row, group).  Each of the 16 waves takes one
+// of the 16 kept blocks; the waves' partial (o, m, l) are merged by
+// log-sum-exp in LDS, so each head's softmax completes inside the workgroup
+// and the output is written directly.  K/V are read only for the kept blocks,
+// straight from the paged pool, and dequantised once for all four heads.
 //
-// Per wave and block (NVFP4 K/V):
-//  * QK: lane = (token slot, 16-dim chunk); all 16 wave-loads of the block's K
-//    (8 tokens x 64 B of packed E2M1 each, 512 B contiguous) are issued before
-//    use, and the block's 1 KB of E4M3 scales is transposed through LDS.
-//    E2M1 -> bf16 with v_cvt_scalef32_pk_bf16_fp4 (exact), dot with the bf16
-//    query slices of the 2 heads on v_dot2c_f32_bf16, the chunk's E4M3 scale
-//    applied once per 16-element partial dot; K's tensor scale and sm_scale
-//    fold into the exp2 argument.  The 8-lane reduction of the 2 head partials
-//    costs 3 DPP adds (lane-dependent head order).
-//  * softmax over the wave's block, p = exp2(z - m) stored to LDS;
-//  * PV: V loads issued before the softmax; E2M1 -> f32 pairs, the E4M3 scale
-//    folded into p, fp32 FMAs into 2 heads x 16 dims per lane; token-slot pairs
-//    summed with one DPP add, the rest through LDS with the waves'
-//    exp2(m_w - M) weights.
+// gfx950 design, per wave and 128-token block (NVFP4 K/V):
+//  * QK on v_mfma_f32_16x16x32_bf16, 16 tokens per tile: A = K codes
+//    (E2M1 -> bf16 exact, one 16-byte load = 32 dims per lane), B = the bf16
+//    queries placed so that MFMA column (j, h) only sums the dims of scale
+//    group 2j (K steps 0-1) or 2j+1 (K steps 2-3) for head h.  The E4M3 group
+//    scales are then applied once per 16-dim partial dot (fp32), and the four
+//    group slots summed with two DPP adds: every product stays exact and the
+//    MFMA runs with all 16 columns in use.
+//  * softmax in registers (the block max per head is exact, so one block per
+//    wave needs no rescaling); p is stored to LDS as f16 (for bf16 K/V as a
+//    bf16 hi + lo pair, two MFMAs: a single bf16 p would carry 2^-9 relative
+//    error into outputs that cancel);
+//  * PV on v_mfma_f32_16x16x32_f16: A = p (rows = the 4 heads), B = V with
+//    the tokens on the contraction axis.  Each lane loads the same 8 dims of 8
+//    tokens (4 bytes each), regroups nibbles into token pairs with two
+//    bit-field merges per pair, converts (E2M1 -> f16 exact) and applies both
+//    tokens' E4M3 scales with one packed f16 multiply (code x scale has <= 6
+//    significant bits: exact in f16).  K's and V's tensor scales and sm_scale
+//    are applied in fp32 outside the MFMAs.
 #pragma once
-
-#include <type_traits>
 
 #include "msa_device.hpp"
 #include "select_device.hpp"
 
 namespace msa {
 
-template <bool FP4>
-struct AttnGeom {
-  static constexpr int kLanesPerToken = FP4 ? 8 : 16;
-  static constexpr int kLog2Lpt = FP4 ? 3 : 4;
-  static constexpr int kTokensPerIter = kWave / kLanesPerToken;  // 8 or 4
-  static constexpr int kIters = kBlock / kTokensPerIter;         // 16 or 32
-  static constexpr int kDimsPerLane = FP4 ? 16 : 8;
-  static constexpr int kPairs = kDimsPerLane / 2;
-  static constexpr int kRowBytes = FP4 ? kDim / 2 : kDim * 2;    // bytes per (token, head) row
-  static constexpr int kLaneBytes = FP4 ? kDimsPerLane / 2 : kDimsPerLane * 2;
-  using Vec = typename std::conditional<FP4, uint2, uint4>::type;  // one lane's bytes of one token
-  static constexpr int kChunk = FP4 ? 16 : 8;                        // loads issued together
-  static constexpr int kScaleBytes = FP4 ? kBlock * (kDim / 16) : 16;
-};
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // LDS written by some lanes of a wave and read by others of the same wave.
 __device__ __forceinline__ void wave_sync() {
@@ -62,295 +55,377 @@ __device__ __forceinline__ void wave_sync() {
 
 constexpr int kAttnThreads = 1024;
 constexpr int kAttnWaves = kAttnThreads / kWave;  // 16
-constexpr int kAttnHeads = 2;                         // query heads per workgroup
-constexpr int kAttnBlocksPerWave = kTopK / kAttnWaves;    // 1
-static_assert(kAttnBlocksPerWave == 1, "one kept block per wave");
-constexpr int kAttnHeadPairs = kHeadsPerGroup / kAttnHeads;
-constexpr int kAttnSlotGroups = 4;                    // token-slot groups left after the in-register step
-constexpr int kDppRowRor8 = 0x128;                // lane i reads lane (i+8) mod 16 of its row (= xor 8)
+static_assert(kTopK == kAttnWaves, "one kept block per wave");
+constexpr int kQkTiles = kBlock / 16;   // 16-token MFMA tiles per block
+constexpr int kPvSteps = kBlock / 32;   // 32-token MFMA contraction steps per block
 
 struct MergeSmem {
-  float o[kAttnWaves][kAttnSlotGroups][kAttnHeads][kDim];     // 64 KB
+  float o[kAttnWaves][kHeadsPerGroup][kDim];  // 32 KB
+  float m[kAttnWaves][kHeadsPerGroup];
+  float l[kAttnWaves][kHeadsPerGroup];
 };
 
-// Linear workgroup id -> (row, group, head pair).  Workgroups are dispatched
-// round-robin over the 8 XCDs (id % 8); the two head-pair workgroups of one
-// (row, group) get ids 8 apart so they share an XCD and its L2, and the second
-// read of the group's K/V blocks hits there.
-__device__ __forceinline__ void attn_decode_wg(int id, int& row, int& g, int& hp) {
-  const int x = id & 7;
-  hp = (id >> 3) & 1;
-  const int pair = (id >> 4) * 8 + x;
-  row = pair / kGroups;
-  g = pair % kGroups;
-}
-
-// 2 per-lane partial dots a0, a1 belong to heads (0 ^ (lane&1)) and (1 ^ (lane&1));
-// after the reduction over 2^LOG2 lanes, lanes whose bits 1..LOG2-1 are zero
-// hold the full dot of head (lane & 1).
-template <int LOG2>
-__device__ __forceinline__ float reduce2_permuted(float a0, float a1) {
-  a0 += dpp<kDppXor1>(a1);
-  a0 += dpp<kDppXor2>(a0);
-  a0 += dpp<kDppRowShl4>(a0);
-  if constexpr (LOG2 == 4) a0 += dpp<kDppRowShl8>(a0);
-  return a0;
-}
-
-template <bool FP4>
 struct AttnSmem {
   union {
     SelectSmem<kAttnThreads> sel;
     MergeSmem merge;
   } u;
-  float p[kAttnWaves][kBlock][kAttnHeads];                   // 16 KB
-  uint8_t sc[kAttnWaves][AttnGeom<FP4>::kScaleBytes];     // 16 KB (NVFP4 scales)
-  float ml[kAttnWaves][kAttnHeads][2];
+  uint16_t p[kAttnWaves][kHeadsPerGroup][kBlock];    // 16 KB: softmax weights (f16, or bf16 hi part)
+  uint16_t plo[kAttnWaves][kHeadsPerGroup][kBlock];  // 16 KB: bf16 lo part (bf16 K/V only)
+  uint8_t ksc[kAttnWaves][kBlock * 8];             // 16 KB: K scales [token][group]
+  uint8_t vsc[kAttnWaves][kBlock * 8];             // 16 KB: V scales [token pair][group][2]
   int32_t sel[kTopK];
 };
 
-// Selection (SELECT: from the block scores) and attention of (row, g, head pair hp).  Every thread of the
-// workgroup must call it.
-template <bool FP4, bool SELECT>
+// 16-dim group scales of 2 tokens (16 bytes: token a's 8, then token b's) ->
+// [group][a, b] byte pairs, tokens past the visible end zeroed (so their V
+// rows, whatever the bytes, contribute 0 x finite).
+__device__ __forceinline__ uint4 pair_scales(uint4 w, bool a_vis, bool b_vis) {
+  const uint32_t a0 = a_vis ? w.x : 0u, a1 = a_vis ? w.y : 0u;
+  const uint32_t b0 = b_vis ? w.z : 0u, b1 = b_vis ? w.w : 0u;
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(b0, a0, 0x05010400u);  // groups 0, 1
+  r.y = __builtin_amdgcn_perm(b0, a0, 0x07030602u);  // groups 2, 3
+  r.z = __builtin_amdgcn_perm(b1, a1, 0x05010400u);  // groups 4, 5
+  r.w = __builtin_amdgcn_perm(b1, a1, 0x07030602u);  // groups 6, 7
+  return r;
+}
+
+// The two E2M1 nibbles of byte k of w -> two f16 (exact), k a constant after unrolling.
+__device__ __forceinline__ f16x2 e2m1x2_to_f16x2(uint32_t w, int k) {
+  switch (k) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
+template <bool FP4>
+struct PvType;
+template <>
+struct PvType<true> {  // NVFP4 V: exact in f16
+  using Vec8 = f16x8;
+  static __device__ __forceinline__ uint16_t pack(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+  static __device__ __forceinline__ float unpack(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+  static __device__ __forceinline__ f32x4 mfma(Vec8 a, Vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct PvType<false> {  // bf16 V
+  using Vec8 = bf16x8;
+  static __device__ __forceinline__ uint16_t pack(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+  static __device__ __forceinline__ float unpack(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+  static __device__ __forceinline__ f32x4 mfma(Vec8 a, Vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Selection (SELECT: from the block scores) and attention of (row, g) for
+// output dims [part * 128 / DSPLIT, (part + 1) * 128 / DSPLIT).  The DSPLIT
+// workgroups of one (row, g) repeat the selection and the softmax (identical,
+// deterministic) and split the PV work; part 0 writes the selected ids.
+// Every thread of the workgroup must call it.
+template <bool FP4, bool SELECT, int DSPLIT>
 __device__ __forceinline__ void attn_workgroup(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
     int32_t* __restrict__ sel_out, float* __restrict__ out, int q_len, int mbps, float qk_scale_log2, float v_scale,
-    int row, int g, int hp, AttnSmem<FP4>& sm) {
-  using Geo = AttnGeom<FP4>;
-  constexpr int DPL = Geo::kDimsPerLane;
-  constexpr int ITERS = Geo::kIters;
-  auto& U = sm.u;
-  auto& lds_p = sm.p;
-  auto& lds_sc = sm.sc;
-  auto& lds_ml = sm.ml;
-  auto& lds_sel = sm.sel;
+    int row, int g, int part, AttnSmem& sm) {
+  static_assert(DSPLIT == 1 || DSPLIT == 2 || DSPLIT == 4, "output split");
+  using PV = PvType<FP4>;
+  constexpr int kRowBytes = FP4 ? kDim / 2 : kDim * 2;  // bytes per (token, head) row
+  constexpr int kDims = kDim / DSPLIT;                  // output dims of this workgroup
+  constexpr int kTiles = kDims / 16;                    // 16-column PV output tiles (8, 4, 2)
+  constexpr int kLaneDims = kTiles;                     // consecutive dims per lane (one scale group)
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int b = row / q_len;
   const int L = seq_lens[b];
-  const int head0 = g * kHeadsPerGroup + hp * kAttnHeads;   // first query head of this workgroup
+  const int head0 = g * kHeadsPerGroup;
+  const int dbase = part * kDims;
   float* out_row = out + ((size_t)row * (kGroups * kHeadsPerGroup) + head0) * kDim;
+  int32_t* sel_row = (sel_out && part == 0) ? sel_out + ((size_t)row * kGroups + g) * kTopK : nullptr;
 
   if (L <= 0) {  // padded row
-    if (tid < kAttnHeads * kDim) out_row[tid] = 0.f;
-    if (SELECT && sel_out && hp == 0 && tid < kTopK) sel_out[((size_t)row * kGroups + g) * kTopK + tid] = -1;
+    if (tid < kHeadsPerGroup * kDims) out_row[(tid / kDims) * kDim + dbase + tid % kDims] = 0.f;
+    if (SELECT && sel_row && tid < kTopK) sel_row[tid] = -1;
     return;
   }
   const int pos = L - q_len + row % q_len;
   if constexpr (SELECT) {
     const int r = min(pos / kBlock, mbps - 1);
-    select_blocks<kAttnThreads>(block_scores + ((size_t)row * kGroups + g) * mbps, r, U.sel, lds_sel);
-    if (sel_out && hp == 0 && tid < kTopK) sel_out[((size_t)row * kGroups + g) * kTopK + tid] = lds_sel[tid];
+    select_blocks<kAttnThreads>(block_scores + ((size_t)row * kGroups + g) * mbps, r, sm.u.sel, sm.sel);
+    if (sel_row && tid < kTopK) sel_row[tid] = sm.sel[tid];
   } else {
-    if (tid < kTopK) lds_sel[tid] = sel_in[((size_t)row * kGroups + g) * kTopK + tid];
+    if (tid < kTopK) sm.sel[tid] = sel_in[((size_t)row * kGroups + g) * kTopK + tid];
     __syncthreads();
   }
 
-  const int chunk = lane & (Geo::kLanesPerToken - 1);
-  const int slot = lane / Geo::kLanesPerToken;
-  const bool owner = chunk < kAttnHeads;   // holds a full (token, head) logit after the reduction
-  const int hh = lane & 1;             // that head, within the pair
+  // MFMA lane roles: quarter c = lane / 16, column n = lane % 16.  QK column
+  // n = (head hq, group slot jj); the 4 slots of a head sit in one DPP quad.
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int hq = n >> 2;
+  const int jj = n & 3;
+  const int d0 = dbase + kLaneDims * n;  // PV: this lane's first output dim
 
-  int j = lds_sel[wave];
+  int j = sm.sel[wave];
   // ids outside the row's visible blocks or the table contribute nothing
   if (j >= mbps || j * kBlock > pos) j = -1;
 
-  float m_w = -INFINITY;
-  float l_lane = 0.f;
+  float m_w = -INFINITY, l_w = 0.f;  // head hq
+  f32x4 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   if (j >= 0) {  // wave-uniform
-    using Vec = typename Geo::Vec;
-    constexpr int CHUNK = Geo::kChunk;
     const int64_t page = block_table[(size_t)b * mbps + j];
     const int64_t row0 = (page * kGroups + g) * kBlock;  // first (token, head) row of this page/head
-    const int visible = pos - j * kBlock + 1;             // tokens 0..visible-1 are keys (>= 1)
-    const uint8_t* kbase = kpool + row0 * Geo::kRowBytes + slot * Geo::kRowBytes + chunk * Geo::kLaneBytes;
-    const uint8_t* vbase = vpool + row0 * Geo::kRowBytes + slot * Geo::kRowBytes + chunk * Geo::kLaneBytes;
-    constexpr int kIterStride = Geo::kTokensPerIter * Geo::kRowBytes;  // bytes between iterations
+    const int nvis = min(pos - j * kBlock + 1, kBlock);   // keys: tokens 0..nvis-1 (>= 1)
+    const uint8_t* kbase = kpool + row0 * kRowBytes;
+    const uint8_t* vbase = vpool + row0 * kRowBytes;
 
-    // ---- issue every K load of the first chunk (all of them for NVFP4) before any use
-    Vec kb[CHUNK];
-#pragma unroll
-    for (int i = 0; i < CHUNK; ++i) kb[i] = *reinterpret_cast<const Vec*>(kbase + i * kIterStride);
-    uint4 sc16 = make_uint4(0, 0, 0, 0);
-    if constexpr (FP4) sc16 = *reinterpret_cast<const uint4*>(k_sf + row0 * (kDim / 16) + lane * 16);
-
-    uint32_t qr[kAttnHeads][Geo::kPairs];
-#pragma unroll
-    for (int k = 0; k < kAttnHeads; ++k) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(
-          q + ((size_t)row * (kGroups * kHeadsPerGroup) + head0 + (k ^ hh)) * kDim + chunk * DPL);
-#pragma unroll
-      for (int p = 0; p < Geo::kPairs; ++p) qr[k][p] = src[p];
-    }
-    // the block's 1 KB of E4M3 scales, transposed through LDS: the scale of
-    // (token slot + 8 it, chunk) is byte 64 it + lane
+    // ---- issue the K loads (NVFP4: the whole block, 16 B per lane and tile)
+    [[maybe_unused]] uint4 kv[kQkTiles];
     if constexpr (FP4) {
-      *reinterpret_cast<uint4*>(&lds_sc[wave][lane * 16]) = sc16;
+#pragma unroll
+      for (int T = 0; T < kQkTiles; ++T)
+        kv[T] = *reinterpret_cast<const uint4*>(kbase + (size_t)(16 * T + n) * kRowBytes + 16 * c);
+    }
+    uint4 ks16 = make_uint4(0, 0, 0, 0), vs16 = make_uint4(0, 0, 0, 0);
+    if constexpr (FP4) {
+      ks16 = *reinterpret_cast<const uint4*>(k_sf + row0 * 8 + lane * 16);
+      vs16 = *reinterpret_cast<const uint4*>(v_sf + row0 * 8 + lane * 16);
+    }
+    // B operands: column (hq, jj) takes head hq's dims 32c + 8s + e when jj == c
+    bf16x8 qb[4];
+    {
+      const uint16_t* qh = q + ((size_t)row * (kGroups * kHeadsPerGroup) + head0 + hq) * kDim + 32 * c;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 w = jj == c ? *reinterpret_cast<const uint4*>(qh + 8 * s) : make_uint4(0, 0, 0, 0);
+        qb[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    if constexpr (FP4) {
+      *reinterpret_cast<uint4*>(&sm.ksc[wave][lane * 16]) = ks16;
+      *reinterpret_cast<uint4*>(&sm.vsc[wave][lane * 16]) = pair_scales(vs16, 2 * lane < nvis, 2 * lane + 1 < nvis);
       wave_sync();
     }
 
-    // ---- QK
-    float z[ITERS];
+    // ---- QK: z[T] = logit (log2 domain) of token 16T + 4c + jj, head hq
+    float z[kQkTiles];
 #pragma unroll
-    for (int c0 = 0; c0 < ITERS; c0 += CHUNK) {
-      if (c0 > 0) {
+    for (int T = 0; T < kQkTiles; ++T) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FP4) {
+        const uint32_t w[4] = {kv[T].x, kv[T].y, kv[T].z, kv[T].w};
+        bf16x8 ka[4];
 #pragma unroll
-        for (int i = 0; i < CHUNK; ++i) kb[i] = *reinterpret_cast<const Vec*>(kbase + (c0 + i) * kIterStride);
-      }
-#pragma unroll
-      for (int i = 0; i < CHUNK; ++i) {
-        const int it = c0 + i;
-        float a0 = 0.f, a1 = 0.f;
-        if constexpr (FP4) {
-          const uint32_t ws[2] = {kb[i].x, kb[i].y};
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const bf16x2 e0 = e2m1x2_to_bf16x2<0>(ws[d]);
-            const bf16x2 e1 = e2m1x2_to_bf16x2<1>(ws[d]);
-            const bf16x2 e2 = e2m1x2_to_bf16x2<2>(ws[d]);
-            const bf16x2 e3 = e2m1x2_to_bf16x2<3>(ws[d]);
-            a0 = dot2(e0, as_bf16x2(qr[0][4 * d + 0]), a0);
-            a1 = dot2(e0, as_bf16x2(qr[1][4 * d + 0]), a1);
-            a0 = dot2(e1, as_bf16x2(qr[0][4 * d + 1]), a0);
-            a1 = dot2(e1, as_bf16x2(qr[1][4 * d + 1]), a1);
-            a0 = dot2(e2, as_bf16x2(qr[0][4 * d + 2]), a0);
-            a1 = dot2(e2, as_bf16x2(qr[1][4 * d + 2]), a1);
-            a0 = dot2(e3, as_bf16x2(qr[0][4 * d + 3]), a0);
-            a1 = dot2(e3, as_bf16x2(qr[1][4 * d + 3]), a1);
-          }
-          const float sc = e4m3_to_f32(lds_sc[wave][it * kWave + lane]);
-          a0 *= sc;
-          a1 *= sc;
-        } else {
-          const uint32_t ws[4] = {kb[i].x, kb[i].y, kb[i].z, kb[i].w};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            a0 = dot2(as_bf16x2(ws[d]), as_bf16x2(qr[0][d]), a0);
-            a1 = dot2(as_bf16x2(ws[d]), as_bf16x2(qr[1][d]), a1);
-          }
+        for (int s = 0; s < 4; ++s) {
+          const bf16x2 e0 = e2m1x2_to_bf16x2<0>(w[s]);
+          const bf16x2 e1 = e2m1x2_to_bf16x2<1>(w[s]);
+          const bf16x2 e2 = e2m1x2_to_bf16x2<2>(w[s]);
+          const bf16x2 e3 = e2m1x2_to_bf16x2<3>(w[s]);
+          ka[s] = bf16x8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
         }
-        const float s = reduce2_permuted<Geo::kLog2Lpt>(a0, a1);
-        const int tok = slot + it * Geo::kTokensPerIter;
-        z[it] = tok < visible ? s * qk_scale_log2 : -INFINITY;
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0], qb[0], a0, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1], qb[1], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[2], qb[2], a1, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[3], qb[3], a1, 0, 0, 0);
+      } else {
+        const uint8_t* kr = kbase + (size_t)(16 * T + n) * kRowBytes + 64 * c;
+        uint4 w[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w[s] = *reinterpret_cast<const uint4*>(kr + 16 * s);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[0]), qb[0], a0, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[1]), qb[1], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[2]), qb[2], a1, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[3]), qb[3], a1, 0, 0, 0);
       }
+      // slot jj's partial of token 16T + 4c + i: groups 2jj (a0) and 2jj+1 (a1)
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FP4) {
+          const int tok = 16 * T + 4 * c + i;
+          const uint32_t sw = *reinterpret_cast<const uint16_t*>(&sm.ksc[wave][tok * 8 + 2 * jj]);
+          const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+          v[i] = fmaf(sc.x, a0[i], sc.y * a1[i]);
+        } else {
+          v[i] = a0[i] + a1[i];
+        }
+      }
+      // reduce-scatter over the quad: lane jj ends with the full dot of token i = jj
+      const bool b1 = (jj & 2) != 0, b0 = (jj & 1) != 0;
+      float y0 = b1 ? v[2] : v[0], y1 = b1 ? v[3] : v[1];
+      const float x0 = b1 ? v[0] : v[2], x1 = b1 ? v[1] : v[3];
+      y0 += dpp<kDppXor2>(x0);
+      y1 += dpp<kDppXor2>(x1);
+      const float keep = b0 ? y1 : y0, send = b0 ? y0 : y1;
+      const float dot = keep + dpp<kDppXor1>(send);
+      z[T] = 16 * T + 4 * c + jj < nvis ? dot * qk_scale_log2 : -INFINITY;
     }
 
-    // ---- issue the first chunk of V loads, then the softmax while they fly
-    Vec vb[CHUNK];
+    // ---- issue the V loads: lane (c, n) takes dims d0 .. d0 + kLaneDims - 1
+    //      of tokens 32s + 8c + e
+    [[maybe_unused]] uint32_t vw[kPvSteps][8];
+    [[maybe_unused]] uint4 vb[FP4 ? 1 : 8];
+    if constexpr (FP4) {
 #pragma unroll
-    for (int i = 0; i < CHUNK; ++i) vb[i] = *reinterpret_cast<const Vec*>(vbase + i * kIterStride);
-    if constexpr (FP4) sc16 = *reinterpret_cast<const uint4*>(v_sf + row0 * (kDim / 16) + lane * 16);
-
-    float mx = -INFINITY;
+      for (int s = 0; s < kPvSteps; ++s)
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) mx = fmaxf(mx, z[it]);
-    m_w = wave_max_xor(mx, Geo::kLanesPerToken);
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const float p = exp2_nonpos(z[it] - m_w);
-      l_lane += p;
-      if (owner) lds_p[wave][slot + it * Geo::kTokensPerIter][hh] = p;
+        for (int e = 0; e < 8; ++e) {
+          const uint8_t* src = vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + d0 / 2;
+          if constexpr (kLaneDims == 8)
+            vw[s][e] = *reinterpret_cast<const uint32_t*>(src);
+          else if constexpr (kLaneDims == 4)
+            vw[s][e] = *reinterpret_cast<const uint16_t*>(src);
+          else
+            vw[s][e] = *src;
+        }
     }
-    if constexpr (FP4) *reinterpret_cast<uint4*>(&lds_sc[wave][lane * 16]) = sc16;
+
+    // ---- softmax over the block (exact block max per head: no rescaling)
+    float mx = z[0];
+#pragma unroll
+    for (int T = 1; T < kQkTiles; ++T) mx = fmaxf(mx, z[T]);
+    mx = fmaxf(mx, dpp<kDppXor1>(mx));
+    mx = fmaxf(mx, dpp<kDppXor2>(mx));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    m_w = mx;  // >= one visible token, so finite
+    float ls = 0.f;
+#pragma unroll
+    for (int T = 0; T < kQkTiles; ++T) {
+      const float p = exp2_nonpos(z[T] - mx);
+      ls += p;
+      const uint16_t ph = PV::pack(p);
+      sm.p[wave][hq][16 * T + 4 * c + jj] = ph;
+      if constexpr (!FP4) sm.plo[wave][hq][16 * T + 4 * c + jj] = PV::pack(p - PV::unpack(ph));
+    }
+    ls += dpp<kDppXor1>(ls);
+    ls += dpp<kDppXor2>(ls);
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_w = ls;
     wave_sync();
 
     // ---- PV
-    float acc[kAttnHeads][DPL];
 #pragma unroll
-    for (int h = 0; h < kAttnHeads; ++h)
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) acc[h][d] = 0.f;
-#pragma unroll
-    for (int c0 = 0; c0 < ITERS; c0 += CHUNK) {
-      if (c0 > 0) {
-#pragma unroll
-        for (int i = 0; i < CHUNK; ++i) vb[i] = *reinterpret_cast<const Vec*>(vbase + (c0 + i) * kIterStride);
+    for (int s = 0; s < kPvSteps; ++s) {
+      // A: p of head n (rows 4..15 zero), tokens 32s + 8c + e
+      [[maybe_unused]] typename PV::Vec8 pa, pl;
+      {
+        const bool head = n < kHeadsPerGroup;
+        const uint4 w = head ? *reinterpret_cast<const uint4*>(&sm.p[wave][n][32 * s + 8 * c]) : make_uint4(0, 0, 0, 0);
+        pa = __builtin_bit_cast(typename PV::Vec8, w);
+        if constexpr (!FP4) {
+          const uint4 wl =
+              head ? *reinterpret_cast<const uint4*>(&sm.plo[wave][n][32 * s + 8 * c]) : make_uint4(0, 0, 0, 0);
+          pl = __builtin_bit_cast(typename PV::Vec8, wl);
+        }
       }
+      if constexpr (FP4) {
+        // token pairs (2p, 2p+1): nibble k of both tokens side by side in one byte
+        uint32_t lo[4], hi[4];
+        f16x2 sc[4];
 #pragma unroll
-      for (int i = 0; i < CHUNK; ++i) {
-        const int it = c0 + i;
-        const int tok = slot + it * Geo::kTokensPerIter;
-        const float2 p2 = *reinterpret_cast<const float2*>(&lds_p[wave][tok][0]);
-        float vv[DPL];
-        float ph[kAttnHeads] = {p2.x, p2.y};
-        if constexpr (FP4) {
-          const uint32_t ws[2] = {vb[i].x, vb[i].y};
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t x = vw[s][2 * p], y = vw[s][2 * p + 1];
+          lo[p] = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+          hi[p] = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+          const int pair = 16 * s + 4 * c + p;
+          const uint32_t sw = *reinterpret_cast<const uint16_t*>(&sm.vsc[wave][pair * 16 + 2 * (d0 >> 4)]);
+          sc[p] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+        }
+        // output tile t holds dims d0 + t
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const f32x2 e0 = e2m1x2_to_f32x2<0>(ws[d]);
-            const f32x2 e1 = e2m1x2_to_f32x2<1>(ws[d]);
-            const f32x2 e2 = e2m1x2_to_f32x2<2>(ws[d]);
-            const f32x2 e3 = e2m1x2_to_f32x2<3>(ws[d]);
-            vv[8 * d + 0] = e0.x; vv[8 * d + 1] = e0.y;
-            vv[8 * d + 2] = e1.x; vv[8 * d + 3] = e1.y;
-            vv[8 * d + 4] = e2.x; vv[8 * d + 5] = e2.y;
-            vv[8 * d + 6] = e3.x; vv[8 * d + 7] = e3.y;
+        for (int k = 0; k < kLaneDims / 2; ++k) {
+          f16x2 bl[4], bh[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            bl[p] = e2m1x2_to_f16x2(lo[p], k) * sc[p];
+            bh[p] = e2m1x2_to_f16x2(hi[p], k) * sc[p];
           }
-          const float vs = e4m3_to_f32(lds_sc[wave][it * kWave + lane]);
-          ph[0] *= vs;
-          ph[1] *= vs;
-        } else {
-          const uint32_t ws[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
+          const f16x8 b0 = {bl[0].x, bl[0].y, bl[1].x, bl[1].y, bl[2].x, bl[2].y, bl[3].x, bl[3].y};
+          const f16x8 b1 = {bh[0].x, bh[0].y, bh[1].x, bh[1].y, bh[2].x, bh[2].y, bh[3].x, bh[3].y};
+          acc[2 * k] = PV::mfma(pa, b0, acc[2 * k]);
+          acc[2 * k + 1] = PV::mfma(pa, b1, acc[2 * k + 1]);
+        }
+      } else {
+        // bf16 V: 8 tokens x kLaneDims dims; tokens past the end zeroed
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            vv[2 * d] = bf16lo_to_f32(ws[d]);
-            vv[2 * d + 1] = bf16hi_to_f32(ws[d]);
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 32 * s + 8 * c + e;
+          const uint8_t* src = vbase + (size_t)tok * kRowBytes + 2 * d0;
+          if constexpr (kLaneDims == 8) {
+            vb[e] = *reinterpret_cast<const uint4*>(src);
+          } else if constexpr (kLaneDims == 4) {
+            const uint2 t2 = *reinterpret_cast<const uint2*>(src);
+            vb[e] = make_uint4(t2.x, t2.y, 0, 0);
+          } else {
+            vb[e] = make_uint4(*reinterpret_cast<const uint32_t*>(src), 0, 0, 0);
           }
+          if (tok >= nvis) vb[e] = make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int h = 0; h < kAttnHeads; ++h)
+        for (int k = 0; k < kLaneDims / 2; ++k) {
+          uint32_t bl[4], bh[4];
 #pragma unroll
-          for (int d = 0; d < DPL; ++d) acc[h][d] = fmaf(ph[h], vv[d], acc[h][d]);
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t xa[4] = {vb[2 * p].x, vb[2 * p].y, vb[2 * p].z, vb[2 * p].w};
+            const uint32_t ya[4] = {vb[2 * p + 1].x, vb[2 * p + 1].y, vb[2 * p + 1].z, vb[2 * p + 1].w};
+            bl[p] = __builtin_amdgcn_perm(ya[k], xa[k], 0x05040100u);  // dim d0 + 2k of both tokens
+            bh[p] = __builtin_amdgcn_perm(ya[k], xa[k], 0x07060302u);  // dim d0 + 2k + 1
+          }
+          const uint4 w0 = make_uint4(bl[0], bl[1], bl[2], bl[3]);
+          const uint4 w1 = make_uint4(bh[0], bh[1], bh[2], bh[3]);
+          acc[2 * k] = PV::mfma(pa, __builtin_bit_cast(bf16x8, w0), acc[2 * k]);
+          acc[2 * k] = PV::mfma(pl, __builtin_bit_cast(bf16x8, w0), acc[2 * k]);
+          acc[2 * k + 1] = PV::mfma(pa, __builtin_bit_cast(bf16x8, w1), acc[2 * k + 1]);
+          acc[2 * k + 1] = PV::mfma(pl, __builtin_bit_cast(bf16x8, w1), acc[2 * k + 1]);
+        }
       }
     }
-
-    // ---- token slots -> 4 slot groups (FP4: pair slots s and s^1 with one DPP add)
-    if constexpr (FP4) {
-#pragma unroll
-      for (int h = 0; h < kAttnHeads; ++h)
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[h][d] += dpp<kDppRowRor8>(acc[h][d]);
-    }
-    const bool writer = FP4 ? (lane & 8) == 0 : true;
-    const int sg = lane >> 4;   // slot group 0..3
-    if (writer) {
-#pragma unroll
-      for (int h = 0; h < kAttnHeads; ++h)
-#pragma unroll
-        for (int d = 0; d < DPL; d += 4)
-          *reinterpret_cast<float4*>(&U.merge.o[wave][sg][h][chunk * DPL + d]) =
-              make_float4(acc[h][d], acc[h][d + 1], acc[h][d + 2], acc[h][d + 3]);
-    }
-    for (int off = Geo::kLanesPerToken; off < kWave; off <<= 1) l_lane += __shfl_xor(l_lane, off);
   }
-  if (lane < kAttnHeads) {  // owner lanes of slot 0: one per head
-    lds_ml[wave][hh][0] = m_w;
-    lds_ml[wave][hh][1] = l_lane;
+  __syncthreads();  // selection LDS is dead: the merge area reuses it
+
+  // ---- per-wave partials to LDS: lanes 0..15 hold heads 0..3 (acc rows) x dims d0 + t
+  if (c == 0) {
+#pragma unroll
+    for (int i = 0; i < kHeadsPerGroup; ++i) {
+      float* dst = &sm.u.merge.o[wave][i][d0];
+#pragma unroll
+      for (int t = 0; t < kTiles; t += 2) *reinterpret_cast<float2*>(dst + t) = make_float2(acc[t][i], acc[t + 1][i]);
+    }
+  }
+  if (c == 0 && jj == 0) {  // one lane per head hq
+    sm.u.merge.m[wave][hq] = m_w;
+    sm.u.merge.l[wave][hq] = l_w;
   }
   __syncthreads();
 
-  // ---- merge the waves and slot groups: thread -> (head, dim)
-  if (tid < kAttnHeads * kDim) {
-    const int h = tid / kDim;
-    const int d = tid % kDim;
+  // ---- merge the waves: thread -> (head, dim)
+  if (tid < kHeadsPerGroup * kDims) {
+    const int h = tid / kDims;
+    const int d = dbase + tid % kDims;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, lds_ml[w][h][0]);
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][h]);
     float o = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = lds_ml[w][h][0];
+        const float mw = sm.u.merge.m[w][h];
         if (mw == -INFINITY) continue;
         const float f = exp2_nonpos(mw - M);
-        float s = 0.f;
-#pragma unroll
-        for (int sgi = 0; sgi < kAttnSlotGroups; ++sgi) s += U.merge.o[w][sgi][h][d];
-        o = fmaf(f, s, o);
-        l = fmaf(f, lds_ml[w][h][1], l);
+        o = fmaf(f, sm.u.merge.o[w][h][d], o);
+        l = fmaf(f, sm.u.merge.l[w][h], l);
       }
     }
     out_row[h * kDim + d] = l > 0.f ? o * (v_scale / l) : 0.f;

@@ -18,7 +18,8 @@
 //     they exist); T_w = the wave's 15th best is a lower bound of the 15th best
 //     block overall, and so is T0 = max_w T_w;
 //  3. keys >= T0 (every true top-15 key among them; at most 15 lanes x 16 keys
-//     per active wave) are compacted into LDS with ballots;
+//     per active wave) are compacted into LDS with ballots (one LDS atomic
+//     per wave);
 //  4. wave 0 merges the candidates 49 at a time into a running top-15;
 //  5. the 15 ids plus the recent block are written in ascending order.
 #pragma once
@@ -108,14 +109,29 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
   return v;
 }
 
-// Appends the keys of this wave with take == true to cand[] (any order).
-__device__ __forceinline__ void sel_append(uint64_t k, bool take, int lane, uint64_t* cand, int* count) {
-  const uint64_t ballot = __ballot(take);
-  if (ballot == 0) return;
+// Appends this wave's keys[e] >= t0 (all E per lane) to cand[] (any order):
+// one ballot per key slot, their popcounts prefix-summed on the scalar unit,
+// and a single LDS atomic per wave.
+template <int E>
+__device__ __forceinline__ void sel_append(const uint64_t (&keys)[E], uint64_t t0, int lane, uint64_t* cand,
+                                           int* count) {
+  uint64_t ballot[E];
+  int total = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ballot[e] = __ballot(keys[e] >= t0);
+    total += __popcll(ballot[e]);
+  }
+  if (total == 0) return;
   int base = 0;
-  if (lane == 0) base = atomicAdd(count, __popcll(ballot));
+  if (lane == 0) base = atomicAdd(count, total);
   base = __shfl(base, 0);
-  if (take) cand[base + __popcll(ballot & ((1ull << lane) - 1ull))] = k;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (keys[e] >= t0) cand[base + __popcll(ballot[e] & below)] = keys[e];
+    base += __popcll(ballot[e]);
+  }
 }
 
 // Selection for one (row, group) by a workgroup of NT threads (NT / 64 >= 16
@@ -170,8 +186,7 @@ __device__ void select_blocks(const float* __restrict__ s, int r, SelectSmem<NT>
 
   // 3. candidates >= T0 (absent keys are 0 and never qualify)
   if (wave < active) {
-#pragma unroll
-    for (int e = 0; e < kSelKeysPerLane; ++e) sel_append(keys[e], keys[e] >= t0, lane, sm.cand, &sm.count);
+    sel_append(keys, t0, lane, sm.cand, &sm.count);
   }
   __syncthreads();
 

@@ -1,50 +1,88 @@
-// sparse_attn.hip - the stand-alone sparse attention kernel (selection fused
-// in the decode path, ids given in the stand-alone entry point); the body is
-// attn_device.hpp.
+// sparse_attn.hip - the sparse attention kernel (selection fused in the
+// decode path, ids given in the stand-alone entry point); the body is
+// attn_device.hpp.  One workgroup per (query row, group, output part).
 #include "attn_device.hpp"
 #include "msa_kernels.hpp"
 
 namespace msa {
 namespace {
 
-template <bool FP4, bool SELECT>
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  The DSPLIT
+// parts of one (row, group) get ids 8 apart, so they run on one XCD and the
+// repeated reads of the group's K blocks hit its L2.
+template <int DSPLIT>
+__device__ __forceinline__ void attn_decode_wg(int id, int& pair, int& part) {
+  const int x = id & 7;
+  const int k = id >> 3;
+  part = k % DSPLIT;
+  pair = (k / DSPLIT) * 8 + x;
+}
+
+template <bool FP4, bool SELECT, int DSPLIT>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
     int32_t* __restrict__ sel_out, float* __restrict__ out, int rows, int q_len, int mbps, float qk_scale_log2,
     float v_scale) {
-  __shared__ AttnSmem<FP4> sm;
-  int row, g, hp;
-  attn_decode_wg(blockIdx.x, row, g, hp);
-  if (row >= rows) return;  // grid padded to a multiple of 16 workgroups
-  attn_workgroup<FP4, SELECT>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores, sel_in,
-                                     sel_out, out, q_len, mbps, qk_scale_log2, v_scale, row, g, hp, sm);
+  __shared__ AttnSmem sm;
+  int pair, part;
+  attn_decode_wg<DSPLIT>(blockIdx.x, pair, part);
+  if (pair >= rows * kGroups) return;  // grid padded to a multiple of 8 (row, group) pairs
+  attn_workgroup<FP4, SELECT, DSPLIT>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores, sel_in,
+                                      sel_out, out, q_len, mbps, qk_scale_log2, v_scale, pair / kGroups,
+                                      pair % kGroups, part, sm);
 }
 
-template <bool SELECT>
-void launch(const AttnArgs& a, hipStream_t stream) {
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+template <bool FP4, bool SELECT, int DSPLIT>
+void launch3(const AttnArgs& a, hipStream_t stream) {
   const long long pairs = (long long)a.rows * kGroups;
-  dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * kAttnHeadPairs));
-  const uint8_t* kp = static_cast<const uint8_t*>(a.k);
-  const uint8_t* vp = static_cast<const uint8_t*>(a.v);
-  if (a.kv_nvfp4)
-    attn_kernel<true, SELECT><<<grid, kAttnThreads, 0, stream>>>(kp, vp, a.k_sf, a.v_sf, a.block_table, a.seq_lens, a.q,
-                                                             a.block_scores, a.sel, a.sel_out, a.out, a.rows, a.q_len, a.mbps,
-                                                             a.qk_scale_log2, a.v_scale);
+  const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * DSPLIT));
+  attn_kernel<FP4, SELECT, DSPLIT><<<grid, kAttnThreads, 0, stream>>>(
+      static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table, a.seq_lens,
+      a.q, a.block_scores, a.sel, a.sel_out, a.out, a.rows, a.q_len, a.mbps, a.qk_scale_log2, a.v_scale);
+}
+
+template <bool FP4, bool SELECT>
+void launch2(const AttnArgs& a, hipStream_t stream) {
+  // Split each (row, group) over 2 or 4 workgroups by output dims while that
+  // still leaves at least one workgroup per CU: few rows are latency-bound.
+  const long long pairs = (long long)a.rows * kGroups;
+  const int cus = device_cus();
+  if (pairs * 4 <= cus)
+    launch3<FP4, SELECT, 4>(a, stream);
+  else if (pairs * 2 <= cus)
+    launch3<FP4, SELECT, 2>(a, stream);
   else
-    attn_kernel<false, SELECT><<<grid, kAttnThreads, 0, stream>>>(kp, vp, a.k_sf, a.v_sf, a.block_table, a.seq_lens, a.q,
-                                                              a.block_scores, a.sel, a.sel_out, a.out, a.rows, a.q_len, a.mbps,
-                                                              a.qk_scale_log2, a.v_scale);
+    launch3<FP4, SELECT, 1>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
-  if (a.block_scores)
-    launch<true>(a, stream);
-  else
-    launch<false>(a, stream);
+  if (a.kv_nvfp4) {
+    if (a.block_scores)
+      launch2<true, true>(a, stream);
+    else
+      launch2<true, false>(a, stream);
+  } else {
+    if (a.block_scores)
+      launch2<false, true>(a, stream);
+    else
+      launch2<false, false>(a, stream);
+  }
   return hipGetLastError();
 }
 
