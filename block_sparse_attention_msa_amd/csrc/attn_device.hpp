@@ -46,13 +46,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// LDS written by some lanes of a wave and read by others of the same wave.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 constexpr int kAttnThreads = 1024;
 constexpr int kAttnWaves = kAttnThreads / kWave;  // 16
 static_assert(kTopK == kAttnWaves, "one kept block per wave");
@@ -75,6 +68,7 @@ struct AttnSmem {
   uint8_t ksc[kAttnWaves][kBlock * 8];             // 16 KB: K scales [token][group]
   uint8_t vsc[kAttnWaves][kBlock * 8];             // 16 KB: V scales [token pair][group][2]
   int32_t sel[kTopK];
+  int32_t page[kTopK];  // page ids of the kept blocks (fused selection)
 };
 
 // 16-dim group scales of 2 tokens (16 bytes: token a's 8, then token b's) ->
@@ -158,7 +152,8 @@ __device__ __forceinline__ void attn_workgroup(
   const int pos = L - q_len + row % q_len;
   if constexpr (SELECT) {
     const int r = min(pos / kBlock, mbps - 1);
-    select_blocks<kAttnThreads>(block_scores + ((size_t)row * kGroups + g) * mbps, r, sm.u.sel, sm.sel);
+    select_blocks<kAttnThreads, true>(block_scores + ((size_t)row * kGroups + g) * mbps,
+                                      block_table + (size_t)b * mbps, r, sm.u.sel, sm.sel, sm.page);
     if (sel_row && tid < kTopK) sel_row[tid] = sm.sel[tid];
   } else {
     if (tid < kTopK) sm.sel[tid] = sel_in[((size_t)row * kGroups + g) * kTopK + tid];
@@ -183,7 +178,7 @@ __device__ __forceinline__ void attn_workgroup(
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (j >= 0) {  // wave-uniform
-    const int64_t page = block_table[(size_t)b * mbps + j];
+    const int64_t page = SELECT ? sm.page[wave] : block_table[(size_t)b * mbps + j];
     const int64_t row0 = (page * kGroups + g) * kBlock;  // first (token, head) row of this page/head
     const int nvis = min(pos - j * kBlock + 1, kBlock);   // keys: tokens 0..nvis-1 (>= 1)
     const uint8_t* kbase = kpool + row0 * kRowBytes;
@@ -214,7 +209,7 @@ __device__ __forceinline__ void attn_workgroup(
     if constexpr (FP4) {
       *reinterpret_cast<uint4*>(&sm.ksc[wave][lane * 16]) = ks16;
       *reinterpret_cast<uint4*>(&sm.vsc[wave][lane * 16]) = pair_scales(vs16, 2 * lane < nvis, 2 * lane + 1 < nvis);
-      wave_sync();
+      wave_sync_lds();
     }
 
     // ---- QK: z[T] = logit (log2 domain) of token 16T + 4c + jj, head hq
@@ -313,7 +308,7 @@ __device__ __forceinline__ void attn_workgroup(
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
     l_w = ls;
-    wave_sync();
+    wave_sync_lds();
 
     // ---- PV
 #pragma unroll

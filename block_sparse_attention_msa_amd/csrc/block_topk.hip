@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kThreads) void block_topk_kernel(const int32_t* __r
   }
   const int pos = L - q_len + row % q_len;
   const int r = min(pos / kBlock, mbps - 1);  // recent block (clamped: never read past the row)
-  select_blocks<kThreads>(block_scores + ((size_t)row * kGroups + g) * mbps, r, sm, out);
+  select_blocks<kThreads, false>(block_scores + ((size_t)row * kGroups + g) * mbps, nullptr, r, sm, out, nullptr);
 }
 
 }  // namespace

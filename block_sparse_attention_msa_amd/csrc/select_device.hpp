@@ -12,16 +12,21 @@
 //
 // Algorithm (one active wave per 1,024 candidate blocks, 16 keys per lane):
 //  1. wave w takes blocks j = 1024 w + lane + 64 e (e < 16; coalesced loads,
-//     all issued before use) as 64-bit keys (ordered score << 32 | ~j) and
-//     keeps each lane's best;
-//  2. each active wave sorts its 64 lane bests (bitonic, DPP lane moves where
-//     they exist); T_w = the wave's 15th best is a lower bound of the 15th best
-//     block overall, and so is T0 = max_w T_w;
-//  3. keys >= T0 (every true top-15 key among them; at most 15 lanes x 16 keys
-//     per active wave) are compacted into LDS with ballots (one LDS atomic
-//     per wave);
-//  4. wave 0 merges the candidates 49 at a time into a running top-15;
-//  5. the 15 ids plus the recent block are written in ascending order.
+//     all issued before use) as 64-bit keys (ordered score << 32 | ~j), and,
+//     for the attention, the blocks' page ids from the block table;
+//  2. each active wave sorts its 64 lane-best scores (32-bit bitonic, DPP lane
+//     moves where they exist); the wave's 15th best score T_w bounds the 15th
+//     best key overall from below (15 distinct blocks reach it), and so does
+//     T0 = max_w T_w;
+//  3. keys whose score is >= T0 (every true top-15 key among them) are
+//     compacted into LDS with ballots, one LDS atomic per wave; a wave whose
+//     count exceeds 15 lanes x 16 keys (many scores tied at T0) uses its exact
+//     64-bit 15th-best lane key instead, which bounds its count again;
+//  4. wave 0 ranks up to 64 candidates by counting larger keys (broadcast LDS
+//     reads); more candidates are merged 49 at a time into a running top-15
+//     with a 64-bit bitonic sort;
+//  5. the 15 ids plus the recent block are written in ascending order, with
+//     their page ids when asked for.
 #pragma once
 
 #include "msa_device.hpp"
@@ -30,14 +35,16 @@ namespace msa {
 
 constexpr int kSelKeysPerLane = 16;                               // keys per lane of an active wave
 constexpr int kSelBlocksPerWave = kWave * kSelKeysPerLane;         // 1,024
-// Candidate bound: per active wave at most 15 lanes hold keys >= T0, 16 keys
-// each; at most kMaxBlocksPerSeq / 1024 = 16 active waves.
-constexpr int kSelCandCap = (kTopK - 1) * kSelKeysPerLane * (kMaxBlocksPerSeq / kSelBlocksPerWave) + kWave;
+constexpr int kSelWaveCap = (kTopK - 1) * kSelKeysPerLane;         // candidates per active wave, at most
+constexpr int kSelCandCap = kSelWaveCap * (kMaxBlocksPerSeq / kSelBlocksPerWave) + kWave;
 
 template <int NT>
 struct SelectSmem {
   uint64_t cand[kSelCandCap];
-  uint64_t wave_t0[NT / kWave];
+  int32_t cand_page[kSelCandCap];
+  uint32_t wave_t0[NT / kWave];
+  int32_t win[kTopK];
+  int32_t win_page[kTopK];
   int count;
 };
 
@@ -67,6 +74,8 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
     return (lane & 4) ? dn : up;
   } else if constexpr (J == 8) {
     return dpp_u32<0x128>(x);                       // row_ror:8 (= xor 8 in a row of 16)
+  } else if constexpr (J == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);  // bit-mask swizzle: lane ^ 16
   } else {
     return (uint32_t)__shfl_xor((int)x, J);
   }
@@ -109,111 +118,213 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
   return v;
 }
 
-// Appends this wave's keys[e] >= t0 (all E per lane) to cand[] (any order):
-// one ballot per key slot, their popcounts prefix-summed on the scalar unit,
-// and a single LDS atomic per wave.
-template <int E>
-__device__ __forceinline__ void sel_append(const uint64_t (&keys)[E], uint64_t t0, int lane, uint64_t* cand,
-                                           int* count) {
-  uint64_t ballot[E];
-  int total = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    ballot[e] = __ballot(keys[e] >= t0);
-    total += __popcll(ballot[e]);
-  }
-  if (total == 0) return;
+// LDS written by some lanes of a wave and read by others of the same wave.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_step32(uint32_t v, int lane) {
+  const uint32_t o = xor_lane<J>(v, lane);
+  const bool take_max = ((lane & J) == 0) == ((lane & K) == 0);
+  return take_max ? (o > v ? o : v) : (o < v ? o : v);
+}
+
+// Bitonic sort of one 32-bit value per lane, descending.
+__device__ __forceinline__ uint32_t wave_sort_desc32(uint32_t v, int lane) {
+  v = bitonic_step32<2, 1>(v, lane);
+  v = bitonic_step32<4, 2>(v, lane);
+  v = bitonic_step32<4, 1>(v, lane);
+  v = bitonic_step32<8, 4>(v, lane);
+  v = bitonic_step32<8, 2>(v, lane);
+  v = bitonic_step32<8, 1>(v, lane);
+  v = bitonic_step32<16, 8>(v, lane);
+  v = bitonic_step32<16, 4>(v, lane);
+  v = bitonic_step32<16, 2>(v, lane);
+  v = bitonic_step32<16, 1>(v, lane);
+  v = bitonic_step32<32, 16>(v, lane);
+  v = bitonic_step32<32, 8>(v, lane);
+  v = bitonic_step32<32, 4>(v, lane);
+  v = bitonic_step32<32, 2>(v, lane);
+  v = bitonic_step32<32, 1>(v, lane);
+  v = bitonic_step32<64, 32>(v, lane);
+  v = bitonic_step32<64, 16>(v, lane);
+  v = bitonic_step32<64, 8>(v, lane);
+  v = bitonic_step32<64, 4>(v, lane);
+  v = bitonic_step32<64, 2>(v, lane);
+  v = bitonic_step32<64, 1>(v, lane);
+  return v;
+}
+
+// Appends this wave's keys[e] >= thr (all E per lane) and their pages to
+// cand[] (any order): one ballot per key slot, the popcounts prefix-summed on
+// the scalar unit, one LDS atomic per wave.
+template <int E, bool PAGES>
+__device__ __forceinline__ void sel_append(const uint64_t (&keys)[E], const int32_t (&pages)[E], uint64_t thr,
+                                           uint64_t (&ballot)[E], int total, int lane, uint64_t* cand,
+                                           int32_t* cand_page, int* count) {
   int base = 0;
   if (lane == 0) base = atomicAdd(count, total);
   base = __shfl(base, 0);
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (keys[e] >= t0) cand[base + __popcll(ballot[e] & below)] = keys[e];
+    if (keys[e] >= thr) {
+      const int at = base + __popcll(ballot[e] & below);
+      cand[at] = keys[e];
+      if constexpr (PAGES) cand_page[at] = pages[e];
+    }
     base += __popcll(ballot[e]);
   }
 }
 
+template <int E>
+__device__ __forceinline__ int sel_ballots(const uint64_t (&keys)[E], uint64_t thr, uint64_t (&ballot)[E]) {
+  int total = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ballot[e] = __ballot(keys[e] >= thr);
+    total += __popcll(ballot[e]);
+  }
+  return total;
+}
+
 // Selection for one (row, group) by a workgroup of NT threads (NT / 64 >= 16
 // waves, so every candidate fits the active waves' registers).
-// s: block scores of the row/group; r: the recent block (0 <= r < row length).
-// Writes 16 ids (ascending, -1 padded) to out[] (LDS or global) from wave 0,
-// then synchronises the workgroup so out[] is readable by every thread when
-// it is in LDS.  Every thread of the workgroup must call it.
-template <int NT>
-__device__ void select_blocks(const float* __restrict__ s, int r, SelectSmem<NT>& sm, int32_t* out) {
+// s: block scores of the row/group; bt_row: its block table row (read only
+// when PAGES); r: the recent block (0 <= r < row length).  Writes 16 ids
+// (ascending, -1 padded) to out[] and, when PAGES, their page ids to
+// out_page[] (0 for padding), then synchronises the workgroup so LDS outputs
+// are readable by every thread.  Every thread of the workgroup must call it.
+template <int NT, bool PAGES>
+__device__ void select_blocks(const float* __restrict__ s, const int32_t* __restrict__ bt_row, int r,
+                              SelectSmem<NT>& sm, int32_t* out, int32_t* out_page) {
   constexpr int kWaves = NT / kWave;
   static_assert(kWaves * kSelBlocksPerWave >= kMaxBlocksPerSeq, "too few waves for the largest row");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   if (r + 1 <= kTopK) {  // every visible block is kept
-    if (tid < kTopK) out[tid] = tid <= r ? tid : -1;
+    if (tid < kTopK) {
+      out[tid] = tid <= r ? tid : -1;
+      if constexpr (PAGES) out_page[tid] = tid <= r ? bt_row[tid] : 0;
+    }
     __syncthreads();
     return;
   }
   const int n = r;  // candidates: blocks 0 .. r-1 (n >= 16)
   const int active = (n + kSelBlocksPerWave - 1) / kSelBlocksPerWave;
   const int j0 = wave * kSelBlocksPerWave + lane;
+  int32_t recent_page = 0;
+  if (PAGES && tid == kTopK - 1) recent_page = bt_row[r];
 
-  // 1. 16 keys per lane of the active waves, and each lane's best
+  // 1. 16 keys (and pages) per lane of the active waves, each lane's best score
   uint64_t keys[kSelKeysPerLane];
-  uint64_t best = 0;
+  int32_t pages[kSelKeysPerLane];
+  uint32_t best = 0;
   if (wave < active) {
     float sv[kSelKeysPerLane];
 #pragma unroll
     for (int e = 0; e < kSelKeysPerLane; ++e) {
-      sv[e] = s[min(j0 + e * kWave, n - 1)];
+      const int idx = min(j0 + e * kWave, n - 1);
+      sv[e] = s[idx];
+      pages[e] = PAGES ? bt_row[idx] : 0;
     }
 #pragma unroll
     for (int e = 0; e < kSelKeysPerLane; ++e) {
       const int j = j0 + e * kWave;
       keys[e] = j < n ? block_key(sv[e], j) : 0;
-      best = keys[e] > best ? keys[e] : best;
+      const uint32_t hi = (uint32_t)(keys[e] >> 32);
+      best = hi > best ? hi : best;
     }
   }
 
-  // 2. T0 = max over active waves of the wave's 15th best lane best (wave 0
-  //    always has at least 16 lanes holding keys, so T0 > 0)
+  // 2. T0 = max over active waves of the wave's 15th best lane-best score (wave
+  //    0 always has at least 16 lanes holding keys, so T0 > 0 and absent keys,
+  //    0, never qualify)
   if (wave < active) {
-    const uint64_t sorted = wave_sort_desc(best, lane);
+    const uint32_t sorted = wave_sort_desc32(best, lane);
     if (lane == kTopK - 2) sm.wave_t0[wave] = sorted;
   }
   if (tid == 0) sm.count = 0;
   __syncthreads();
-  uint64_t t0 = sm.wave_t0[0];
+  uint32_t t0 = sm.wave_t0[0];
   for (int w = 1; w < active; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
 
-  // 3. candidates >= T0 (absent keys are 0 and never qualify)
+  // 3. candidates: score >= T0, or, in a wave with too many ties at T0, key >=
+  //    the wave's exact 15th-best lane key
   if (wave < active) {
-    sel_append(keys, t0, lane, sm.cand, &sm.count);
+    uint64_t thr = (uint64_t)t0 << 32;
+    uint64_t ballot[kSelKeysPerLane];
+    int total = sel_ballots(keys, thr, ballot);
+    if (total > kSelWaveCap) {  // wave-uniform
+      uint64_t best64 = 0;
+#pragma unroll
+      for (int e = 0; e < kSelKeysPerLane; ++e) best64 = keys[e] > best64 ? keys[e] : best64;
+      const uint64_t sorted = wave_sort_desc(best64, lane);
+      const uint64_t tw = ((uint64_t)__shfl((uint32_t)(sorted >> 32), kTopK - 2) << 32) |
+                          (uint32_t)__shfl((uint32_t)sorted, kTopK - 2);
+      thr = tw > thr ? tw : thr;
+      total = sel_ballots(keys, thr, ballot);
+    }
+    sel_append<kSelKeysPerLane, PAGES>(keys, pages, thr, ballot, total, lane, sm.cand, sm.cand_page, &sm.count);
   }
   __syncthreads();
 
   if (wave == 0) {
-    // 4. running top-15 in lanes 0..14, 49 new candidates per round
-    const int count = sm.count;
-    uint64_t top = 0;
-    for (int base = 0; base < count; base += kWave - (kTopK - 1)) {
-      uint64_t v = 0;
-      if (lane < kTopK - 1) {
-        v = top;
-      } else {
-        const int idx = base + lane - (kTopK - 1);
-        if (idx < count) v = sm.cand[idx];
+    // 4. the 15 best candidates -> lanes 0..14 (any order): (myj, mypage)
+    const int count = sm.count;  // >= 15: every top-15 key qualifies
+    int myj = 0x7fffffff;
+    int32_t mypage = 0;
+    if (count <= kWave) {
+      const uint64_t mine = lane < count ? sm.cand[lane] : 0;
+      int rank = 0;
+#pragma unroll 8
+      for (int i = 0; i < count; ++i) rank += sm.cand[i] > mine ? 1 : 0;
+      if (lane < count && rank < kTopK - 1) {  // rank is unique: keys are distinct
+        sm.win[rank] = key_block(mine);
+        if constexpr (PAGES) sm.win_page[rank] = sm.cand_page[lane];
       }
-      top = wave_sort_desc(v, lane);
+      wave_sync_lds();
+      if (lane < kTopK - 1) {
+        myj = sm.win[lane];
+        if constexpr (PAGES) mypage = sm.win_page[lane];
+      }
+    } else {
+      // running top-15 in lanes 0..14, 49 new candidates per round
+      uint64_t top = 0;
+      for (int base = 0; base < count; base += kWave - (kTopK - 1)) {
+        uint64_t v = 0;
+        if (lane < kTopK - 1) {
+          v = top;
+        } else {
+          const int idx = base + lane - (kTopK - 1);
+          if (idx < count) v = sm.cand[idx];
+        }
+        top = wave_sort_desc(v, lane);
+      }
+      if (lane < kTopK - 1) {
+        myj = key_block(top);
+        if constexpr (PAGES) mypage = bt_row[myj];
+      }
     }
     // 5. 15 winners ascending by block id, then the recent block
-    const int myj = lane < kTopK - 1 ? key_block(top) : 0x7fffffff;
     int rank = 0;
 #pragma unroll
     for (int m = 0; m < kTopK - 1; ++m) {
       const int other = __shfl(myj, m);
       rank += other < myj ? 1 : 0;
     }
-    if (lane < kTopK - 1) out[rank] = myj;
-    if (lane == kTopK - 1) out[kTopK - 1] = r;
+    if (lane < kTopK - 1) {
+      out[rank] = myj;
+      if constexpr (PAGES) out_page[rank] = mypage;
+    }
+    if (lane == kTopK - 1) {
+      out[kTopK - 1] = r;
+      if constexpr (PAGES) out_page[kTopK - 1] = recent_page;
+    }
   }
   __syncthreads();
 }

@@ -165,6 +165,24 @@ def test_selection_kernel_exact_on_ties(dev):
             assert np.array_equal(got[b, g], ref), (b, g, got[b, g], ref)
 
 
+def test_fused_selection_on_ties(dev):
+    """All index queries zero: every block score is 0 (ties everywhere, -0 and
+    +0 alike), so the fused path must keep blocks 0..14 plus the recent block
+    (lower ids win ties), with the right pages, and attend over exactly those.
+    Rows of 300, 2000 and 5000 blocks take the tie fallbacks of the
+    selection (more candidates than one wave holds)."""
+    msa = _msa()
+    w = synth.make_workload(seq_lens=[128 * 300 + 7, 128 * 2000, 128 * 17, 128 * 5000 + 1], plant=0,
+                            layout="paged", seed=44, device=dev)
+    w.iq.zero_()
+    out, sel, bs = check_workload(w, label="all index scores tied")
+    for row, L in enumerate(w.seq_lens.cpu().tolist()):
+        r = (L - 1) // 128
+        want = list(range(15)) + [r] if r >= 16 else list(range(r + 1)) + [-1] * (15 - r)
+        for g in range(4):
+            assert sel[row, g].tolist() == want, (row, g, sel[row, g])
+
+
 def test_paged_permutation_invariance(dev):
     """Physical page permutation leaves ids and outputs bitwise unchanged."""
     w = synth.make_workload(seq_lens=[7000, 4100, 300], plant=3, seed=24, spare_pages=3, device=dev)
