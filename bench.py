@@ -128,7 +128,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="paged_b32_128k")
     ap.add_argument("--copies", type=int, default=2, help="input copies the steps rotate through")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=16)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
                     help="counters: only the scan kernel and a plain 512 MiB copy of known size, for rocprofv3 --pmc")
