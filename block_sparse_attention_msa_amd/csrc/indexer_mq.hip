@@ -9,14 +9,24 @@
 // queries x 4 groups per sequence the scores are a real dense contraction:
 //   S[t][r] = sum_d ik[t][d] * iq[r][d],  t = tokens, r = (query, group) rows.
 //
-// gfx950 design: one workgroup per (sequence, 128-token block).  The block's
-// index keys are converted once (E4M3 -> bf16, exact) into LDS as the MFMA A
-// operand (M = tokens); each wave takes pairs of 32-row tiles of the bf16 index
-// queries as B operands (N = rows) straight from global memory, and runs
-// v_mfma_f32_32x32x16_bf16 over 4 token tiles x 8 K steps (bf16 x bf16 products
-// are exact, fp32 accumulation).  The epilogue applies the causal mask and the
-// max over the block's tokens in registers, so the score matrix never reaches
-// memory; each row's block score is written once.
+// gfx950 design: the index queries stay, the keys stream.
+//  * One 512-thread workgroup per (sequence, 256-row chunk, 8-block range).
+//    The chunk's bf16 index queries (64 KB) are staged once in LDS (rows padded
+//    to 272 B: conflict-free 16-byte reads) and serve as MFMA B operands.
+//  * Each wave takes one block of the range: 4 tiles of 32 tokens.  A lane
+//    loads one token's 64 contiguous dims (FP8: 64 B) and converts them in
+//    registers (E4M3 -> bf16, exact) into the A operands of 8 K steps; the
+//    contraction axis is permuted (lane half h, step s, element e -> dim
+//    64h + 8s + e) identically for A and B, so both come from contiguous
+//    bytes.  The whole block's A operands stay in registers while the wave
+//    walks the row tiles, so every B read from LDS feeds four
+//    v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products are exact, fp32
+//    accumulation) and each row tile's block maximum is final at once.
+//  * The epilogue applies the causal mask (row r = 4i + g sees tokens at or
+//    before its query's position) and the max over the block's tokens in
+//    registers; the score matrix never reaches memory and each (row, block)
+//    score is written once.  Keys are re-read once per row chunk, from the
+//    Infinity Cache after the first chunk.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -26,14 +36,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMqThreads = 256;
-constexpr int kMqWaves = kMqThreads / kWave;
-constexpr int kRowTile = 32;                       // MFMA N
-constexpr int kTokTile = 32;                       // MFMA M
-constexpr int kKStep = 16;                         // MFMA K
-constexpr int kTokTiles = kBlock / kTokTile;       // 4
-constexpr int kKSteps = kDim / kKStep;             // 8
-constexpr int kLdsRow = kDim * 2 + 16;             // bf16 row + 16 B pad: conflict-free 16-lane groups
+constexpr int kMqThreads = 512;
+constexpr int kMqWaves = kMqThreads / kWave;       // 8
+constexpr int kRowChunk = 256;                     // index-query rows staged per workgroup
+constexpr int kRowTiles = kRowChunk / 32;          // MFMA N tiles
+constexpr int kRangeBlocks = kMqWaves;             // blocks per workgroup (one per wave)
+constexpr int kTokTiles = kBlock / 32;             // MFMA M tiles per block
+constexpr int kLdsRow = kDim * 2 + 16;             // bf16 row + 16 B pad
 
 // MFMA 32x32x16 bf16 lane layout (gfx950): lane l supplies A[l%32][8(l/32)+e]
 // and B[8(l/32)+e][l%32], e = 0..7; result register q of lane l holds
@@ -44,120 +53,130 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
                                                              const int32_t* __restrict__ seq_lens,
                                                              const uint16_t* __restrict__ iq,
                                                              float* __restrict__ block_scores, int q_len, int mbps,
-                                                             float idx_scale) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBlock * kLdsRow];   // 34 KB
-  const int blk = blockIdx.x;
+                                                             int nchunks, float idx_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[kRowChunk * kLdsRow];  // 68 KB
+  constexpr int kKeyRow = FP8 ? kDim : kDim * 2;  // bytes per token of an index-key page
   const int b = blockIdx.y;
+  const int rc = blockIdx.x % nchunks;
+  const int br = blockIdx.x / nchunks;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int L = seq_lens[b];
-  const int nrows = q_len * kGroups;                         // (query, group) rows of this sequence
-  const size_t row_base = (size_t)b * nrows;                  // first row of the sequence in [rows][4]
-  float* bs = block_scores + row_base * mbps + blk;           // bs[rr * mbps] for local row rr
+  const int nrows = q_len * kGroups;                 // (query, group) rows of this sequence
+  const int row0 = rc * kRowChunk;                   // first row of this chunk
+  const int crow = min(kRowChunk, nrows - row0);     // rows in this chunk (>= 1)
+  const int ntiles = (crow + 31) / 32;
+  const size_t srow = (size_t)b * nrows + row0;      // first global row of the chunk
+  float* bs = block_scores + srow * mbps;            // bs[r * mbps + blk], r chunk-local
   const int nb = L > 0 ? (L - 1) / kBlock + 1 : 0;
-  const int pos0 = L - q_len;                                 // position of query 0
-  if (blk >= nb || (long long)blk * kBlock > (long long)pos0 + q_len - 1) {
-    for (int rr = tid; rr < nrows; rr += kMqThreads) bs[(size_t)rr * mbps] = -INFINITY;
-    return;
-  }
+  const int pos0 = L - q_len;                        // position of query 0
+  const int pos_min = pos0 + row0 / kGroups;         // first and last query of the chunk
+  const int pos_max = pos0 + (row0 + crow - 1) / kGroups;
 
-  // ---- stage the block's index keys as bf16 [token][dim] (+pad) in LDS
-  const int64_t page = block_table[(size_t)b * mbps + blk];
-  if constexpr (FP8) {
-    const uint8_t* src = idx_pool + page * (kBlock * kDim) + tid * 64;   // token tid/2, dims (tid%2)*64..
-    u32x4 w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const u32x4*>(src + i * 16);
-    uint8_t* dst = lds_a + (tid >> 1) * kLdsRow + (tid & 1) * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-      u32x4 o0, o1;
-      o0.x = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(ws[0]));
-      o0.y = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(ws[0]));
-      o0.z = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(ws[1]));
-      o0.w = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(ws[1]));
-      o1.x = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(ws[2]));
-      o1.y = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(ws[2]));
-      o1.z = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(ws[3]));
-      o1.w = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(ws[3]));
-      *reinterpret_cast<u32x4*>(dst + i * 32) = o0;
-      *reinterpret_cast<u32x4*>(dst + i * 32 + 16) = o1;
-    }
-  } else {
-    const uint8_t* src = idx_pool + page * (kBlock * kDim * 2) + tid * 128;  // token tid/2, dims (tid%2)*64..
-    uint8_t* dst = lds_a + (tid >> 1) * kLdsRow + (tid & 1) * 128;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(dst + i * 16) = *reinterpret_cast<const u32x4*>(src + i * 16);
+  // ---- stage the chunk's index queries (rows past crow zero-filled)
+  for (int i = tid; i < ntiles * 32 * 16; i += kMqThreads) {
+    const int r = i >> 4, piece = i & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < crow) v = *reinterpret_cast<const uint4*>(iq + (srow + r) * kDim + piece * 8);
+    *reinterpret_cast<uint4*>(lds_q + r * kLdsRow + piece * 16) = v;
   }
   __syncthreads();
 
-  const int half = lane >> 5;       // 0: k 0..7 / tokens +0..3; 1: k 8..15 / tokens +4..7
-  const int col = lane & 31;        // A row (token) for operands, D column (row) for results
-  const int visible_all = pos0 - blk * kBlock + 1;   // tokens of this block visible to query 0
-  const int ntiles = (nrows + kRowTile - 1) / kRowTile;
+  const int h = lane >> 5;   // dim half of the A/B operands; token quarter of the results
+  const int col = lane & 31; // A: token of the tile; B and results: row of the tile
+  const int blk = br * kRangeBlocks + wave;
+  if (blk >= mbps) return;
+  if (blk >= nb || (long long)blk * kBlock > pos_max) {  // no row of the chunk sees this block
+    for (int r = lane; r < crow; r += kWave) bs[(size_t)r * mbps + blk] = -INFINITY;
+    return;
+  }
+  const int64_t page = block_table[(size_t)b * mbps + blk];
+  const uint8_t* kp = idx_pool + page * (kBlock * kKeyRow) + col * kKeyRow + h * (kKeyRow / 2);
+  const bool full = (long long)blk * kBlock + kBlock - 1 <= pos_min;  // every row sees the whole block
+  const int vis0 = pos0 - blk * kBlock + 1;                           // tokens visible to query 0
 
-  // ---- wave w takes 32-row tile pairs (2w, 2w+1), (2w + 8, ...), ...
-  for (int tp = wave * 2; tp < ntiles; tp += 2 * kMqWaves) {
-    // B operands of the two row tiles for all 8 K steps (rows past the end load row 0)
-    bf16x8 bq[2][kKSteps];
+  // ---- A operands of the whole block: 4 token tiles x 8 K steps
+  bf16x8 a[kTokTiles][8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int rr = (tp + u) * kRowTile + col;
-      rr = rr < nrows ? rr : 0;
-      const uint16_t* qrow = iq + (row_base + rr) * kDim + half * 8;
+  for (int tt = 0; tt < kTokTiles; ++tt) {
+    const uint8_t* src = kp + (size_t)(32 * tt) * kKeyRow;
+    if constexpr (FP8) {
+      u32x4 w[4];
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
-        bq[u][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + s * kKStep));
-    }
-    // causal positions of this lane's two rows (row = tile*32 + col -> query row / 4)
-    int vis[2];
+      for (int i = 0; i < 4; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * i));
+      const uint32_t d[16] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w,
+                              w[2].x, w[2].y, w[2].z, w[2].w, w[3].x, w[3].y, w[3].z, w[3].w};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) vis[u] = visible_all + ((tp + u) * kRowTile + col) / kGroups;
-    const bool full = visible_all >= kBlock;   // every row of the sequence sees the whole block
-    float mx[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-    for (int m = 0; m < kTokTiles; ++m) {
-      f32x16 acc[2] = {{}, {}};
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(lds_a + (m * kTokTile + col) * kLdsRow + (s * kKStep + half * 8) * 2));
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[0][s], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[1][s], acc[1], 0, 0, 0);
+      for (int s = 0; s < 8; ++s) {
+        const bf16x2 p0 = e4m3x2_to_bf16x2<false>(d[2 * s]);
+        const bf16x2 p1 = e4m3x2_to_bf16x2<true>(d[2 * s]);
+        const bf16x2 p2 = e4m3x2_to_bf16x2<false>(d[2 * s + 1]);
+        const bf16x2 p3 = e4m3x2_to_bf16x2<true>(d[2 * s + 1]);
+        a[tt][s] = bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
       }
+    } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int s = 0; s < 8; ++s)
+        a[tt][s] =
+            __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * s)));
+    }
+  }
+
+  // ---- row tiles: 4 accumulators, every B read from LDS feeds 4 MFMAs
+#pragma unroll 1
+  for (int rt = 0; rt < ntiles; ++rt) {
+    const uint8_t* qrow = lds_q + (32 * rt + col) * kLdsRow + h * kDim;  // dims 64h..
+    bf16x8 bq[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+    f32x16 acc[kTokTiles];
+#pragma unroll
+    for (int tt = 0; tt < kTokTiles; ++tt) acc[tt] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int tt = 0; tt < kTokTiles; ++tt)
+        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tt][s], bq[s], acc[tt], 0, 0, 0);
+      // keep the four independent accumulator chains interleaved: a chain's
+      // next MFMA then issues only after the other three
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float m = -INFINITY;
+    if (full) {  // wave-uniform: no mask
+#pragma unroll
+      for (int q = 0; q < 16; ++q) m = fmaxf(m, fmaxf(fmaxf(acc[0][q], acc[1][q]), fmaxf(acc[2][q], acc[3][q])));
+    } else {
+      // this lane's row (column of D) sees tokens < vis of the block
+      const int vis = vis0 + (row0 + 32 * rt + col) / kGroups;
+#pragma unroll
+      for (int tt = 0; tt < kTokTiles; ++tt)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int tok = m * kTokTile + 8 * (q >> 2) + 4 * half + (q & 3);
-          const float v = (full || tok < vis[u]) ? acc[u][q] : -INFINITY;
-          mx[u] = fmaxf(mx[u], v);
+          const int tok = 32 * tt + 8 * (q >> 2) + 4 * h + (q & 3);
+          m = fmaxf(m, tok < vis ? acc[tt][q] : -INFINITY);
         }
-      }
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], 32));
-      const int rr = (tp + u) * kRowTile + col;
-      if (half == 0 && rr < nrows) bs[(size_t)rr * mbps] = mx[u] * idx_scale;
-    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const int r = 32 * rt + col;
+    if (h == 0 && r < crow) bs[(size_t)r * mbps + blk] = m * idx_scale;
   }
 }
 
 }  // namespace
 
 hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream) {
-  dim3 grid(a.mbps, a.num_seqs);
+  const int nrows = q_len * kGroups;
+  const int nchunks = (nrows + kRowChunk - 1) / kRowChunk;
+  const int ranges = (a.mbps + kRangeBlocks - 1) / kRangeBlocks;
+  dim3 grid(ranges * nchunks, a.num_seqs);
   if (a.idx_fp8)
     scan_mq_kernel<true><<<grid, kMqThreads, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                           a.seq_lens, a.iq, a.block_scores, q_len, a.mbps,
+                                                           a.seq_lens, a.iq, a.block_scores, q_len, a.mbps, nchunks,
                                                            a.idx_scale);
   else
     scan_mq_kernel<false><<<grid, kMqThreads, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                            a.seq_lens, a.iq, a.block_scores, q_len, a.mbps,
+                                                            a.seq_lens, a.iq, a.block_scores, q_len, a.mbps, nchunks,
                                                             a.idx_scale);
   return hipGetLastError();
 }
