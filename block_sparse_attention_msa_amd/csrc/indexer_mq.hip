@@ -39,7 +39,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kMqThreads = 512;
 constexpr int kMqWaves = kMqThreads / kWave;       // 8
 constexpr int kRowChunk = 256;                     // index-query rows staged per workgroup
-constexpr int kRowTiles = kRowChunk / 32;          // MFMA N tiles
 constexpr int kRangeBlocks = kMqWaves;             // blocks per workgroup (one per wave)
 constexpr int kTokTiles = kBlock / 32;             // MFMA M tiles per block
 constexpr int kLdsRow = kDim * 2 + 16;             // bf16 row + 16 B pad

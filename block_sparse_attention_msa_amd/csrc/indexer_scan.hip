@@ -19,7 +19,10 @@ namespace {
 constexpr int kScanWaves = 8;
 
 template <bool FP8>
-__global__ __launch_bounds__(kScanWaves * kWave) void scan_decode_kernel(const uint8_t* __restrict__ idx_pool,
+// At most 102 VGPRs (5 waves per SIMD): one more resident wave per SIMD than
+// the unconstrained allocation (100 VGPRs, 4 waves) keeps more page loads in
+// flight.
+__global__ __launch_bounds__(kScanWaves * kWave, 5) void scan_decode_kernel(const uint8_t* __restrict__ idx_pool,
                                                                           const int32_t* __restrict__ block_table,
                                                                           const int32_t* __restrict__ seq_lens,
                                                                           const uint16_t* __restrict__ iq,
@@ -38,10 +41,10 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_decode_kernel(const u
 }  // namespace
 
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
-  // 8-wave workgroups, 1-2 pages per wave: measured best on the batch-32 x
-  // 128K workload (2 pages per wave: 82 us vs 84-88 us for 1, 4, 8 or 16).
-  const long long total_blocks = (long long)a.num_seqs * a.mbps;
-  const int bpw = total_blocks >= 16384 ? 2 : 1;
+  // 8-wave workgroups, one page per wave: measured best on the batch-32 x
+  // 128K workload with 5 waves per SIMD (81.4-81.7 us vs 82.2-83.3 us for 2 or
+  // 4 pages per wave and 82.8-85.7 us at 4 waves per SIMD).
+  const int bpw = 1;
   constexpr int waves_per_wg = kScanWaves;
   dim3 grid((a.mbps + waves_per_wg * bpw - 1) / (waves_per_wg * bpw), a.num_seqs);
   dim3 block(waves_per_wg * kWave);
