@@ -9,10 +9,10 @@
 // restricted to the selected set, computed with an online softmax over split
 // work whose partial outputs are merged).
 //
-// One 1024-thread workgroup per (row, group).  Each of the 16 waves takes one
-// of the 16 kept blocks; the waves' partial (o, m, l) are merged by
-// log-sum-exp in LDS, so each head's softmax completes inside the workgroup
-// and the output is written directly.  K/V are read only for the kept blocks,
+// One workgroup per (row, group): 16 waves with one kept block each, or 8
+// waves with two (online softmax across the pair); the waves' partial
+// (o, m, l) are merged by log-sum-exp in LDS, so each head's softmax completes
+// inside the workgroup and the output is written directly.  K/V are read only for the kept blocks,
 // straight from the paged pool, and dequantised once for all four heads.
 //
 // gfx950 design, per wave and 128-token block (NVFP4 K/V):
@@ -46,27 +46,38 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnThreads = 1024;
-constexpr int kAttnWaves = kAttnThreads / kWave;  // 16
-static_assert(kTopK == kAttnWaves, "one kept block per wave");
 constexpr int kQkTiles = kBlock / 16;   // 16-token MFMA tiles per block
 constexpr int kPvSteps = kBlock / 32;   // 32-token MFMA contraction steps per block
 
-struct MergeSmem {
-  float o[kAttnWaves][kHeadsPerGroup][kDim];  // 32 KB
-  float m[kAttnWaves][kHeadsPerGroup];
-  float l[kAttnWaves][kHeadsPerGroup];
+// Workgroup shapes: NT = 1024 (16 waves, one kept block each) or NT = 512
+// (8 waves, two kept blocks each, online softmax across the pair; rows of at
+// most 8,192 blocks).  The 512-thread form needs about half the LDS, so two
+// workgroups share a CU and hide each other's load and selection latency.
+template <int NT>
+struct AttnShape {
+  static constexpr int kWaves = NT / kWave;
+  static constexpr int kBlocksPerWave = kTopK / kWaves;
+  static_assert(kWaves * kBlocksPerWave == kTopK, "kept blocks split evenly over the waves");
 };
 
+template <int NT>
+struct MergeSmem {
+  float o[NT / kWave][kHeadsPerGroup][kDim];
+  float m[NT / kWave][kHeadsPerGroup];
+  float l[NT / kWave][kHeadsPerGroup];
+};
+
+template <int NT>
 struct AttnSmem {
+  static constexpr int kWaves = NT / kWave;
   union {
-    SelectSmem<kAttnThreads> sel;
-    MergeSmem merge;
+    SelectSmem<NT> sel;
+    MergeSmem<NT> merge;
   } u;
-  uint16_t p[kAttnWaves][kHeadsPerGroup][kBlock];    // 16 KB: softmax weights (f16, or bf16 hi part)
-  uint16_t plo[kAttnWaves][kHeadsPerGroup][kBlock];  // 16 KB: bf16 lo part (bf16 K/V only)
-  uint8_t ksc[kAttnWaves][kBlock * 8];             // 16 KB: K scales [token][group]
-  uint8_t vsc[kAttnWaves][kBlock * 8];             // 16 KB: V scales [token pair][group][2]
+  uint16_t p[kWaves][kHeadsPerGroup][kBlock];    // 1 KB per wave: softmax weights (f16, or bf16 hi part)
+  uint16_t plo[kWaves][kHeadsPerGroup][kBlock];  // 1 KB per wave: bf16 lo part (bf16 K/V only)
+  uint8_t ksc[kWaves][kBlock * 8];               // 1 KB per wave: K scales [token][group]
+  uint8_t vsc[kWaves][kBlock * 8];               // 1 KB per wave: V scales [token pair][group][2]
   int32_t sel[kTopK];
   int32_t page[kTopK];  // page ids of the kept blocks (fused selection)
 };
@@ -120,15 +131,18 @@ struct PvType<false> {  // bf16 V
 // output dims [part * 128 / DSPLIT, (part + 1) * 128 / DSPLIT).  The DSPLIT
 // workgroups of one (row, g) repeat the selection and the softmax (identical,
 // deterministic) and split the PV work; part 0 writes the selected ids.
-// Every thread of the workgroup must call it.
-template <bool FP4, bool SELECT, int DSPLIT>
+// With SELECT, mbps must not exceed sel_max_blocks<NT>().  Every thread of the
+// workgroup must call it.
+template <bool FP4, bool SELECT, int DSPLIT, int NT>
 __device__ __forceinline__ void attn_workgroup(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
     int32_t* __restrict__ sel_out, float* __restrict__ out, int q_len, int mbps, float qk_scale_log2, float v_scale,
-    int row, int g, int part, AttnSmem& sm) {
+    int row, int g, int part, AttnSmem<NT>& sm) {
   static_assert(DSPLIT == 1 || DSPLIT == 2 || DSPLIT == 4, "output split");
+  constexpr int kWaves = AttnShape<NT>::kWaves;
+  constexpr int kBpw = AttnShape<NT>::kBlocksPerWave;
   using PV = PvType<FP4>;
   constexpr int kRowBytes = FP4 ? kDim / 2 : kDim * 2;  // bytes per (token, head) row
   constexpr int kDims = kDim / DSPLIT;                  // output dims of this workgroup
@@ -152,7 +166,7 @@ __device__ __forceinline__ void attn_workgroup(
   const int pos = L - q_len + row % q_len;
   if constexpr (SELECT) {
     const int r = min(pos / kBlock, mbps - 1);
-    select_blocks<kAttnThreads, true>(block_scores + ((size_t)row * kGroups + g) * mbps,
+    select_blocks<NT, true>(block_scores + ((size_t)row * kGroups + g) * mbps,
                                       block_table + (size_t)b * mbps, r, sm.u.sel, sm.sel, sm.page);
     if (sel_row && tid < kTopK) sel_row[tid] = sm.sel[tid];
   } else {
@@ -168,17 +182,28 @@ __device__ __forceinline__ void attn_workgroup(
   const int jj = n & 3;
   const int d0 = dbase + kLaneDims * n;  // PV: this lane's first output dim
 
-  int j = sm.sel[wave];
-  // ids outside the row's visible blocks or the table contribute nothing
-  if (j >= mbps || j * kBlock > pos) j = -1;
-
   float m_w = -INFINITY, l_w = 0.f;  // head hq
   f32x4 acc[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (j >= 0) {  // wave-uniform
-    const int64_t page = SELECT ? sm.page[wave] : block_table[(size_t)b * mbps + j];
+  // B operands: column (hq, jj) takes head hq's dims 32c + 8s + e when jj == c
+  bf16x8 qb[4];
+  {
+    const uint16_t* qh = q + ((size_t)row * (kGroups * kHeadsPerGroup) + head0 + hq) * kDim + 32 * c;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 w = jj == c ? *reinterpret_cast<const uint4*>(qh + 8 * s) : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  for (int kb = 0; kb < kBpw; ++kb) {
+    const int slot = wave + kWaves * kb;
+    const int j = sm.sel[slot];
+    // ids outside the row's visible blocks or the table contribute nothing
+    if (j < 0 || j >= mbps || j * kBlock > pos) continue;  // wave-uniform
+    const int64_t page = SELECT ? sm.page[slot] : block_table[(size_t)b * mbps + j];
     const int64_t row0 = (page * kGroups + g) * kBlock;  // first (token, head) row of this page/head
     const int nvis = min(pos - j * kBlock + 1, kBlock);   // keys: tokens 0..nvis-1 (>= 1)
     const uint8_t* kbase = kpool + row0 * kRowBytes;
@@ -195,16 +220,6 @@ __device__ __forceinline__ void attn_workgroup(
     if constexpr (FP4) {
       ks16 = *reinterpret_cast<const uint4*>(k_sf + row0 * 8 + lane * 16);
       vs16 = *reinterpret_cast<const uint4*>(v_sf + row0 * 8 + lane * 16);
-    }
-    // B operands: column (hq, jj) takes head hq's dims 32c + 8s + e when jj == c
-    bf16x8 qb[4];
-    {
-      const uint16_t* qh = q + ((size_t)row * (kGroups * kHeadsPerGroup) + head0 + hq) * kDim + 32 * c;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 w = jj == c ? *reinterpret_cast<const uint4*>(qh + 8 * s) : make_uint4(0, 0, 0, 0);
-        qb[s] = __builtin_bit_cast(bf16x8, w);
-      }
     }
     if constexpr (FP4) {
       *reinterpret_cast<uint4*>(&sm.ksc[wave][lane * 16]) = ks16;
@@ -285,7 +300,7 @@ __device__ __forceinline__ void attn_workgroup(
         }
     }
 
-    // ---- softmax over the block (exact block max per head: no rescaling)
+    // ---- softmax over the block; with two blocks per wave, online across them
     float mx = z[0];
 #pragma unroll
     for (int T = 1; T < kQkTiles; ++T) mx = fmaxf(mx, z[T]);
@@ -293,7 +308,19 @@ __device__ __forceinline__ void attn_workgroup(
     mx = fmaxf(mx, dpp<kDppXor2>(mx));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    m_w = mx;  // >= one visible token, so finite
+    mx = fmaxf(mx, m_w);  // >= one visible token, so finite
+    if constexpr (kBpw > 1) {
+      const float alpha = exp2_nonpos(m_w - mx);  // 0 on the wave's first block
+      l_w *= alpha;
+      // acc row i is head i; lane 4i holds head i's factor
+#pragma unroll
+      for (int i = 0; i < kHeadsPerGroup; ++i) {
+        const float ai = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 4 * i));
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) acc[t][i] *= ai;
+      }
+    }
+    m_w = mx;
     float ls = 0.f;
 #pragma unroll
     for (int T = 0; T < kQkTiles; ++T) {
@@ -307,7 +334,7 @@ __device__ __forceinline__ void attn_workgroup(
     ls += dpp<kDppXor2>(ls);
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
-    l_w = ls;
+    l_w += ls;
     wave_sync_lds();
 
     // ---- PV
@@ -387,6 +414,7 @@ __device__ __forceinline__ void attn_workgroup(
         }
       }
     }
+    wave_sync_lds();  // the next block rewrites this wave's LDS
   }
   __syncthreads();  // selection LDS is dead: the merge area reuses it
 
@@ -411,11 +439,11 @@ __device__ __forceinline__ void attn_workgroup(
     const int d = dbase + tid % kDims;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][h]);
     float o = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
+      for (int w = 0; w < kWaves; ++w) {
         const float mw = sm.u.merge.m[w][h];
         if (mw == -INFINITY) continue;
         const float f = exp2_nonpos(mw - M);

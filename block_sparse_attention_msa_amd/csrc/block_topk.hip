@@ -9,6 +9,7 @@ namespace msa {
 namespace {
 
 constexpr int kThreads = 1024;
+static_assert(sel_max_blocks<kThreads>() >= kMaxBlocksPerSeq, "every row length fits one workgroup");
 
 __global__ __launch_bounds__(kThreads) void block_topk_kernel(const int32_t* __restrict__ seq_lens,
                                                               const float* __restrict__ block_scores,

@@ -36,12 +36,16 @@ namespace msa {
 constexpr int kSelKeysPerLane = 16;                               // keys per lane of an active wave
 constexpr int kSelBlocksPerWave = kWave * kSelKeysPerLane;         // 1,024
 constexpr int kSelWaveCap = (kTopK - 1) * kSelKeysPerLane;         // candidates per active wave, at most
-constexpr int kSelCandCap = kSelWaveCap * (kMaxBlocksPerSeq / kSelBlocksPerWave) + kWave;
+
+// A workgroup of NT threads selects among at most (NT / 64) x 1,024 blocks.
+template <int NT>
+constexpr int sel_max_blocks() { return NT / kWave * kSelBlocksPerWave; }
 
 template <int NT>
 struct SelectSmem {
-  uint64_t cand[kSelCandCap];
-  int32_t cand_page[kSelCandCap];
+  static constexpr int kCandCap = kSelWaveCap * (NT / kWave) + kWave;  // at most 15 x 16 keys per active wave
+  uint64_t cand[kCandCap];
+  int32_t cand_page[kCandCap];
   uint32_t wave_t0[NT / kWave];
   int32_t win[kTopK];
   int32_t win_page[kTopK];
@@ -191,8 +195,9 @@ __device__ __forceinline__ int sel_ballots(const uint64_t (&keys)[E], uint64_t t
   return total;
 }
 
-// Selection for one (row, group) by a workgroup of NT threads (NT / 64 >= 16
-// waves, so every candidate fits the active waves' registers).
+// Selection for one (row, group) by a workgroup of NT threads; r must be below
+// sel_max_blocks<NT>() so that every candidate fits the active waves'
+// registers (1,024 per wave).
 // s: block scores of the row/group; bt_row: its block table row (read only
 // when PAGES); r: the recent block (0 <= r < row length).  Writes 16 ids
 // (ascending, -1 padded) to out[] and, when PAGES, their page ids to
@@ -202,7 +207,7 @@ template <int NT, bool PAGES>
 __device__ void select_blocks(const float* __restrict__ s, const int32_t* __restrict__ bt_row, int r,
                               SelectSmem<NT>& sm, int32_t* out, int32_t* out_page) {
   constexpr int kWaves = NT / kWave;
-  static_assert(kWaves * kSelBlocksPerWave >= kMaxBlocksPerSeq, "too few waves for the largest row");
+  static_assert(NT % kWave == 0 && kWaves >= 1, "whole waves");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;

@@ -18,18 +18,19 @@ __device__ __forceinline__ void attn_decode_wg(int id, int& pair, int& part) {
   pair = (k / DSPLIT) * 8 + x;
 }
 
-template <bool FP4, bool SELECT, int DSPLIT>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
+// Four waves per SIMD: for the 512-thread form, room for two workgroups per CU.
+template <bool FP4, bool SELECT, int DSPLIT, int NT>
+__global__ __launch_bounds__(NT, 4) void attn_kernel(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
     int32_t* __restrict__ sel_out, float* __restrict__ out, int rows, int q_len, int mbps, float qk_scale_log2,
     float v_scale) {
-  __shared__ AttnSmem sm;
+  __shared__ AttnSmem<NT> sm;
   int pair, part;
   attn_decode_wg<DSPLIT>(blockIdx.x, pair, part);
   if (pair >= rows * kGroups) return;  // grid padded to a multiple of 8 (row, group) pairs
-  attn_workgroup<FP4, SELECT, DSPLIT>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores, sel_in,
+  attn_workgroup<FP4, SELECT, DSPLIT, NT>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores, sel_in,
                                       sel_out, out, q_len, mbps, qk_scale_log2, v_scale, pair / kGroups,
                                       pair % kGroups, part, sm);
 }
@@ -46,11 +47,11 @@ int device_cus() {
   return cached[dev];
 }
 
-template <bool FP4, bool SELECT, int DSPLIT>
+template <bool FP4, bool SELECT, int DSPLIT, int NT>
 void launch3(const AttnArgs& a, hipStream_t stream) {
   const long long pairs = (long long)a.rows * kGroups;
   const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * DSPLIT));
-  attn_kernel<FP4, SELECT, DSPLIT><<<grid, kAttnThreads, 0, stream>>>(
+  attn_kernel<FP4, SELECT, DSPLIT, NT><<<grid, NT, 0, stream>>>(
       static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table, a.seq_lens,
       a.q, a.block_scores, a.sel, a.sel_out, a.out, a.rows, a.q_len, a.mbps, a.qk_scale_log2, a.v_scale);
 }
@@ -61,12 +62,23 @@ void launch2(const AttnArgs& a, hipStream_t stream) {
   // still leaves at least one workgroup per CU: few rows are latency-bound.
   const long long pairs = (long long)a.rows * kGroups;
   const int cus = device_cus();
-  if (pairs * 4 <= cus)
-    launch3<FP4, SELECT, 4>(a, stream);
-  else if (pairs * 2 <= cus)
-    launch3<FP4, SELECT, 2>(a, stream);
-  else
-    launch3<FP4, SELECT, 1>(a, stream);
+  // With more (row, group) pairs than CUs, 512-thread workgroups (two kept
+  // blocks per wave) let two workgroups share a CU when the row fits their
+  // selection (at most 8,192 blocks); bf16 K/V keep the 1024-thread form
+  // (their two-block body does not fit 128 VGPRs).
+  if (pairs * 4 <= cus) {
+    launch3<FP4, SELECT, 4, 1024>(a, stream);
+  } else if (pairs * 2 <= cus) {
+    launch3<FP4, SELECT, 2, 1024>(a, stream);
+  } else {
+    if constexpr (FP4) {
+      if (!SELECT || a.mbps <= sel_max_blocks<512>()) {
+        launch3<FP4, SELECT, 1, 512>(a, stream);
+        return;
+      }
+    }
+    launch3<FP4, SELECT, 1, 1024>(a, stream);
+  }
 }
 
 }  // namespace
