@@ -24,6 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "MSA decode µs/layer-step + achieved HBM GB/s (%peak), 128K ctx, batch 32"
 
 
@@ -51,6 +52,19 @@ def scan_bytes(w) -> float:
             + w.rows * w.num_kv_heads * w.max_blocks_per_seq * 4)
 
 
+def scan_flops(w) -> float:
+    """Algorithmic flops of one multi-query index scan: 2 x 128 per (row,
+    group, visible key) pair; row i of sequence b sees its tokens at or before
+    position seq_lens[b] - q_len + i."""
+    total = 0
+    for L in [int(x) for x in w.seq_lens.cpu().tolist()]:
+        if L <= 0:
+            continue
+        first = L - w.q_len + 1                      # keys visible to query 0
+        total += w.num_kv_heads * (w.q_len * first + w.q_len * (w.q_len - 1) // 2)
+    return 2.0 * 128 * total
+
+
 def clone_workload(w):
     import copy
     w2 = copy.copy(w)
@@ -64,15 +78,20 @@ def cpu_baseline(w, sample_seqs: int, t_gpu_us: float):
     import oracle
     P = oracle.Problem.from_workload(w)
     cores = len(os.sched_getaffinity(0))
-    n = min(sample_seqs, w.num_seqs)
+    if w.q_len == 1:
+        n = min(sample_seqs, w.num_seqs)
+        rows, what = n, f"{n} of {w.num_seqs} sequences (rows 0-{n - 1})"
+    else:  # multi-query rows each scan the whole context: a few rows bound the CPU time
+        rows = min(16, w.rows)
+        what = f"{rows} of {w.rows} query rows (rows 0-{rows - 1})"
     t0 = time.perf_counter()
-    P.decode(0, n * w.q_len, nthreads=cores, want_scores=False)
+    P.decode(0, rows, nthreads=cores, want_scores=False)
     dt = time.perf_counter() - t0
-    scaled_us = dt * 1e6 * (w.num_seqs / n)
+    scaled_us = dt * 1e6 * (w.rows / rows)
     return {"value": round(scaled_us, 1), "unit": "us/layer-step", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.num_seqs} sequences (rows 0-{n - 1}), full {int(w.seq_lens[0])}-token "
-                      f"context each, fp64 C oracle with OpenMP over (row, group); wall {dt:.2f} s scaled by "
-                      f"{w.num_seqs / n:g} to the whole step; CPU: {cpu_model()}",
+            "sample": f"{what}, full {int(w.seq_lens[0])}-token context each, fp64 C oracle with OpenMP over "
+                      f"(row, group); wall {dt:.2f} s scaled by {w.rows / rows:g} to the whole step; "
+                      f"CPU: {cpu_model()}",
             "gpu_speedup": round(scaled_us / t_gpu_us, 1)}
 
 
@@ -201,7 +220,19 @@ def main():
     log(f"[bench] step {us_step:.1f} us ({step_gbps:.0f} GB/s algorithmic, {nb['total'] / 1e6:.1f} MB), "
         f"scan {scan_us:.1f} us ({scan_gbps:.0f} GB/s, {sb / 1e6:.1f} MB), host wall {wall / args.steps * 1e6:.1f} us")
 
-    traffic = scan_traffic()
+    if w.q_len == 1:
+        roofline = {"bound": "hbm", "kernel": "index scan + block max-pool", "achieved": round(scan_gbps, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
+                    "traffic": scan_traffic() if args.config == "paged_b32_128k" else None,
+                    "launch_us": round(scan_us, 2), "algorithmic_bytes": int(sb)}
+    else:  # the multi-query scan is a dense contraction on the matrix cores
+        fl = scan_flops(w)
+        tflops = fl / (scan_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "multi-query index scan + causal block max-pool (bf16 MFMA)",
+                    "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "launch_us": round(scan_us, 2), "algorithmic_flops": int(fl)}
+        log(f"[bench] multi-query scan {fl / 1e9:.1f} GFLOP, {tflops:.0f} TFLOP/s")
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -230,9 +261,7 @@ def main():
         "bytes_per_step": int(nb["total"]),
         "bytes_per_ctx_token": round(per_tok, 1),
         "vs_dense_fp8_kv_per_token": round(per_tok / 1024.0, 4),
-        "roofline": {"bound": "hbm", "kernel": "index scan + block max-pool", "achieved": round(scan_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "launch_us": round(scan_us, 2), "algorithmic_bytes": int(sb)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
