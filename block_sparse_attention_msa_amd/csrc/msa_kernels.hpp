@@ -62,4 +62,7 @@ struct AttnArgs {
 // Selection (fused path) + attention: one launch.
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 }  // namespace msa

@@ -35,18 +35,6 @@ __global__ __launch_bounds__(NT, 4) void attn_kernel(
                                       pair % kGroups, part, sm);
 }
 
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
-  }
-  return cached[dev];
-}
-
 template <bool FP4, bool SELECT, int DSPLIT, int NT>
 void launch3(const AttnArgs& a, hipStream_t stream) {
   const long long pairs = (long long)a.rows * kGroups;
@@ -82,6 +70,18 @@ void launch2(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.kv_nvfp4) {
