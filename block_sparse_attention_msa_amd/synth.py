@@ -9,7 +9,9 @@ any of the computation under test.
 Stored formats (the layouts the library reads):
   q      bf16  [rows][Hq][128]          rows = num_seqs * q_len, request-major
   iq     bf16  [rows][Hkv][128]         one index query per GQA group
-  idx_k  FP8 E4M3 (uint8) or bf16  [P][128 tokens][128]
+  idx_k  FP8 E4M3 (uint8) or bf16  [P][128 tokens][128], or NVFP4 uint8
+         [P][128 tokens][64] + E4M3 scales idx_sf uint8 [P][128 tokens][8]
+         (one shared index head; its fp32 tensor scale is idx_scale)
   k, v   NVFP4: uint8 [P][Hkv][128 tokens][64]   (element 2i in the low nibble)
          + E4M3 scales uint8 [P][Hkv][128 tokens][8]  (one per 16 elements)
          + one fp32 tensor scale each;
@@ -32,6 +34,8 @@ import torch
 
 BLOCK = 128
 DIM = 128
+# stored bytes of one token's index key: FP8 128, bf16 256, NVFP4 64 + 8 scales
+IDX_BYTES_PER_TOKEN = {"fp8": DIM, "bf16": 2 * DIM, "nvfp4": DIM // 2 + DIM // 16}
 E4M3_MAX = 448.0
 # E2M1 magnitude grid, code index == magnitude code (OCP FP4)
 _E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
@@ -93,7 +97,7 @@ class Workload:
     max_blocks_per_seq: int
     num_pages: int
     kv_dtype: str            # "bf16" | "nvfp4"
-    idx_dtype: str           # "bf16" | "fp8"
+    idx_dtype: str           # "bf16" | "fp8" | "nvfp4"
     sm_scale: float
     k_scale: float
     v_scale: float
@@ -108,6 +112,7 @@ class Workload:
     block_table: torch.Tensor
     seq_lens: torch.Tensor
     meta: dict = field(default_factory=dict)
+    idx_sf: Optional[torch.Tensor] = None   # NVFP4 index keys: E4M3 group scales [P][128][8]
 
     @property
     def rows(self) -> int:
@@ -126,7 +131,7 @@ class Workload:
             return t.detach().contiguous().cpu().numpy()
 
         return dict(q=u16(self.q), iq=u16(self.iq), idx_k=raw(self.idx_k), k=raw(self.k), v=raw(self.v),
-                    k_sf=raw(self.k_sf), v_sf=raw(self.v_sf),
+                    k_sf=raw(self.k_sf), v_sf=raw(self.v_sf), idx_sf=raw(self.idx_sf),
                     block_table=self.block_table.cpu().numpy().astype(np.int32),
                     seq_lens=self.seq_lens.cpu().numpy().astype(np.int32))
 
@@ -135,7 +140,7 @@ class Workload:
         every visible token's index key, K+V of the selected tokens only,
         the used block-table entries, q, iq and the fp32 output."""
         lens = [int(x) for x in self.seq_lens.cpu().tolist()]
-        b_idx = DIM * (1 if self.idx_dtype == "fp8" else 2)
+        b_idx = IDX_BYTES_PER_TOKEN[self.idx_dtype]
         b_kv_tok = DIM * (0.5 + 1.0 / 16) if self.kv_dtype == "nvfp4" else DIM * 2.0
         scan = sum(lens) * b_idx
         gather = 0.0
@@ -214,45 +219,67 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
         direction = (iq_last / iq_last.norm(dim=-1, keepdim=True)).float()     # [S][G][D]
 
     # ---- index keys, per sequence in logical order, scattered to pages
-    bidx = 1 if idx_dtype == "fp8" else 2
-    idx_pool = torch.zeros(P, BLOCK, DIM * bidx, dtype=torch.uint8, device=dev)
-    gi = _gen(dev, seed * 7919 + 3)
-    gsel = _gen("cpu", seed * 7919 + 4)
     planted = {}
-    for b in range(S):
-        nb, L = nbs[b], seq_lens[b]
-        if nb == 0:
-            continue
-        if idx_dist == "normal":
-            keys = torch.randn(nb, BLOCK, DIM, generator=gi, device=dev)
-        elif idx_dist == "uniform":
-            keys = torch.rand(nb, BLOCK, DIM, generator=gi, device=dev) * 2.0 - 1.0
-        else:
-            raise ValueError(idx_dist)
-        r_last = nb - 1
-        bias = torch.zeros(nb, DIM, device=dev)
-        for g in range(G):
-            dvec = direction[b, g].to(dev)
-            if plant and r_last > 0:
-                n = min(plant, r_last)
-                picks = torch.randperm(r_last, generator=gsel)[:n]
-                planted[(b, g)] = sorted(int(x) for x in picks)
-                bias[picks.to(dev)] += 2.0 * dvec
-            if zipf is not None and r_last > 0:
-                ranks = torch.randperm(r_last, generator=gsel).to(torch.float64) + 1.0  # block j -> rank
-                w = (zipf_amp * ranks.pow(-zipf)).to(torch.float32).to(dev)
-                bias[:r_last] += w[:, None] * dvec[None, :]
-        keys += bias[:, None, :]
-        tail = L - (nb - 1) * BLOCK
-        if tail < BLOCK:
-            keys[nb - 1, tail:] = 3.0 * direction[b].sum(dim=0).to(dev)  # poison past the end
-        if idx_dtype == "fp8":
-            kb = quant_e4m3(keys)
-        else:
-            kb = keys.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(nb, BLOCK, DIM * 2)
-        idx_pool[bt[b, :nb].long().to(dev)] = kb
-    if idx_dtype == "bf16":
-        idx_pool = idx_pool.view(torch.bfloat16).reshape(P, BLOCK, DIM)
+
+    def index_keys():
+        """(b, float keys [nb][128][128]) per sequence, from fresh generators
+        (NVFP4 walks the stream twice: amax first, then the same keys)."""
+        gi = _gen(dev, seed * 7919 + 3)
+        gsel = _gen("cpu", seed * 7919 + 4)
+        for b in range(S):
+            nb, L = nbs[b], seq_lens[b]
+            if nb == 0:
+                continue
+            if idx_dist == "normal":
+                keys = torch.randn(nb, BLOCK, DIM, generator=gi, device=dev)
+            elif idx_dist == "uniform":
+                keys = torch.rand(nb, BLOCK, DIM, generator=gi, device=dev) * 2.0 - 1.0
+            else:
+                raise ValueError(idx_dist)
+            r_last = nb - 1
+            bias = torch.zeros(nb, DIM, device=dev)
+            for g in range(G):
+                dvec = direction[b, g].to(dev)
+                if plant and r_last > 0:
+                    n = min(plant, r_last)
+                    picks = torch.randperm(r_last, generator=gsel)[:n]
+                    planted[(b, g)] = sorted(int(x) for x in picks)
+                    bias[picks.to(dev)] += 2.0 * dvec
+                if zipf is not None and r_last > 0:
+                    ranks = torch.randperm(r_last, generator=gsel).to(torch.float64) + 1.0  # block j -> rank
+                    w = (zipf_amp * ranks.pow(-zipf)).to(torch.float32).to(dev)
+                    bias[:r_last] += w[:, None] * dvec[None, :]
+            keys += bias[:, None, :]
+            tail = L - (nb - 1) * BLOCK
+            if tail < BLOCK:
+                keys[nb - 1, tail:] = 3.0 * direction[b].sum(dim=0).to(dev)  # poison past the end
+            yield b, keys
+
+    idx_sf = None
+    if idx_dtype == "nvfp4":
+        amax = 0.0
+        for _, keys in index_keys():
+            amax = max(amax, float(keys.abs().max()))
+        idx_gs = nvfp4_tensor_scale(amax)
+        idx_pool = torch.zeros(P, BLOCK, DIM // 2, dtype=torch.uint8, device=dev)
+        idx_sf = torch.zeros(P, BLOCK, DIM // 16, dtype=torch.uint8, device=dev)
+        for b, keys in index_keys():
+            pages = bt[b, :nbs[b]].long().to(dev)
+            idx_pool[pages], idx_sf[pages] = quant_nvfp4(keys, idx_gs)
+        idx_scale = idx_scale * idx_gs
+    elif idx_dtype in ("fp8", "bf16"):
+        bidx = 1 if idx_dtype == "fp8" else 2
+        idx_pool = torch.zeros(P, BLOCK, DIM * bidx, dtype=torch.uint8, device=dev)
+        for b, keys in index_keys():
+            if idx_dtype == "fp8":
+                kb = quant_e4m3(keys)
+            else:
+                kb = keys.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(nbs[b], BLOCK, DIM * 2)
+            idx_pool[bt[b, :nbs[b]].long().to(dev)] = kb
+        if idx_dtype == "bf16":
+            idx_pool = idx_pool.view(torch.bfloat16).reshape(P, BLOCK, DIM)
+    else:
+        raise ValueError(idx_dtype)
 
     # ---- K / V pools (i.i.d. N(0,1), generated page-chunk by page-chunk)
     def kv_pool(seed_k):
@@ -289,7 +316,8 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
                     q=q, iq=iq, idx_k=idx_pool, k=k, v=v, k_sf=k_sf, v_sf=v_sf,
                     block_table=bt.to(dev), seq_lens=torch.tensor(seq_lens, dtype=torch.int32, device=dev),
                     meta=dict(seed=seed, layout=layout, plant=plant, zipf=zipf, idx_dist=idx_dist,
-                              planted=planted))
+                              planted=planted),
+                    idx_sf=idx_sf)
 
 
 # The five workloads the method is evaluated on.  Every config uses 4 KV heads

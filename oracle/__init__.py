@@ -29,15 +29,18 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+IDX_FORMATS = {"bf16": 0, "fp8": 1, "nvfp4": 2}
+
+
 class _Problem(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("kv_nvfp4", ctypes.c_int32), ("idx_fp8", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("kv_nvfp4", ctypes.c_int32), ("idx_fmt", ctypes.c_int32),
                 ("sm_scale", ctypes.c_double), ("k_scale", ctypes.c_double), ("v_scale", ctypes.c_double),
                 ("idx_scale", ctypes.c_double),
                 ("q", ctypes.c_void_p), ("iq", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_sf", ctypes.c_void_p), ("v_sf", ctypes.c_void_p), ("idx_k", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("idx_sf", ctypes.c_void_p)]
 
 
 def _load():
@@ -74,11 +77,14 @@ class Problem:
 
     def __init__(self, *, num_seqs, q_len, num_q_heads, num_kv_heads, max_blocks_per_seq, num_pages, kv_dtype,
                  idx_dtype, sm_scale, k_scale, v_scale, idx_scale, q, iq, idx_k, k, v, k_sf, v_sf, block_table,
-                 seq_lens):
+                 seq_lens, idx_sf=None):
         c = np.ascontiguousarray
         self.arrays = dict(q=c(q), iq=c(iq), idx_k=c(idx_k), k=c(k), v=c(v),
                            k_sf=None if k_sf is None else c(k_sf), v_sf=None if v_sf is None else c(v_sf),
+                           idx_sf=None if idx_sf is None else c(idx_sf),
                            block_table=c(block_table, dtype=np.int32), seq_lens=c(seq_lens, dtype=np.int32))
+        if idx_dtype == "nvfp4" and idx_sf is None:
+            raise ValueError("NVFP4 index keys need their scales (idx_sf)")
         a = self.arrays
         self.num_seqs, self.q_len = int(num_seqs), int(q_len)
         self.num_q_heads, self.num_kv_heads = int(num_q_heads), int(num_kv_heads)
@@ -87,10 +93,11 @@ class Problem:
         self.sm_scale, self.k_scale = float(sm_scale), float(k_scale)
         self.v_scale, self.idx_scale = float(v_scale), float(idx_scale)
         self._s = _Problem(self.num_seqs, self.q_len, self.num_q_heads, self.num_kv_heads, self.max_blocks_per_seq,
-                           int(num_pages), 1 if kv_dtype == "nvfp4" else 0, 1 if idx_dtype == "fp8" else 0,
+                           int(num_pages), 1 if kv_dtype == "nvfp4" else 0, IDX_FORMATS[idx_dtype],
                            float(sm_scale), float(k_scale), float(v_scale), float(idx_scale),
                            _ptr(a["q"]), _ptr(a["iq"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["k_sf"]),
-                           _ptr(a["v_sf"]), _ptr(a["idx_k"]), _ptr(a["block_table"]), _ptr(a["seq_lens"]))
+                           _ptr(a["v_sf"]), _ptr(a["idx_k"]), _ptr(a["block_table"]), _ptr(a["seq_lens"]),
+                           _ptr(a["idx_sf"]))
 
     @classmethod
     def from_workload(cls, w):

@@ -52,7 +52,8 @@ typedef struct {
   int32_t max_blocks_per_seq;
   int32_t num_pages;
   int32_t kv_nvfp4;  /* 0: K/V bf16 [P][Hkv][128][128]; 1: NVFP4 values [P][Hkv][128][64] + E4M3 scales [P][Hkv][128][8] */
-  int32_t idx_fp8;   /* 0: index keys bf16 [P][128][128]; 1: FP8 E4M3 [P][128][128] */
+  int32_t idx_fmt;   /* index keys: 0 bf16 [P][128][128]; 1 FP8 E4M3 [P][128][128];
+                        2 NVFP4 values [P][128][64] + E4M3 scales idx_sf [P][128][8] */
   double sm_scale;
   double k_scale;
   double v_scale;
@@ -66,6 +67,7 @@ typedef struct {
   const void* idx_k;
   const int32_t* block_table; /* [num_seqs][max_blocks_per_seq] */
   const int32_t* seq_lens;    /* [num_seqs] */
+  const uint8_t* idx_sf;      /* NVFP4 index keys only: E4M3 scale of each 16-element group */
 } oracle_problem;
 
 /* ---- 1. decoding stored bytes ------------------------------------------ */
@@ -120,10 +122,19 @@ static double kv_elem(const oracle_problem* p, const void* pool, const uint8_t* 
   return msa_oracle_e2m1(nib) * group_scale * tensor_scale;
 }
 
-/* One index-key element d of token `tok` of physical page `page`. */
+/* One index-key element d of token `tok` of physical page `page`.  NVFP4 index
+ * keys ("NVFP4 indexer DCP" of the vLLM MiniMax-M3.1-Flash post: the index
+ * cache in NVFP4) use the K/V layout with one head: element 2k in the low
+ * nibble of byte k of the token row, elements 16c..16c+15 sharing scale byte c. */
 static double idx_elem(const oracle_problem* p, int64_t page, int tok, int d) {
-  int64_t off = (page * OR_BLOCK + tok) * OR_DIM + d;
-  if (p->idx_fp8) return msa_oracle_e4m3(((const uint8_t*)p->idx_k)[off]) * p->idx_scale;
+  int64_t row = page * OR_BLOCK + tok;
+  if (p->idx_fmt == 2) {
+    uint8_t byte = ((const uint8_t*)p->idx_k)[row * (OR_DIM / 2) + d / 2];
+    uint8_t nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    return msa_oracle_e2m1(nib) * msa_oracle_e4m3(p->idx_sf[row * (OR_DIM / 16) + d / 16]) * p->idx_scale;
+  }
+  int64_t off = row * OR_DIM + d;
+  if (p->idx_fmt == 1) return msa_oracle_e4m3(((const uint8_t*)p->idx_k)[off]) * p->idx_scale;
   return msa_oracle_bf16(((const uint16_t*)p->idx_k)[off]) * p->idx_scale;
 }
 

@@ -38,7 +38,9 @@ def dense_seq(P, b: int):
     L = int(a["seq_lens"][b])
     nb = (L - 1) // 128 + 1 if L > 0 else 0
     pages = a["block_table"][b, :nb].astype(np.int64)
-    if a["idx_k"].dtype == np.uint8:
+    if a.get("idx_sf") is not None:
+        idx = nvfp4_t(a["idx_k"][pages], a["idx_sf"][pages], P.idx_scale)
+    elif a["idx_k"].dtype == np.uint8:
         idx = e4m3_t(a["idx_k"][pages]) * P.idx_scale
     else:
         idx = bf16_t(a["idx_k"][pages]) * P.idx_scale

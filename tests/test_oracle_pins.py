@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from block_sparse_attention_msa_amd import synth
-from _ref import BYTE_MODEL, E2M1_TABLE, bf16_t, dense_seq, e4m3_t, make_problem, row_queries
+from _ref import BYTE_MODEL, E2M1_TABLE, bf16_t, dense_seq, e4m3_t, make_problem, nvfp4_t, row_queries
 
 
 # ---- formats -------------------------------------------------------------
@@ -279,8 +279,10 @@ def test_split_merge_exact():
 
 def test_maxpool_matches_torch_amax():
     """P-i: block scores == torch.amax over [nb,128] of fp64 token scores
-    (idx @ iq with torch's matmul), -inf padding past the end."""
-    for kv, idx in [("nvfp4", "fp8"), ("bf16", "bf16")]:
+    (idx @ iq with torch's matmul), -inf padding past the end.  The index keys
+    are decoded test-side (torch's E4M3 cast, the OCP E2M1 table), for FP8,
+    bf16 and NVFP4 index keys."""
+    for kv, idx in [("nvfp4", "fp8"), ("bf16", "bf16"), ("nvfp4", "nvfp4")]:
         w = synth.make_workload(seq_lens=[3001, 128 * 20], kv_dtype=kv, idx_dtype=idx, plant=3, seed=8,
                                 layout="paged", max_blocks_per_seq=30)
         P = make_problem(w)
@@ -298,6 +300,41 @@ def test_maxpool_matches_torch_amax():
                 assert nbv == nb
                 np.testing.assert_allclose(bs[:nb], ref[g].numpy(), rtol=1e-12, atol=1e-12)
                 assert np.isneginf(bs[nb:]).all()
+
+
+def test_nvfp4_index_keys_round_trip():
+    """NVFP4 index keys: values placed exactly on the format's grid (E2M1 code
+    x E4M3 group scale x power-of-two tensor scale, every group holding a +-6)
+    survive the generator's quantiser unchanged, and the test-side decode
+    (OCP table, torch's E4M3 cast; element 2i in the low nibble) returns them;
+    the oracle's block scores of such keys equal fp64 matmul + amax of the
+    original floats."""
+    rng = np.random.default_rng(11)
+    gs = 2.0 ** -7
+    grid = E2M1_TABLE.numpy()
+    codes = rng.integers(0, 16, size=(3, 128, 8, 16))
+    codes[..., 0] = 7                                   # +6 in every group: amax16 = 6 * s * gs
+    sc_bytes = rng.integers(0x08, 0x78, size=(3, 128, 8)).astype(np.uint8)  # normal E4M3, below 448
+    sc = e4m3_t(sc_bytes).numpy()
+    x = torch.from_numpy(grid[codes] * sc[..., None] * gs).reshape(3, 128, 128)
+    packed, scales = synth.quant_nvfp4(x, gs)
+    assert np.array_equal(scales.numpy(), sc_bytes)
+    back = nvfp4_t(packed.numpy(), scales.numpy(), gs)
+    assert torch.equal(back, x)
+    w = synth.make_workload(seq_lens=[3 * 128 - 9], idx_dtype="nvfp4", seed=12)
+    w.idx_k[:] = packed
+    w.idx_sf[:] = scales
+    w.idx_scale = gs
+    P = make_problem(w)
+    _, iq = row_queries(P, 0)
+    s = x.reshape(3 * 128, 128)[:3 * 128 - 9] @ iq.T
+    pad = torch.full((3 * 128, 4), -math.inf, dtype=torch.float64)
+    pad[:3 * 128 - 9] = s
+    ref = pad.reshape(3, 128, 4).amax(dim=1).T
+    for g in range(4):
+        bs, nbv = P.block_scores(0, g)
+        assert nbv == 3
+        np.testing.assert_allclose(bs[:3], ref[g].numpy(), rtol=1e-12, atol=1e-12)
 
 
 def test_tail_is_masked():
