@@ -45,8 +45,9 @@ def cpu_model() -> str:
 def scan_bytes(w) -> float:
     """Algorithmic bytes of one index-scan launch: every visible token's index
     key, the used block-table entries, the index queries, the block scores."""
+    from block_sparse_attention_msa_amd.synth import IDX_BYTES_PER_TOKEN
     lens = [int(x) for x in w.seq_lens.cpu().tolist()]
-    key_b = 128 * (1 if w.idx_dtype == "fp8" else 2)
+    key_b = IDX_BYTES_PER_TOKEN[w.idx_dtype]
     nbs = [((L - 1) // 128 + 1) if L > 0 else 0 for L in lens]
     return (sum(lens) * key_b + sum(nbs) * 4 + w.rows * w.num_kv_heads * 128 * 2
             + w.rows * w.num_kv_heads * w.max_blocks_per_seq * 4)
@@ -68,7 +69,7 @@ def scan_flops(w) -> float:
 def clone_workload(w):
     import copy
     w2 = copy.copy(w)
-    for name in ("q", "iq", "idx_k", "k", "v", "k_sf", "v_sf", "block_table", "seq_lens"):
+    for name in ("q", "iq", "idx_k", "idx_sf", "k", "v", "k_sf", "v_sf", "block_table", "seq_lens"):
         t = getattr(w, name)
         setattr(w2, name, None if t is None else t.clone())
     return w2
@@ -251,7 +252,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-idx/nvfp4-kv, fp32 accumulate",
+        "dtype": f"{w.idx_dtype}-idx/{w.kv_dtype}-kv, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": args.config, "num_seqs": w.num_seqs, "context_tokens": int(w.seq_lens[0]),
                    "q_len": w.q_len, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": 128,

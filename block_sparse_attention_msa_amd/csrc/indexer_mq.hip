@@ -196,7 +196,7 @@ hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream) {
   const int cus = device_cus();
   const int wgs = (int)(groups >= cus ? 1 : cus / groups);
   dim3 grid((unsigned)(groups * wgs));
-  if (a.idx_fp8)
+  if (a.idx_fmt == kIdxFp8)
     scan_mq_kernel<true><<<grid, kMqThreads, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
                                                            a.seq_lens, a.iq, a.block_scores, q_len, a.mbps, nchunks, wgs,
                                                            a.idx_scale);

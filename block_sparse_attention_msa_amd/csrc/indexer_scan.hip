@@ -38,6 +38,22 @@ __global__ __launch_bounds__(kScanWaves * kWave, 5) void scan_decode_kernel(cons
                         block_scores + (size_t)b * kGroups * mbps, mbps, jbeg, jend, idx_scale, lane);
 }
 
+// NVFP4 index keys: 8 waves, one page each; 1 KB of LDS per wave for the
+// page's scales.
+__global__ __launch_bounds__(kScanWaves * kWave, 4) void scan_decode_nvfp4_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int mbps,
+    float idx_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kScanWaves][kBlock * 8];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int j = blockIdx.x * kScanWaves + wave;
+  if (j >= mbps) return;
+  scan_wave_nvfp4(codes, scales, block_table + (size_t)b * mbps, seq_lens[b], iq + (size_t)b * kGroups * kDim,
+                  block_scores + (size_t)b * kGroups * mbps, mbps, j, j + 1, idx_scale, lds_sc[wave], lane);
+}
+
 }  // namespace
 
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
@@ -48,7 +64,12 @@ hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
   constexpr int waves_per_wg = kScanWaves;
   dim3 grid((a.mbps + waves_per_wg * bpw - 1) / (waves_per_wg * bpw), a.num_seqs);
   dim3 block(waves_per_wg * kWave);
-  if (a.idx_fp8)
+  if (a.idx_fmt == kIdxNvfp4) {
+    dim3 g2((a.mbps + kScanWaves - 1) / kScanWaves, a.num_seqs);
+    scan_decode_nvfp4_kernel<<<g2, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
+                                                       a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
+                                                       a.idx_scale);
+  } else if (a.idx_fmt == kIdxFp8)
     scan_decode_kernel<true><<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale);
   else

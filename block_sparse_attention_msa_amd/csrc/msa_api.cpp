@@ -49,8 +49,10 @@ msa_status check_shape(const msa_shape* s) {
   if (s->num_pages < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages = %d < 1", s->num_pages);
   if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "kv_dtype = %d", s->kv_dtype);
-  if (s->idx_dtype != MSA_IDX_BF16 && s->idx_dtype != MSA_IDX_FP8_E4M3)
+  if (s->idx_dtype != MSA_IDX_BF16 && s->idx_dtype != MSA_IDX_FP8_E4M3 && s->idx_dtype != MSA_IDX_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "idx_dtype = %d", s->idx_dtype);
+  if (s->idx_dtype == MSA_IDX_NVFP4 && s->q_len != 1)
+    return fail(MSA_ERR_UNSUPPORTED, "NVFP4 index keys with q_len = %d (supported for q_len 1)", s->q_len);
   if (!finite_pos(s->sm_scale) || !finite_pos(s->k_scale) || !finite_pos(s->v_scale) || !finite_pos(s->idx_scale))
     return fail(MSA_ERR_INVALID_ARGUMENT, "scales must be finite and > 0 (sm %g, k %g, v %g, idx %g)",
                 (double)s->sm_scale, (double)s->k_scale, (double)s->v_scale, (double)s->idx_scale);
@@ -65,6 +67,8 @@ msa_status check_cache(const msa_shape* s, const msa_cache* c, bool need_idx, bo
   if (!c) return fail(MSA_ERR_INVALID_ARGUMENT, "cache is NULL");
   if (!c->block_table || !c->seq_lens) return fail(MSA_ERR_INVALID_ARGUMENT, "block_table / seq_lens is NULL");
   if (need_idx && !c->idx_k) return fail(MSA_ERR_INVALID_ARGUMENT, "idx_k is NULL");
+  if (need_idx && s->idx_dtype == MSA_IDX_NVFP4 && !c->idx_sf)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "idx_sf is NULL for NVFP4 index keys");
   if (need_kv) {
     if (!c->k || !c->v) return fail(MSA_ERR_INVALID_ARGUMENT, "k / v is NULL");
     if (s->kv_dtype == MSA_KV_NVFP4 && (!c->k_sf || !c->v_sf))
@@ -115,7 +119,8 @@ msa::ScanArgs scan_args(const msa_shape* s, const msa_cache* c, const void* idx_
   a.num_seqs = s->num_seqs;
   a.mbps = s->max_blocks_per_seq;
   a.idx_scale = s->idx_scale;
-  a.idx_fp8 = s->idx_dtype == MSA_IDX_FP8_E4M3;
+  a.idx_sf = c->idx_sf;
+  a.idx_fmt = s->idx_dtype == MSA_IDX_NVFP4 ? msa::kIdxNvfp4 : s->idx_dtype == MSA_IDX_FP8_E4M3 ? msa::kIdxFp8 : msa::kIdxBf16;
   return a;
 }
 

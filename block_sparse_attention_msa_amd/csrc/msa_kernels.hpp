@@ -14,8 +14,11 @@ constexpr int kGroups = 4;                // KV heads == GQA groups
 constexpr int kHeadsPerGroup = 4;         // query heads per group
 constexpr int kMaxBlocksPerSeq = 16384;   // 2M tokens per sequence
 
+enum IdxFormat { kIdxBf16 = 0, kIdxFp8 = 1, kIdxNvfp4 = 2 };
+
 struct ScanArgs {
-  const void* idx_pool;        // [P][128][128] FP8 or bf16
+  const void* idx_pool;        // [P][128][128] FP8 or bf16, or [P][128][64] NVFP4 codes
+  const uint8_t* idx_sf;       // NVFP4: E4M3 scales [P][128][8]
   const int32_t* block_table;  // [S][mbps]
   const int32_t* seq_lens;     // [S]
   const uint16_t* iq;          // bf16 [S][4][128]
@@ -23,7 +26,7 @@ struct ScanArgs {
   int num_seqs;
   int mbps;
   float idx_scale;
-  bool idx_fp8;
+  int idx_fmt;                 // IdxFormat
 };
 // Decode (one query row per sequence) index scan + block max-pool.
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream);

@@ -103,3 +103,110 @@ __device__ __forceinline__ void scan_wave(const uint8_t* __restrict__ idx_pool, 
 }
 
 }  // namespace msa
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// NVFP4 index keys (E2M1 codes [P][128][64] + E4M3 scales [P][128][8]): block
+// scores of blocks [jbeg, jend) of one sequence, one wave per block.
+//
+// With 64 B of codes per token a wave-load holds 16 whole tokens, so the scan
+// takes the attention's exact QK tile: v_mfma_f32_16x16x32_bf16 with A = the
+// codes of 16 tokens (E2M1 -> bf16, exact, one 16-B load = 32 dims per lane)
+// and B = the four index queries, MFMA column (group hq, slot jj) holding
+// group hq's dims of scale groups 2jj (K steps 0-1, accumulator a0) and 2jj+1
+// (K steps 2-3, a1).  Each 16-dim partial dot is scaled once by its token's
+// E4M3 group scale in fp32, and a reduce-scatter over the quad leaves lane
+// (c, hq, jj) with the full score of token 16T + 4c + jj for group hq.
+// Products are exact in fp32 (E2M1 x bf16 and the scale products), sums fp32.
+// VALU per token: 4 conversions, 2 scale products and the reductions, about
+// a third of the FP8 scan's per-byte work at 72 B per token.
+__device__ __forceinline__ void scan_wave_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                const int32_t* __restrict__ bt_row, int L,
+                                                const uint16_t* __restrict__ iq_row, float* __restrict__ bs_row,
+                                                int mbps, int jbeg, int jend, float idx_scale, uint8_t* lds_sc,
+                                                int lane) {
+  const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int hq = n >> 2;   // index query (group) of this MFMA column
+  const int jj = n & 3;    // scale-group slot of this column
+
+  // B operands: column (hq, jj) takes group hq's dims 32c + 8s + e when jj == c
+  bf16x8 qb[4];
+  {
+    const uint16_t* qh = iq_row + hq * kDim + 32 * c;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 w = jj == c ? *reinterpret_cast<const uint4*>(qh + 8 * s) : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  for (int j = jbeg; j < jend; ++j) {
+    if (j >= nbv) {
+      if (lane < 4) bs_row[lane * mbps + j] = -INFINITY;
+      continue;
+    }
+    const int64_t page = bt_row[j];
+    const uint8_t* kbase = codes + page * (kBlock * kDim / 2);
+    u32x4 kv[8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+      kv[T] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)(16 * T + n) * 64 + 16 * c));
+    const u32x4 sc16 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(scales + page * (kBlock * 8) + lane * 16));
+    *reinterpret_cast<u32x4*>(lds_sc + lane * 16) = sc16;  // [token][group], this wave's 1 KB
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int visible = L - j * kBlock;  // tokens of this block at or before the query
+    float m = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const uint32_t w[4] = {kv[T].x, kv[T].y, kv[T].z, kv[T].w};
+      bf16x8 ka[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x2 e0 = e2m1x2_to_bf16x2<0>(w[s]);
+        const bf16x2 e1 = e2m1x2_to_bf16x2<1>(w[s]);
+        const bf16x2 e2 = e2m1x2_to_bf16x2<2>(w[s]);
+        const bf16x2 e3 = e2m1x2_to_bf16x2<3>(w[s]);
+        ka[s] = bf16x8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+      }
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0], qb[0], a0, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1], qb[1], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[2], qb[2], a1, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[3], qb[3], a1, 0, 0, 0);
+      // slot jj's partial of token 16T + 4c + i: groups 2jj (a0) and 2jj+1 (a1)
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * T + 4 * c + i;
+        const uint32_t sw = *reinterpret_cast<const uint16_t*>(lds_sc + tok * 8 + 2 * jj);
+        const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+        v[i] = fmaf(sc.x, a0[i], sc.y * a1[i]);
+      }
+      // reduce-scatter over the quad: lane jj ends with the full score of token i = jj
+      const bool b1 = (jj & 2) != 0, b0 = (jj & 1) != 0;
+      float y0 = b1 ? v[2] : v[0], y1 = b1 ? v[3] : v[1];
+      const float x0 = b1 ? v[0] : v[2], x1 = b1 ? v[1] : v[3];
+      y0 += dpp<kDppXor2>(x0);
+      y1 += dpp<kDppXor2>(x1);
+      const float keep = b0 ? y1 : y0, send = b0 ? y0 : y1;
+      const float dot = keep + dpp<kDppXor1>(send);
+      m = fmaxf(m, 16 * T + 4 * c + jj < visible ? dot : -INFINITY);
+    }
+    // max over the 16 lanes of group hq: c (lane bits 4, 5) and jj (bits 0, 1)
+    m = fmaxf(m, dpp<kDppXor1>(m));
+    m = fmaxf(m, dpp<kDppXor2>(m));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (c == 0 && jj == 0) bs_row[hq * mbps + j] = m * idx_scale;
+    __builtin_amdgcn_wave_barrier();  // the next block rewrites this wave's scales
+  }
+}
+
+}  // namespace msa

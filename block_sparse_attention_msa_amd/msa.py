@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_HIP = range(5)
 MSA_KV_BF16, MSA_KV_NVFP4 = 0, 1
-MSA_IDX_BF16, MSA_IDX_FP8_E4M3 = 0, 1
+MSA_IDX_BF16, MSA_IDX_FP8_E4M3, MSA_IDX_NVFP4 = 0, 1, 2
+_IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
             "msa_sparse_attn_decode", "msa_decode", "msa_status_string", "msa_last_error")
 
@@ -39,27 +40,29 @@ class MsaShape(ctypes.Structure):
     def from_workload(cls, w) -> "MsaShape":
         return cls(w.num_seqs, w.q_len, w.num_q_heads, w.num_kv_heads, w.max_blocks_per_seq, w.num_pages,
                    MSA_KV_NVFP4 if w.kv_dtype == "nvfp4" else MSA_KV_BF16,
-                   MSA_IDX_FP8_E4M3 if w.idx_dtype == "fp8" else MSA_IDX_BF16,
+                   _IDX[w.idx_dtype],
                    w.sm_scale, w.k_scale, w.v_scale, w.idx_scale)
 
 
 class MsaCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_sf", ctypes.c_void_p), ("v_sf", ctypes.c_void_p),
-                ("idx_k", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("idx_k", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("idx_sf", ctypes.c_void_p)]
 
     @classmethod
-    def from_tensors(cls, *, k, v, k_sf, v_sf, idx_k, block_table, seq_lens) -> "MsaCache":
+    def from_tensors(cls, *, k, v, k_sf, v_sf, idx_k, block_table, seq_lens, idx_sf=None) -> "MsaCache":
         for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
             if t.dtype != torch.int32:
                 raise TypeError(f"{name} must be int32")
-        c = cls(_ptr(k), _ptr(v), _ptr(k_sf), _ptr(v_sf), _ptr(idx_k), _ptr(block_table), _ptr(seq_lens))
-        c._keep = (k, v, k_sf, v_sf, idx_k, block_table, seq_lens)
+        c = cls(_ptr(k), _ptr(v), _ptr(k_sf), _ptr(v_sf), _ptr(idx_k), _ptr(block_table), _ptr(seq_lens),
+                _ptr(idx_sf))
+        c._keep = (k, v, k_sf, v_sf, idx_k, block_table, seq_lens, idx_sf)
         return c
 
     @classmethod
     def from_workload(cls, w) -> "MsaCache":
         return cls.from_tensors(k=w.k, v=w.v, k_sf=w.k_sf, v_sf=w.v_sf, idx_k=w.idx_k, block_table=w.block_table,
-                                seq_lens=w.seq_lens)
+                                seq_lens=w.seq_lens, idx_sf=w.idx_sf)
 
 
 def _ptr(t):

@@ -337,6 +337,10 @@ CONFIGS = {
     # batch 2 x 256 new query tokens appended causally to a 128K paged context
     "verify_b2_q256_128k": dict(seq_lens=[131072 + 256] * 2, q_len=256, zipf=1.1, layout="paged",
                                 shared_bias_iq=True, seed=4),
+    # the batch-32 x 128K shape with the index cache in NVFP4 (72 B per token
+    # instead of 128 B), the M3.1 production setting; not one of the five above
+    "paged_b32_128k_nvfp4_idx": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", idx_dtype="nvfp4",
+                                     seed=2),
 }
 
 

@@ -36,7 +36,12 @@
  *  - q      bf16 [rows][num_q_heads][128]; iq bf16 [rows][num_kv_heads][128].
  *  - idx_k  index-key pool, one shared head: FP8 E4M3 (OCP, bias 7) bytes
  *           [num_pages][128 tokens][128], or bf16 [num_pages][128][128];
- *           value = stored x idx_scale.
+ *           value = stored x idx_scale.  NVFP4 ("NVFP4 indexer DCP" of the
+ *           M3.1 post: the index cache in NVFP4, 72 B per token): uint8
+ *           [num_pages][128 tokens][64] (element 2i in the low nibble of byte
+ *           i, E2M1) plus idx_sf uint8 E4M3 [num_pages][128 tokens][8];
+ *           value = e2m1 x scale x idx_scale.  NVFP4 index keys are
+ *           supported for q_len 1 (MSA_ERR_UNSUPPORTED otherwise).
  *  - k, v   NVFP4: uint8 [num_pages][num_kv_heads][128 tokens][64], element 2i
  *           in the low nibble of byte i (E2M1), plus k_sf / v_sf uint8 E4M3
  *           [num_pages][num_kv_heads][128 tokens][8] (one scale per 16
@@ -73,7 +78,7 @@ typedef enum {
 } msa_status;
 
 typedef enum { MSA_KV_BF16 = 0, MSA_KV_NVFP4 = 1 } msa_kv_dtype;
-typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1 } msa_idx_dtype;
+typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1, MSA_IDX_NVFP4 = 2 } msa_idx_dtype;
 
 /* Host-side problem shape; read only during the call. */
 typedef struct {
@@ -99,6 +104,7 @@ typedef struct {
   const void* idx_k;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const uint8_t* idx_sf;      /* NVFP4 index keys only; NULL otherwise */
 } msa_cache;
 
 /* Bytes of device workspace msa_decode needs for this shape: the fp32 block

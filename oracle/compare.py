@@ -24,12 +24,20 @@ TIE_REL = 1e-4
 
 
 def _ik_dense(P, b):
+    """The sequence's index keys as fp64 stored values (before idx_scale)."""
     a = P.arrays
     L = int(a["seq_lens"][b])
     nb = (L - 1) // 128 + 1 if L > 0 else 0
     pages = a["block_table"][b, :nb].astype(np.int64)
     raw = a["idx_k"][pages]
-    if raw.dtype == np.uint8:
+    if a.get("idx_sf") is not None:  # NVFP4: E2M1 code (low nibble first) x E4M3 group scale
+        from . import e2m1
+        table = torch.tensor([e2m1(n) for n in range(16)], dtype=torch.float64)
+        p = torch.from_numpy(np.ascontiguousarray(raw)).to(torch.int64)
+        codes = torch.stack([p & 15, p >> 4], dim=-1).reshape(nb, 128, 128)
+        sc = torch.from_numpy(np.ascontiguousarray(a["idx_sf"][pages])).view(torch.float8_e4m3fn).to(torch.float64)
+        ik = table[codes] * sc.repeat_interleave(16, dim=-1)
+    elif raw.dtype == np.uint8:
         ik = torch.from_numpy(np.ascontiguousarray(raw)).view(torch.float8_e4m3fn).to(torch.float64)
     else:
         ik = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).to(torch.float64)

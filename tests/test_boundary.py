@@ -42,7 +42,7 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
 
 
 def _cache(**kw):
-    d = dict(k=FAKE, v=FAKE, k_sf=FAKE, v_sf=FAKE, idx_k=FAKE, block_table=FAKE, seq_lens=FAKE)
+    d = dict(k=FAKE, v=FAKE, k_sf=FAKE, v_sf=FAKE, idx_k=FAKE, block_table=FAKE, seq_lens=FAKE, idx_sf=FAKE)
     d.update(kw)
     return msa.MsaCache(*[d[f] for f, _ in msa.MsaCache._fields_])
 
@@ -91,6 +91,15 @@ def test_null_and_pointer_validation():
     # bf16 K/V needs no scale arrays; validation then proceeds to the workspace check
     assert _decode(_shape(kv_dtype=msa.MSA_KV_BF16), cache=_cache(k_sf=None, v_sf=None), nbytes=0) == \
         msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_nvfp4_index_keys_validation():
+    """NVFP4 index keys need their scale array and are supported for q_len 1."""
+    s = _shape(idx_dtype=msa.MSA_IDX_NVFP4)
+    assert _decode(s, cache=_cache(idx_sf=None)) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert "idx_sf" in msa.last_error()
+    assert _decode(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=4)) == msa.MSA_ERR_UNSUPPORTED
+    assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=4))) == 0
 
 
 def test_workspace_size_and_too_small():

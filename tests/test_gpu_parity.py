@@ -98,7 +98,8 @@ def test_paged_b4_512k_config_sampled(dev):
             assert set(w.meta["planted"][(b, g)]) <= set(sel[b, g].tolist())
 
 
-@pytest.mark.parametrize("kv,idx", [("nvfp4", "fp8"), ("bf16", "bf16"), ("nvfp4", "bf16"), ("bf16", "fp8")])
+@pytest.mark.parametrize("kv,idx", [("nvfp4", "fp8"), ("bf16", "bf16"), ("nvfp4", "bf16"), ("bf16", "fp8"),
+                                    ("nvfp4", "nvfp4"), ("bf16", "nvfp4")])
 def test_ragged_lengths_all_dtypes(dev, kv, idx):
     """Ragged contexts: 1 token, partial blocks, exactly 16 and 17 blocks,
     a padded row, table wider than any sequence, paged layout."""
@@ -137,6 +138,30 @@ def test_exhaustive_format_codes(dev):
     w.k_scale = w.v_scale = 1.0 / (448 * 6)
     w.idx_scale = 1.0 / 64
     check_workload(w, label="exhaustive codes")
+
+
+def test_exhaustive_nvfp4_index_codes(dev):
+    """NVFP4 index keys: every E2M1 nibble in every position of a token row and
+    every finite E4M3 group scale appear; checks the NVFP4 scan's conversions,
+    nibble order and scale indexing end to end."""
+    w = synth.make_workload(seq_lens=[128 * 37, 128 * 20 + 11], idx_dtype="nvfp4", seed=26, layout="paged", device=dev)
+    codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8, device=dev)
+    nib = torch.arange(256, dtype=torch.uint8, device=dev)
+    m = w.idx_k.numel()
+    w.idx_k.view(-1).copy_(nib.repeat(m // 256 + 1)[:m])
+    perm = torch.randperm(m, generator=torch.Generator().manual_seed(3)).to(dev)
+    w.idx_k.view(-1).copy_(w.idx_k.view(-1)[perm])
+    m = w.idx_sf.numel()
+    w.idx_sf.view(-1).copy_(codes.repeat(m // codes.numel() + 1)[:m])
+    w.idx_scale = 1.0 / 512
+    check_workload(w, label="exhaustive NVFP4 index codes")
+
+
+def test_paged_b32_128k_nvfp4_index_sampled(dev):
+    """The headline shape with NVFP4 index keys, in the bench's launch
+    configuration, checked on sampled rows."""
+    w = synth.make_config("paged_b32_128k_nvfp4_idx", device=dev)
+    check_workload(w, rows=[0, 13, 31])
 
 
 def test_selection_kernel_exact_on_ties(dev):
