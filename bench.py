@@ -98,7 +98,10 @@ def cpu_baseline(w, sample_seqs: int, t_gpu_us: float):
 
 COPY_BYTES = 512 << 20
 SCAN_SOURCES = ("indexer_scan.hip", "scan_device.hpp", "msa_device.hpp", "msa_kernels.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_paged_b32_128k_traffic.json")
+
+
+def traffic_file(config: str) -> str:
+    return os.path.join(ROOT, "profiles", f"scan_{config}_traffic.json")
 
 
 def scan_source_hash() -> str:
@@ -109,12 +112,12 @@ def scan_source_hash() -> str:
     return h.hexdigest()
 
 
-def scan_traffic():
+def scan_traffic(config: str):
     """HBM bytes per scan launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (each scaled by what the counter read for a plain copy of
-    known size), or None if the scan's sources changed since."""
+    known size), or None if there are none or the scan's sources changed since."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(config)))
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != scan_source_hash():
@@ -122,10 +125,54 @@ def scan_traffic():
     return rec.get("bytes_per_launch")
 
 
+def _counter_means(run_dir: str, counter: str):
+    """{kernel name: (mean counter value per dispatch, dispatches)} from a
+    rocprofv3 --pmc CSV run directory."""
+    import csv
+    import glob
+    sums = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            k = r["Kernel_Name"]
+            v, n = sums.get(k, (0.0, 0))
+            sums[k] = (v + float(r["Counter_Value"]), n + 1)
+    return {k: (v / n, n) for k, (v, n) in sums.items()}
+
+
+def write_traffic(config: str, fetch_dir: str, write_dir: str):
+    """Turns the FETCH_SIZE and WRITE_SIZE runs of `--mode counters` into the
+    traffic record of the config's scan: each counter is scaled by what it
+    read for the plain copy of COPY_BYTES in the same runs."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    scan = [k for k in fetch if "scan_decode" in k]
+    if len(scan) != 1:
+        raise SystemExit(f"expected one scan kernel in {fetch_dir}, found {scan}")
+    scan = scan[0]
+    # the calibration kernel: torch's negation of COPY_BYTES, once per scan launch
+    copy = [k for k in write if "neg" in k.lower() and k in fetch and write[k][1] == fetch[scan][1]]
+    if len(copy) != 1:
+        raise SystemExit(f"expected one calibration kernel in {write_dir}, found {copy}")
+    copy = copy[0]
+    fs, ws = COPY_BYTES / (fetch[copy][0] * 1024.0), COPY_BYTES / (write[copy][0] * 1024.0)
+    fb, wb = fetch[scan][0] * 1024.0 * fs, write[scan][0] * 1024.0 * ws
+    import re
+    rec = {"kernel": re.search(r"scan_decode\w*(?:<[^>]*>)?", scan).group(0), "workload": config, "source_sha256": scan_source_hash(),
+           "fetch_kib_per_dispatch_raw": fetch[scan][0], "write_kib_per_dispatch_raw": write[scan][0],
+           "copy_fetch_kib_raw": fetch[copy][0], "copy_write_kib_raw": write[copy][0], "copy_bytes": COPY_BYTES,
+           "fetch_scale": fs, "write_scale": ws, "fetch_bytes": fb, "write_bytes": wb,
+           "bytes_per_launch": int(round(fb + wb)), "dispatches": fetch[scan][1]}
+    with open(traffic_file(config), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def run_counter_pass(args, w, copies, shape, caches):
     """Launches for hardware-counter runs: the index scan (steps x) and a plain
-    device copy of COPY_BYTES (steps x) whose FETCH_SIZE / WRITE_SIZE per
-    dispatch calibrate the counters against a known byte count."""
+    streaming kernel over COPY_BYTES (torch's negation: reads and writes
+    COPY_BYTES, steps x) whose FETCH_SIZE / WRITE_SIZE per dispatch calibrate
+    the counters against a known byte count."""
     import torch
     from block_sparse_attention_msa_amd import msa
     dev = w.q.device
@@ -135,7 +182,7 @@ def run_counter_pass(args, w, copies, shape, caches):
     for i in range(args.steps):
         c = copies[i % len(copies)]
         msa.msa_indexer_score(shape, caches[i % len(copies)], c.iq, bs)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log(f"[bench] counters pass: {args.steps} scan launches ({scan_bytes(w)} algorithmic B each), "
         f"{args.steps} copies of {COPY_BYTES} B")
@@ -152,7 +199,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
                     help="counters: only the scan kernel and a plain 512 MiB copy of known size, for rocprofv3 --pmc")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/scan_<config>_traffic.json from the rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                         "runs of --mode counters (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.config, *args.write_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the MSA decode step; runs on more than one GPU are not "
@@ -224,7 +277,7 @@ def main():
     if w.q_len == 1:
         roofline = {"bound": "hbm", "kernel": "index scan + block max-pool", "achieved": round(scan_gbps, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
-                    "traffic": scan_traffic() if args.config == "paged_b32_128k" else None,
+                    "traffic": scan_traffic(args.config),
                     "launch_us": round(scan_us, 2), "algorithmic_bytes": int(sb)}
     else:  # the multi-query scan is a dense contraction on the matrix cores
         fl = scan_flops(w)

@@ -38,17 +38,21 @@ __global__ __launch_bounds__(kScanWaves * kWave, 5) void scan_decode_kernel(cons
                         block_scores + (size_t)b * kGroups * mbps, mbps, jbeg, jend, idx_scale, lane);
 }
 
-// NVFP4 index keys: 8 waves, one page each; 1 KB of LDS per wave for the
-// page's scales.
-__global__ __launch_bounds__(kScanWaves * kWave, 4) void scan_decode_nvfp4_kernel(
+// NVFP4 index keys: one page per wave; 1 KB of LDS per wave for the scales.
+// 4-wave workgroups at 6 waves per SIMD (at most 85 VGPRs), from a sweep on
+// the batch-32 x 128K shape: 48.0-48.4 us, against 49.4-54.2 us for 8 waves
+// at 5 per SIMD, 53.7-55.5 us for 16 waves, 59-62 us for two pages per wave
+// with the second page's loads issued ahead, and 70 us at 7 per SIMD.
+constexpr int kNvfp4ScanWaves = 4;
+__global__ __launch_bounds__(kNvfp4ScanWaves * kWave, 6) void scan_decode_nvfp4_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int mbps,
     float idx_scale) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kScanWaves][kBlock * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kNvfp4ScanWaves][kBlock * 8];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int j = blockIdx.x * kScanWaves + wave;
+  const int j = blockIdx.x * kNvfp4ScanWaves + wave;
   if (j >= mbps) return;
   scan_wave_nvfp4(codes, scales, block_table + (size_t)b * mbps, seq_lens[b], iq + (size_t)b * kGroups * kDim,
                   block_scores + (size_t)b * kGroups * mbps, mbps, j, j + 1, idx_scale, lds_sc[wave], lane);
@@ -58,15 +62,16 @@ __global__ __launch_bounds__(kScanWaves * kWave, 4) void scan_decode_nvfp4_kerne
 
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
   // 8-wave workgroups, one page per wave: measured best on the batch-32 x
-  // 128K workload with 5 waves per SIMD (81.4-81.7 us vs 82.2-83.3 us for 2 or
-  // 4 pages per wave and 82.8-85.7 us at 4 waves per SIMD).
+  // 128K workload with 5 waves per SIMD (81.4-84.2 us vs 82.2-83.3 us for 2 or
+  // 4 pages per wave, 82.8-85.7 us at 4 waves per SIMD, 84.0-85.1 us for 2- or
+  // 4-wave workgroups and 116 us at 6 waves per SIMD).
   const int bpw = 1;
   constexpr int waves_per_wg = kScanWaves;
   dim3 grid((a.mbps + waves_per_wg * bpw - 1) / (waves_per_wg * bpw), a.num_seqs);
   dim3 block(waves_per_wg * kWave);
   if (a.idx_fmt == kIdxNvfp4) {
-    dim3 g2((a.mbps + kScanWaves - 1) / kScanWaves, a.num_seqs);
-    scan_decode_nvfp4_kernel<<<g2, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
+    dim3 g2((a.mbps + kNvfp4ScanWaves - 1) / kNvfp4ScanWaves, a.num_seqs);
+    scan_decode_nvfp4_kernel<<<g2, dim3(kNvfp4ScanWaves * kWave), 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
                                                        a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
                                                        a.idx_scale);
   } else if (a.idx_fmt == kIdxFp8)
