@@ -61,6 +61,15 @@ def _load():
         lib.msa_oracle_attend.restype = ctypes.c_int
         lib.msa_oracle_attend.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p]
+        lib.msa_oracle_e4m3_rne.restype = ctypes.c_uint8
+        lib.msa_oracle_e4m3_rne.argtypes = [ctypes.c_float]
+        lib.msa_oracle_e2m1_rne.restype = ctypes.c_uint8
+        lib.msa_oracle_e2m1_rne.argtypes = [ctypes.c_float]
+        lib.msa_oracle_quant_nvfp4_group.restype = None
+        lib.msa_oracle_quant_nvfp4_group.argtypes = [ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+        lib.msa_oracle_kv_insert.restype = ctypes.c_int
+        lib.msa_oracle_kv_insert.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p]
         lib.msa_oracle_decode.restype = ctypes.c_int
         lib.msa_oracle_decode.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
@@ -122,6 +131,16 @@ class Problem:
         _load().msa_oracle_attend(ctypes.byref(self._s), int(row), int(g), sel.ctypes.data, out.ctypes.data)
         return out
 
+    def kv_insert(self, k_new, v_new, idx_new):
+        """Quantises the new tokens of every query row into this problem's own
+        copies of the pools (self.arrays), in place.  k_new, v_new: bf16 bits
+        (uint16) [rows][Hkv][128]; idx_new: bf16 bits [rows][128]."""
+        def f32(bits):
+            return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+        kf, vf, xf = f32(k_new), f32(v_new), f32(idx_new)
+        assert kf.shape == (self.rows, self.num_kv_heads, 128) and xf.shape == (self.rows, 128)
+        _load().msa_oracle_kv_insert(ctypes.byref(self._s), kf.ctypes.data, vf.ctypes.data, xf.ctypes.data)
+
     def decode(self, row_begin: int = 0, row_end=None, nthreads: int = 0, want_scores: bool = True):
         """Whole path for rows [row_begin, row_end): (bs, sel, out)."""
         row_end = self.rows if row_end is None else int(row_end)
@@ -142,6 +161,24 @@ def select(bs, nbv: int):
     sel = np.empty(16, dtype=np.int32)
     _load().msa_oracle_select(bs.ctypes.data, int(nbv), sel.ctypes.data)
     return sel
+
+
+def e4m3_rne(y: float) -> int:
+    return int(_load().msa_oracle_e4m3_rne(float(y)))
+
+
+def e2m1_rne(y: float) -> int:
+    return int(_load().msa_oracle_e2m1_rne(float(y)))
+
+
+def quant_nvfp4_group(x16, gs: float):
+    """16 float32 values -> (8 packed bytes, scale byte)."""
+    x = np.ascontiguousarray(x16, dtype=np.float32)
+    assert x.shape == (16,)
+    packed = np.zeros(8, dtype=np.uint8)
+    sc = np.zeros(1, dtype=np.uint8)
+    _load().msa_oracle_quant_nvfp4_group(x.ctypes.data, float(gs), packed.ctypes.data, sc.ctypes.data)
+    return packed, int(sc[0])
 
 
 def e4m3(byte: int) -> float:

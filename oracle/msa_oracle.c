@@ -296,3 +296,131 @@ int msa_oracle_decode(const oracle_problem* p, int row_begin, int row_end, doubl
   }
   return 0;
 }
+
+/* ---- the write side: quantising new tokens into the paged pools -------- */
+
+/* The method keeps K/V in NVFP4 and the index cache in FP8 or NVFP4 ("What is
+ * new in M3.1" and "NVFP4 indexer DCP" of the vLLM MiniMax-M3.1-Flash post);
+ * the pages do not print the quantiser.  Reading taken (the generator's): per
+ * group of 16 elements x with tensor scale gs,
+ *   s = E4M3 nearest-even of amax|x| / (6 gs), at most 448;
+ *   code_i = E2M1 nearest-even of x_i / (s gs), saturating at +-6;
+ * a group with amax 0 or s == 0 stores scale 0 and codes 0; an E2M1 code that
+ * rounds to zero is +0, an E4M3 byte keeps the sign.  Every step is a
+ * single fp32 operation, in this order (6 * gs, amax / that, s * gs,
+ * x_i / that): an integer decision must come out the same on both sides, so
+ * the oracle takes it in the kernel's precision.  Rounding to nearest-even is
+ * done here by search over the format's values, in exact (double) arithmetic. */
+
+/* E4M3 byte of the value nearest to y (finite, |y| <= 448); ties to the code
+ * with an even mantissa; the sign is kept, also when the result is zero. */
+uint8_t msa_oracle_e4m3_rne(float y) {
+  double a = fabs((double)y);
+  int best = 0;
+  double bd = a;
+  for (int c = 1; c <= 0x7E; ++c) {
+    double d = fabs(msa_oracle_e4m3((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(signbit(y) ? (best | 0x80) : best);
+}
+
+/* E2M1 code of the value nearest to y, ties to the code with an even
+ * mantissa, |y| > 6 saturating to 6; -0 is not produced. */
+uint8_t msa_oracle_e2m1_rne(float y) {
+  double a = fabs((double)y);
+  int best = 0;
+  double bd = a;
+  for (int c = 1; c <= 7; ++c) {
+    double d = fabs(msa_oracle_e2m1((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)((y < 0 && best != 0) ? (best | 8) : best);
+}
+
+/* One NVFP4 group: 16 values -> 8 packed bytes (element 2k in the low nibble
+ * of byte k) and its E4M3 scale byte. */
+void msa_oracle_quant_nvfp4_group(const float* x, float gs, uint8_t* packed, uint8_t* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  uint8_t codes[16] = {0};
+  uint8_t s = 0;
+  if (amax > 0.0f) {
+    float denom = 6.0f * gs;
+    float t = amax / denom;
+    s = msa_oracle_e4m3_rne(fminf(t, 448.0f));
+  }
+  if (s != 0) {
+    float d = (float)msa_oracle_e4m3(s) * gs;
+    for (int i = 0; i < 16; ++i) codes[i] = msa_oracle_e2m1_rne(x[i] / d);
+  }
+  for (int k = 0; k < 8; ++k) packed[k] = (uint8_t)(codes[2 * k] | (codes[2 * k + 1] << 4));
+  *scale = s;
+}
+
+/* bf16 nearest-even of a float (finite). */
+static uint16_t or_bf16_rne(float f) {
+  uint32_t w;
+  memcpy(&w, &f, sizeof w);
+  uint32_t lsb = (w >> 16) & 1u;
+  w += 0x7FFFu + lsb;
+  return (uint16_t)(w >> 16);
+}
+
+/* Quantise the new tokens of every query row into the pools of p (whose
+ * pointers must then be writable host copies).  Row (b, i) sits at position
+ * seq_lens[b] - q_len + i, i.e. token row pos % 128 of page
+ * block_table[b][pos / 128]; padded rows (seq_lens[b] == 0) write nothing.
+ *   k_new, v_new float [rows][Hkv][128] (the bf16 inputs, exactly);
+ *   idx_new      float [rows][128].
+ * K / V: NVFP4 with tensor scales k_scale / v_scale, or bf16 of x / scale.
+ * Index keys: FP8 E4M3 nearest-even of x / idx_scale clamped to +-448, NVFP4
+ * with tensor scale idx_scale, or bf16 of x / idx_scale. */
+int msa_oracle_kv_insert(const oracle_problem* p, const float* k_new, const float* v_new, const float* idx_new) {
+  int rows = p->num_seqs * p->q_len, G = p->num_kv_heads;
+  for (int row = 0; row < rows; ++row) {
+    int b;
+    int64_t pos;
+    if (!row_geometry(p, row, &b, &pos)) continue;
+    int64_t page = p->block_table[(int64_t)b * p->max_blocks_per_seq + pos / OR_BLOCK];
+    int tok = (int)(pos % OR_BLOCK);
+    for (int which = 0; which < 2; ++which) {
+      const float* src = which ? v_new : k_new;
+      void* pool = (void*)(which ? p->v : p->k);
+      uint8_t* sf = (uint8_t*)(which ? p->v_sf : p->k_sf);
+      float gs = (float)(which ? p->v_scale : p->k_scale);
+      for (int h = 0; h < G; ++h) {
+        const float* x = src + ((int64_t)row * G + h) * OR_DIM;
+        int64_t r = (page * G + h) * OR_BLOCK + tok;
+        if (p->kv_nvfp4) {
+          for (int c = 0; c < OR_DIM / 16; ++c)
+            msa_oracle_quant_nvfp4_group(x + 16 * c, gs, (uint8_t*)pool + r * (OR_DIM / 2) + 8 * c, sf + r * (OR_DIM / 16) + c);
+        } else {
+          for (int d = 0; d < OR_DIM; ++d) ((uint16_t*)pool)[r * OR_DIM + d] = or_bf16_rne(x[d] / gs);
+        }
+      }
+    }
+    const float* x = idx_new + (int64_t)row * OR_DIM;
+    int64_t r = page * OR_BLOCK + tok;
+    float is = (float)p->idx_scale;
+    if (p->idx_fmt == 2) {
+      for (int c = 0; c < OR_DIM / 16; ++c)
+        msa_oracle_quant_nvfp4_group(x + 16 * c, is, (uint8_t*)p->idx_k + r * (OR_DIM / 2) + 8 * c,
+                                     (uint8_t*)p->idx_sf + r * (OR_DIM / 16) + c);
+    } else if (p->idx_fmt == 1) {
+      for (int d = 0; d < OR_DIM; ++d) {
+        float y = x[d] / is;
+        ((uint8_t*)p->idx_k)[r * OR_DIM + d] = msa_oracle_e4m3_rne(fmaxf(-448.0f, fminf(448.0f, y)));
+      }
+    } else {
+      for (int d = 0; d < OR_DIM; ++d) ((uint16_t*)p->idx_k)[r * OR_DIM + d] = or_bf16_rne(x[d] / is);
+    }
+  }
+  return 0;
+}

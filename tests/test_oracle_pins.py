@@ -412,3 +412,131 @@ def test_planted_blocks_selected_b8_32k():
     for b in range(8):
         for g in range(4):
             assert set(w.meta["planted"][(b, g)]) <= set(sel[b, g].tolist())
+
+
+# ---- the write side (KV insert quantiser) ---------------------------------
+
+def _e4m3_values():
+    return e4m3_t(np.arange(0x7F, dtype=np.uint8)).numpy()     # 0 .. 448, ascending
+
+
+def test_e4m3_rne_matches_torch_cast():
+    """E4M3 rounding of the insert against torch's float8_e4m3fn cast (a
+    library round-to-nearest-even, sign kept on zero): every midpoint between
+    neighbours (exact ties), the floats next to them, zero, subnormals, values
+    that round to zero and random values."""
+    v = _e4m3_values()
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (v[:-1] + v[1:]) / 2)   # the ties are exact in fp32
+    pts = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000)),
+                          v.astype(np.float32), np.random.default_rng(1).uniform(0, 448, 3000).astype(np.float32),
+                          np.float32([2.0 ** -10, 2.0 ** -11, 2.0 ** -12, 1e-7, 0.0])])
+    pts = np.concatenate([pts, -pts])
+    ref = torch.from_numpy(pts).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_rne(y) for y in pts], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e2m1_rne_brute_force_and_generator():
+    """E2M1 rounding: nearest magnitude by brute force (ties to the even code),
+    saturating at 6; and equal to the generator's torch quantiser."""
+    grid = E2M1_TABLE.numpy()[:8]
+    mids = (grid[:-1] + grid[1:]) / 2
+    rng = np.random.default_rng(2)
+    ys = np.concatenate([mids, grid, rng.uniform(-8, 8, 4000), [7.0, 100.0, 6.1, 5.9]]).astype(np.float32)
+    ys = np.concatenate([ys, -ys])
+    for y in ys:
+        a = abs(float(y))
+        d = np.abs(grid - a)
+        cand = np.flatnonzero(d == d.min())
+        code = int(cand[0]) if len(cand) == 1 else int([c for c in cand if c % 2 == 0][0])
+        if a > 6:
+            code = 7
+        want = code | (8 if (y < 0 and code) else 0)
+        assert oracle.e2m1_rne(y) == want, (y, oracle.e2m1_rne(y), want)
+    gen = synth.quant_e2m1_codes(torch.from_numpy(ys)).numpy()
+    assert np.array_equal(np.array([oracle.e2m1_rne(y) for y in ys], dtype=np.uint8), gen)
+
+
+def test_nvfp4_group_quantiser_matches_generator():
+    """Whole NVFP4 groups: with a power-of-two tensor scale the generator's
+    torch quantiser performs the same fp32 operations, so the two independent
+    implementations must store the same bytes; zero groups store scale 0."""
+    rng = np.random.default_rng(3)
+    for gs in (2.0 ** -9, 2.0 ** -3, 1.0):
+        x = (rng.standard_normal((40, 128)) * rng.uniform(0.01, 3.0, (40, 1))).astype(np.float32)
+        x[0, :16] = 0.0
+        x[1, 16:32] = 1e-6
+        packed, scales = synth.quant_nvfp4(torch.from_numpy(x), gs)
+        for r in range(40):
+            for c in range(8):
+                p8, s = oracle.quant_nvfp4_group(x[r, 16 * c:16 * c + 16], gs)
+                assert s == int(scales[r, c]), (gs, r, c)
+                assert np.array_equal(p8, packed[r, 8 * c:8 * c + 8].numpy()), (gs, r, c)
+        assert int(scales[0, 0]) == 0 and not packed[0, :8].any()
+
+
+def test_nvfp4_group_quantiser_round_trip():
+    """Values on the NVFP4 grid whose group holds a +-6 (so amax / (6 gs) is
+    the stored scale exactly) come back unchanged through quantise + decode."""
+    rng = np.random.default_rng(4)
+    grid = E2M1_TABLE.numpy()
+    for _ in range(200):
+        gs = 2.0 ** int(rng.integers(-10, 2))
+        codes = rng.integers(0, 16, 16)
+        codes[rng.integers(0, 16)] = 7 + 8 * int(rng.integers(0, 2))
+        s = int(rng.integers(0x08, 0x78))
+        x = (grid[codes] * oracle.e4m3(s) * gs).astype(np.float32)
+        p8, s_got = oracle.quant_nvfp4_group(x, gs)
+        assert s_got == s
+        back = np.array([oracle.e2m1((int(p8[k // 2]) >> (4 * (k & 1))) & 15) for k in range(16)]) * oracle.e4m3(s_got) * gs
+        assert np.array_equal(back, x.astype(np.float64))
+
+
+def test_kv_insert_writes_the_right_rows():
+    """The insert writes row (b, i) at position seq_lens[b] - q_len + i: token
+    row pos % 128 of page block_table[b][pos // 128] (located here with numpy),
+    as the generator's quantiser stores those values (power-of-two tensor
+    scales, where the two quantisers agree), and touches no other byte; a
+    padded sequence writes nothing."""
+    for idx_dtype in ("fp8", "nvfp4", "bf16"):
+        w = synth.make_workload(seq_lens=[300, 0, 128 * 3], q_len=3, idx_dtype=idx_dtype, layout="paged", seed=13,
+                                spare_pages=2)
+        w.k_scale, w.v_scale = 2.0 ** -6, 2.0 ** -5
+        w.idx_scale = 2.0 ** -4 if idx_dtype == "nvfp4" else 1.0
+        P = make_problem(w)
+        before = {k: None if v is None else v.copy() for k, v in P.arrays.items()}
+        rng = np.random.default_rng(5)
+        rows = w.rows
+        kf = torch.from_numpy(rng.standard_normal((rows, 4, 128)).astype(np.float32)).to(torch.bfloat16)
+        vf = torch.from_numpy(rng.standard_normal((rows, 4, 128)).astype(np.float32)).to(torch.bfloat16)
+        xf = torch.from_numpy(rng.standard_normal((rows, 128)).astype(np.float32)).to(torch.bfloat16)
+        bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+        P.kv_insert(bits(kf), bits(vf), bits(xf))
+        a = P.arrays
+        touched = {k: np.zeros(v.shape[:3] if k in ("k", "v", "k_sf", "v_sf") else v.shape[:2], bool)
+                   for k, v in a.items() if k in ("k", "v", "k_sf", "v_sf", "idx_k", "idx_sf") and v is not None}
+        for row in range(rows):
+            b, i = divmod(row, w.q_len)
+            L = int(a["seq_lens"][b])
+            if L == 0:
+                continue
+            pos = L - w.q_len + i
+            page, tok = int(a["block_table"][b, pos // 128]), pos % 128
+            for name, src, gs in (("k", kf, w.k_scale), ("v", vf, w.v_scale)):
+                packed, sc = synth.quant_nvfp4(src[row].float(), gs)
+                assert np.array_equal(a[name][page, :, tok], packed.numpy())
+                assert np.array_equal(a[name + "_sf"][page, :, tok], sc.numpy())
+                touched[name][page, :, tok] = touched[name + "_sf"][page, :, tok] = True
+            if idx_dtype == "nvfp4":
+                packed, sc = synth.quant_nvfp4(xf[row].float(), w.idx_scale)
+                assert np.array_equal(a["idx_k"][page, tok], packed.numpy())
+                assert np.array_equal(a["idx_sf"][page, tok], sc.numpy())
+                touched["idx_sf"][page, tok] = True
+            elif idx_dtype == "fp8":
+                assert np.array_equal(a["idx_k"][page, tok], synth.quant_e4m3(xf[row].float()).numpy())
+            else:
+                assert np.array_equal(a["idx_k"][page, tok], bits(xf[row]))
+            touched["idx_k"][page, tok] = True
+        for name, t in touched.items():
+            assert np.array_equal(a[name][~t], before[name][~t]), name
