@@ -217,6 +217,41 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   return hip_status(e, "selection + sparse attention");
 }
 
+msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const void* k_new, const void* v_new,
+                         const void* idx_new, hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(shape, cache, true, true)) != MSA_OK) return st;
+  if (!k_new || !v_new || !idx_new) return fail(MSA_ERR_INVALID_ARGUMENT, "k_new / v_new / idx_new is NULL");
+  const void* aligned16[] = {k_new, v_new, idx_new, cache->k, cache->v, cache->idx_k};
+  const char* names[] = {"k_new", "v_new", "idx_new", "k", "v", "idx_k"};
+  for (int i = 0; i < 6; ++i)
+    if ((st = check_aligned(aligned16[i], 16, names[i])) != MSA_OK) return st;
+  if (shape->num_seqs == 0) return ok();
+  msa::InsertArgs a;
+  // the pools are written: the cache's pointers are taken as writable
+  a.k = static_cast<uint8_t*>(const_cast<void*>(cache->k));
+  a.v = static_cast<uint8_t*>(const_cast<void*>(cache->v));
+  a.k_sf = const_cast<uint8_t*>(cache->k_sf);
+  a.v_sf = const_cast<uint8_t*>(cache->v_sf);
+  a.idx = static_cast<uint8_t*>(const_cast<void*>(cache->idx_k));
+  a.idx_sf = const_cast<uint8_t*>(cache->idx_sf);
+  a.block_table = cache->block_table;
+  a.seq_lens = cache->seq_lens;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.idx_new = static_cast<const uint16_t*>(idx_new);
+  a.rows = (int)rows_of(shape);
+  a.q_len = shape->q_len;
+  a.mbps = shape->max_blocks_per_seq;
+  a.k_scale = shape->k_scale;
+  a.v_scale = shape->v_scale;
+  a.idx_scale = shape->idx_scale;
+  a.kv_nvfp4 = shape->kv_dtype == MSA_KV_NVFP4;
+  a.idx_fmt = shape->idx_dtype == MSA_IDX_NVFP4 ? msa::kIdxNvfp4 : shape->idx_dtype == MSA_IDX_FP8_E4M3 ? msa::kIdxFp8 : msa::kIdxBf16;
+  return hip_status(msa::launch_kv_insert(a, stream), "kv insert");
+}
+
 const char* msa_status_string(msa_status status) {
   switch (status) {
     case MSA_OK: return "MSA_OK";

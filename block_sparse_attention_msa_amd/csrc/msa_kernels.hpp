@@ -65,6 +65,30 @@ struct AttnArgs {
 // Selection (fused path) + attention: one launch.
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
+// Write side: new tokens quantised into the paged pools (one launch).
+struct InsertArgs {
+  uint8_t* k;                  // NVFP4 [P][4][128][64] or bf16 [P][4][128][128]
+  uint8_t* v;
+  uint8_t* k_sf;               // NVFP4: [P][4][128][8]
+  uint8_t* v_sf;
+  uint8_t* idx;                // FP8 [P][128][128], bf16 [P][128][128] or NVFP4 [P][128][64]
+  uint8_t* idx_sf;             // NVFP4 index keys: [P][128][8]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const uint16_t* k_new;       // bf16 [rows][4][128]
+  const uint16_t* v_new;
+  const uint16_t* idx_new;     // bf16 [rows][128]
+  int rows;
+  int q_len;
+  int mbps;
+  float k_scale;
+  float v_scale;
+  float idx_scale;
+  bool kv_nvfp4;
+  int idx_fmt;                 // IdxFormat
+};
+hipError_t launch_kv_insert(const InsertArgs& a, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cus();
 

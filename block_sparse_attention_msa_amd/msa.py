@@ -20,7 +20,7 @@ MSA_KV_BF16, MSA_KV_NVFP4 = 0, 1
 MSA_IDX_BF16, MSA_IDX_FP8_E4M3, MSA_IDX_NVFP4 = 0, 1, 2
 _IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
-            "msa_sparse_attn_decode", "msa_decode", "msa_status_string", "msa_last_error")
+            "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_status_string", "msa_last_error")
 
 
 class MsaError(RuntimeError):
@@ -96,7 +96,8 @@ def lib():
         L.msa_block_topk.argtypes = [P(MsaShape), vp, vp, vp, vp]
         L.msa_sparse_attn_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        for f in ("msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode", "msa_decode"):
+        L.msa_kv_insert.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp]
+        for f in ("msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -156,6 +157,12 @@ def msa_decode(shape, cache, q, idx_q, out, sel_blocks, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().msa_decode(ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(idx_q), _ptr(out),
                             _ptr(sel_blocks), _ptr(workspace), nbytes, _stream(stream)), "msa_decode")
+
+
+def msa_kv_insert(shape, cache, k_new, v_new, idx_new, stream=None):
+    """Quantises the new tokens into the pools that `cache` points at (written)."""
+    _check(lib().msa_kv_insert(ctypes.byref(shape), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(idx_new),
+                               _stream(stream)), "msa_kv_insert")
 
 
 # ---- small conveniences over a synth.Workload (allocation via torch) -------

@@ -160,6 +160,26 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
 msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
                       int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The write side of a decode step ("Decode execution" of the M3 post: the
+ * step updates the cache before scoring; "What is new in M3.1": NVFP4 K/V,
+ * E2M1 values with one E4M3 scale per 16 elements and a tensor scale): the
+ * new tokens of every query row are quantised into the pools of `cache`,
+ * which are WRITTEN through its pointers.  Row (b, i) goes to position
+ * seq_lens[b] - q_len + i (seq_lens already counting the new tokens): token
+ * row pos % 128 of page block_table[b][pos / 128], which must be allocated.
+ * Padded rows (seq_lens[b] == 0) write nothing; nothing else is touched.
+ *   k_new, v_new bf16 [rows][num_kv_heads][128]; idx_new bf16 [rows][128].
+ * Quantiser, per group of 16 values x with tensor scale gs (k_scale, v_scale,
+ * idx_scale): s = E4M3 nearest-even of amax|x| / (6 gs) (at most 448),
+ * code_i = E2M1 nearest-even of x_i / (s gs) saturating at +-6 (zero as +0);
+ * amax 0 or s == 0 store scale 0 and codes 0.  Each step is one fp32
+ * operation in that order.  FP8 index keys: E4M3 nearest-even of
+ * x / idx_scale clamped to +-448, sign kept on zero.  bf16 pools: bf16
+ * nearest-even of x / scale.  Calls that write the same pages must be
+ * ordered; with msa_decode on the same stream the insert comes first. */
+msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const void* k_new, const void* v_new,
+                         const void* idx_new, hipStream_t stream);
+
 const char* msa_status_string(msa_status status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* msa_last_error(void);

@@ -102,6 +102,19 @@ def test_nvfp4_index_keys_validation():
     assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=4))) == 0
 
 
+def test_kv_insert_validation():
+    """msa_kv_insert validates like the other entry points, before any HIP call."""
+    L = msa.lib()
+    ins = lambda s, c=None, k=FAKE, v=FAKE, x=FAKE: L.msa_kv_insert(ctypes.byref(s), ctypes.byref(c or _cache()), k, v,
+                                                                     x, None)
+    assert ins(_shape(), k=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert ins(_shape(), x=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert ins(_shape(), k=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT          # misaligned
+    assert ins(_shape(), c=_cache(v_sf=None)) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert ins(_shape(num_kv_heads=2)) == msa.MSA_ERR_UNSUPPORTED
+    assert ins(_shape(num_seqs=0)) == msa.MSA_OK
+
+
 def test_workspace_size_and_too_small():
     L = msa.lib()
     s = _shape(num_seqs=32, max_blocks_per_seq=1024)

@@ -6,6 +6,7 @@ configuration the bench times and compared on sampled rows.  Rules (ids
 bit-exact except near ties, out within 2e-3 + 1e-2|ref|, block scores within
 the fp32 rounding bound) are in oracle/compare.py.
 """
+import math
 import sys
 
 import numpy as np
@@ -311,3 +312,50 @@ def test_deterministic(dev):
     b = run_all(w)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def _bits(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("kv,idx,q_len", [("nvfp4", "fp8", 1), ("nvfp4", "nvfp4", 1), ("bf16", "bf16", 1),
+                                          ("nvfp4", "bf16", 3), ("nvfp4", "fp8", 3), ("bf16", "fp8", 3)])
+def test_kv_insert_matches_oracle(dev, kv, idx, q_len):
+    """msa_kv_insert writes exactly the oracle's bytes (every pool, bit for
+    bit: the quantiser's integer decisions are taken in the same fp32 steps),
+    touches nothing else, and the decode over the updated cache matches the
+    oracle.  New tokens mix magnitudes from 1e-3 to 30, an all-zero group, a
+    group of tiny values, E4M3 ties (x = midpoints) in the index keys and
+    negative values that round to zero; a padded sequence writes nothing."""
+    msa = _msa()
+    lens = [300, 0, 128 * 3, 5000 + q_len]
+    w = synth.make_workload(seq_lens=lens, q_len=q_len, kv_dtype=kv, idx_dtype=idx, plant=2, layout="paged",
+                            seed=50 + q_len, spare_pages=3, device=dev)
+    P = oracle.Problem.from_workload(w)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    rows = w.rows
+    mag = torch.exp(torch.empty(rows, 1, 1).uniform_(math.log(1e-3), math.log(30.0), generator=g))
+    k_new = (torch.randn(rows, 4, 128, generator=g) * mag).to(torch.bfloat16)
+    v_new = (torch.randn(rows, 4, 128, generator=g) * mag).to(torch.bfloat16)
+    x_new = torch.randn(rows, 128, generator=g).to(torch.bfloat16)
+    k_new[0, 0, :16] = 0.0                                    # zero group
+    v_new[0, 1, 16:32] = 1e-30                                # tiny group
+    k_new[0, 2, 32:48] = torch.tensor([6.0] + [-5.0] * 15)    # saturating codes after scale rounding
+    x_new[0, :8] = torch.tensor([1.0625, -1.0625, 0.5625, 3.25, -0.0001, 2.0 ** -10, 1.5 * 2 ** -8, 448.0])
+    if x_new.shape[0] > 1:
+        x_new[-1, :4] = torch.tensor([1000.0, -1000.0, 0.0, -0.0])   # clamped to +-448 in FP8
+    before = {k: getattr(w, k).clone() for k in ("k", "v", "k_sf", "v_sf", "idx_k", "idx_sf") if getattr(w, k) is not None}
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    msa.msa_kv_insert(shape, cache, k_new.to(dev), v_new.to(dev), x_new.to(dev))
+    torch.cuda.synchronize()
+    P.kv_insert(_bits(k_new), _bits(v_new), _bits(x_new))
+    h = w.host_arrays()
+    changed = 0
+    for name in before:
+        got, want = h[name], P.arrays[name]
+        assert np.array_equal(got, want), f"{name}: {np.count_nonzero(got != want)} bytes differ"
+        old = before[name]
+        old = _bits(old) if old.dtype == torch.bfloat16 else old.cpu().numpy()
+        changed += int(np.count_nonzero(got != old))
+    assert changed > 0
+    check_workload(w, label=f"decode after insert {kv}/{idx} q_len={q_len}")
