@@ -265,6 +265,24 @@ def main():
     torch.cuda.synchronize()
     scan_us = e0.elapsed_time(e1) / args.steps * 1e3
 
+    # the write side of the step, timed apart: the new tokens' K/V/index keys
+    # quantised into the pools (msa_kv_insert; not part of `value`)
+    insert_us = None
+    if w.idx_dtype != "nvfp4" or w.q_len == 1:
+        gi = torch.Generator(device=dev).manual_seed(11)
+        k_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
+        v_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
+        x_new = torch.randn(w.rows, 128, generator=gi, device=dev).to(torch.bfloat16)
+        for i in range(args.warmup):
+            msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        insert_us = e0.elapsed_time(e1) / args.steps * 1e3
+
     nb = w.nbytes_algorithmic()
     step_gbps = nb["total"] / (us_step * 1e-6) / 1e9
     sb = scan_bytes(w)
@@ -272,7 +290,8 @@ def main():
     ctx_tokens = int(w.seq_lens.sum())
     per_tok = nb["total"] / ctx_tokens
     log(f"[bench] step {us_step:.1f} us ({step_gbps:.0f} GB/s algorithmic, {nb['total'] / 1e6:.1f} MB), "
-        f"scan {scan_us:.1f} us ({scan_gbps:.0f} GB/s, {sb / 1e6:.1f} MB), host wall {wall / args.steps * 1e6:.1f} us")
+        f"scan {scan_us:.1f} us ({scan_gbps:.0f} GB/s, {sb / 1e6:.1f} MB), host wall {wall / args.steps * 1e6:.1f} us"
+        + ("" if insert_us is None else f", kv insert {insert_us:.1f} us"))
 
     if w.q_len == 1:
         roofline = {"bound": "hbm", "kernel": "index scan + block max-pool", "achieved": round(scan_gbps, 1),
@@ -317,6 +336,7 @@ def main():
         "vs_dense_fp8_kv_per_token": round(per_tok / 1024.0, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "kv_insert_us": None if insert_us is None else round(insert_us, 2),
     }
     print(json.dumps(rec), flush=True)
 
