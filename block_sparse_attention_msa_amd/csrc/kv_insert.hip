@@ -4,8 +4,10 @@
 // Method ("What is new in M3.1" and "NVFP4 indexer DCP" of the vLLM
 // MiniMax-M3.1-Flash post: the KV cache in NVFP4, E2M1 values with one E4M3
 // scale per 16 elements and a tensor scale; the index cache in FP8 or NVFP4;
-// "Decode execution" of the MiniMax M3 x vLLM post: each step updates the
-// cache state before scoring).  The pages do not print the quantiser; the one
+// "QKV GEMM + Norm + RoPE + KV-insert fusion" there: K, V and the index key
+// quantised to NVFP4 and written straight into their caches; "Decode
+// execution" of the MiniMax M3 x vLLM post: each step updates the cache
+// state before scoring).  The pages do not print the quantiser; the one
 // here, per group of 16 values x with tensor scale gs:
 //   s = E4M3 nearest-even of amax|x| / (6 gs) (at most 448);
 //   code_i = E2M1 nearest-even of x_i / (s gs), saturating at +-6;
