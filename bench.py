@@ -16,6 +16,7 @@ import argparse
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -146,7 +147,7 @@ def write_traffic(config: str, fetch_dir: str, write_dir: str):
     traffic record of the config's scan: each counter is scaled by what it
     read for the plain copy of COPY_BYTES in the same runs."""
     fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
-    scan = [k for k in fetch if "scan_decode" in k]
+    scan = [k for k in fetch if re.search(r"scan_(decode|cols)", k)]
     if len(scan) != 1:
         raise SystemExit(f"expected one scan kernel in {fetch_dir}, found {scan}")
     scan = scan[0]
@@ -157,8 +158,7 @@ def write_traffic(config: str, fetch_dir: str, write_dir: str):
     copy = copy[0]
     fs, ws = COPY_BYTES / (fetch[copy][0] * 1024.0), COPY_BYTES / (write[copy][0] * 1024.0)
     fb, wb = fetch[scan][0] * 1024.0 * fs, write[scan][0] * 1024.0 * ws
-    import re
-    rec = {"kernel": re.search(r"scan_decode\w*(?:<[^>]*>)?", scan).group(0), "workload": config, "source_sha256": scan_source_hash(),
+    rec = {"kernel": re.search(r"scan_(?:decode|cols)\w*(?:<[^>]*>)?", scan).group(0), "workload": config, "source_sha256": scan_source_hash(),
            "fetch_kib_per_dispatch_raw": fetch[scan][0], "write_kib_per_dispatch_raw": write[scan][0],
            "copy_fetch_kib_raw": fetch[copy][0], "copy_write_kib_raw": write[copy][0], "copy_bytes": COPY_BYTES,
            "fetch_scale": fs, "write_scale": ws, "fetch_bytes": fb, "write_bytes": wb,
@@ -283,7 +283,7 @@ def main():
         torch.cuda.synchronize()
         insert_us = e0.elapsed_time(e1) / args.steps * 1e3
 
-    nb = w.nbytes_algorithmic()
+    nb = w.nbytes_algorithmic(sel if w.q_len > 1 else None)
     step_gbps = nb["total"] / (us_step * 1e-6) / 1e9
     sb = scan_bytes(w)
     scan_gbps = sb / (scan_us * 1e-6) / 1e9
@@ -293,19 +293,33 @@ def main():
         f"scan {scan_us:.1f} us ({scan_gbps:.0f} GB/s, {sb / 1e6:.1f} MB), host wall {wall / args.steps * 1e6:.1f} us"
         + ("" if insert_us is None else f", kv insert {insert_us:.1f} us"))
 
+    # The bound is the one that gives the longer ideal time: the decode scan and
+    # short multi-query batches (a few rows per sequence) stream the keys with
+    # little arithmetic per byte; long ones are a dense contraction.
+    fl = scan_flops(w) if w.q_len > 1 else 0.0
+    mfma_bound = fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > sb / (HBM_PEAK_GBPS * 1e9)
     if w.q_len == 1:
-        roofline = {"bound": "hbm", "kernel": "index scan + block max-pool", "achieved": round(scan_gbps, 1),
+        kname = {"fp8": "index scan + block max-pool (FP8 keys, bf16 MFMA)",
+                 "nvfp4": "index scan + block max-pool (NVFP4 keys, bf16 MFMA)",
+                 "bf16": "index scan + block max-pool (bf16 keys, VALU dot2)"}[w.idx_dtype]
+    elif w.idx_dtype == "fp8" and w.q_len <= 8:
+        kname = f"index scan + causal block max-pool, {4 * w.q_len} (query, group) columns per sequence (bf16 MFMA)"
+    else:
+        kname = "multi-query index scan + causal block max-pool (bf16 MFMA)"
+    if not mfma_bound:
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(scan_gbps, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
                     "traffic": scan_traffic(args.config),
                     "launch_us": round(scan_us, 2), "algorithmic_bytes": int(sb)}
-    else:  # the multi-query scan is a dense contraction on the matrix cores
-        fl = scan_flops(w)
+    else:
         tflops = fl / (scan_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": "multi-query index scan + causal block max-pool (bf16 MFMA)",
+        roofline = {"bound": "mfma", "kernel": kname,
                     "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                     "launch_us": round(scan_us, 2), "algorithmic_flops": int(fl)}
-        log(f"[bench] multi-query scan {fl / 1e9:.1f} GFLOP, {tflops:.0f} TFLOP/s")
+    if fl:
+        log(f"[bench] multi-query scan {fl / 1e9:.1f} GFLOP, {fl / (scan_us * 1e-6) / 1e12:.0f} TFLOP/s, "
+            f"{'mfma' if mfma_bound else 'hbm'}-bound")
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()

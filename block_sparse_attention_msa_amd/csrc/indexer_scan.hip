@@ -58,13 +58,59 @@ __global__ __launch_bounds__(kNvfp4ScanWaves * kWave, 6) void scan_decode_nvfp4_
                   block_scores + (size_t)b * kGroups * mbps, mbps, j, j + 1, idx_scale, lds_sc[wave], lane);
 }
 
+// FP8 index keys, q_len <= 8: 16 x NT (query, group) columns per sequence on
+// MFMA, pages_per_wave consecutive pages per wave (the B operands are loaded
+// once per wave).
+constexpr int kColsScanWaves = 8;
+template <int NT>
+__global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_kernel(const uint8_t* __restrict__ idx_pool,
+                                                                         const int32_t* __restrict__ block_table,
+                                                                         const int32_t* __restrict__ seq_lens,
+                                                                         const uint16_t* __restrict__ iq,
+                                                                         float* __restrict__ block_scores, int q_len,
+                                                                         int mbps, int pages_per_wave, float idx_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t[kColsScanWaves][2 * 2048];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int jbeg = (blockIdx.x * kColsScanWaves + wave) * pages_per_wave;
+  if (jbeg >= mbps) return;
+  const int jend = min(jbeg + pages_per_wave, mbps);
+  const size_t ncols = (size_t)q_len * kGroups;
+  scan_wave_fp8_mfma<NT>(idx_pool, block_table + (size_t)b * mbps, seq_lens[b], q_len, iq + b * ncols * kDim,
+                         block_scores + b * ncols * mbps, mbps, jbeg, jend, idx_scale, lds_t[wave], lane);
+}
+
 }  // namespace
 
+hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
+  if (q_len < 1 || q_len > 8 || a.idx_fmt != kIdxFp8) return hipErrorInvalidValue;
+  // 8-wave workgroups at 4 waves per SIMD; from a sweep on the batch-32 x 128K
+  // shape: q_len 1 80.6 us with one page per wave (81.3-81.8 us with 2 or 4),
+  // q_len 4 88 us with two (91.5 us with one, 88 us with four); 4- and 16-wave
+  // workgroups 1-10 % slower, 5 waves per SIMD (at most 102 VGPRs) 11-13 %.
+  const int ppw = q_len == 1 ? 1 : 2;
+  const int per_wg = kColsScanWaves * ppw;
+  dim3 grid((a.mbps + per_wg - 1) / per_wg, a.num_seqs);
+  dim3 block(kColsScanWaves * kWave);
+  const uint8_t* pool = static_cast<const uint8_t*>(a.idx_pool);
+  if (q_len <= 4)
+    scan_cols_kernel<1><<<grid, block, 0, stream>>>(pool, a.block_table, a.seq_lens, a.iq, a.block_scores, q_len,
+                                                     a.mbps, ppw, a.idx_scale);
+  else
+    scan_cols_kernel<2><<<grid, block, 0, stream>>>(pool, a.block_table, a.seq_lens, a.iq, a.block_scores, q_len,
+                                                     a.mbps, ppw, a.idx_scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
-  // 8-wave workgroups, one page per wave: measured best on the batch-32 x
-  // 128K workload with 5 waves per SIMD (81.4-84.2 us vs 82.2-83.3 us for 2 or
-  // 4 pages per wave, 82.8-85.7 us at 4 waves per SIMD, 84.0-85.1 us for 2- or
-  // 4-wave workgroups and 116 us at 6 waves per SIMD).
+  // FP8 index keys: the MFMA column scan (80.6 us on the batch-32 x 128K
+  // shape against 82-85 us for the VALU scan below with FP8 keys).
+  if (a.idx_fmt == kIdxFp8) return launch_scan_cols(a, 1, stream);
+  // bf16 index keys: the VALU scan, 8-wave workgroups, one page per wave (with
+  // FP8 keys on the batch-32 x 128K workload: 81.4-84.2 us at 5 waves per
+  // SIMD vs 82.2-83.3 us for 2 or 4 pages per wave, 82.8-85.7 us at 4 waves
+  // per SIMD, 84.0-85.1 us for 2- or 4-wave workgroups, 116 us at 6 per SIMD).
   const int bpw = 1;
   constexpr int waves_per_wg = kScanWaves;
   dim3 grid((a.mbps + waves_per_wg * bpw - 1) / (waves_per_wg * bpw), a.num_seqs);
@@ -74,10 +120,7 @@ hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
     scan_decode_nvfp4_kernel<<<g2, dim3(kNvfp4ScanWaves * kWave), 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
                                                        a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
                                                        a.idx_scale);
-  } else if (a.idx_fmt == kIdxFp8)
-    scan_decode_kernel<true><<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                          a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale);
-  else
+  } else
     scan_decode_kernel<false><<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
                                                            a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale);
   return hipGetLastError();

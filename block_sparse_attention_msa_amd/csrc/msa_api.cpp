@@ -124,9 +124,13 @@ msa::ScanArgs scan_args(const msa_shape* s, const msa_cache* c, const void* idx_
   return a;
 }
 
-// q_len == 1: the VALU decode scan; q_len > 1: the MFMA multi-query scan.
+// q_len == 1: the decode scan; FP8 index keys with q_len <= 8: pages streamed
+// by waves with the few (query, group) columns on MFMA; otherwise the
+// multi-query scan (query rows staged in LDS, keys streamed per row chunk).
 hipError_t launch_scan(const msa_shape* s, const msa::ScanArgs& a, hipStream_t stream) {
-  return s->q_len == 1 ? msa::launch_scan_decode(a, stream) : msa::launch_scan_mq(a, s->q_len, stream);
+  if (s->q_len == 1) return msa::launch_scan_decode(a, stream);
+  if (a.idx_fmt == msa::kIdxFp8 && s->q_len <= 8) return msa::launch_scan_cols(a, s->q_len, stream);
+  return msa::launch_scan_mq(a, s->q_len, stream);
 }
 
 msa_status check_aligned(const void* p, size_t a, const char* what) {

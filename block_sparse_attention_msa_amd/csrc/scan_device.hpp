@@ -210,3 +210,123 @@ __device__ __forceinline__ void scan_wave_nvfp4(const uint8_t* __restrict__ code
 }
 
 }  // namespace msa
+
+namespace msa {
+
+// FP8 index keys, short multi-query batches: block scores of blocks
+// [jbeg, jend) of one sequence for its q_len x 4 (query, group) columns,
+// 16 x NT of them at most, one wave per block.
+//
+// The dense form of the scan, S[t][col] = sum_d ik[t][d] * iq[col][d], on
+// v_mfma_f32_16x16x32_bf16: A = 16 tokens (E4M3 -> bf16, exact), B = 16
+// columns, column col = 4 i + g of the sequence (query i, group g) exactly as
+// the block-score rows are laid out.
+//  * The page streams in as 16 contiguous 1 KB wave-loads (lane l: token
+//    8i + l/8, 16-B chunk l%8), all issued before use, as in the decode scan.
+//  * Per 16-token tile the wave moves its 2 KB through LDS into the MFMA
+//    layout: chunk k of tile token t is stored at t*128 + 16 (k ^ (t % 8)), so
+//    both the row writes and the column reads touch 8 distinct 16-B slots per
+//    8 lanes (conflict-free).  Lane (c, n) = (lane / 16, lane % 16) reads
+//    chunks 4h + c of token n (h = 0, 1): MFMA step s = 2h + u takes dims
+//    64h + 16c + 8u + e at K index 8c + e, for A and B alike.
+//  * The result holds tokens 4c + i of column n: a running max per lane with
+//    the causal limit of the lane's column (query i sees tokens at or before
+//    position seq_len - q_len + i), then 2 cross-lane steps per block.
+// Products are exact in fp32, sums fp32 (the MFMA's accumulation).
+template <int NT>
+__device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ idx_pool,
+                                                   const int32_t* __restrict__ bt_row, int L, int q_len,
+                                                   const uint16_t* __restrict__ iq_seq, float* __restrict__ bs_seq,
+                                                   int mbps, int jbeg, int jend, float idx_scale, uint8_t* lds,
+                                                   int lane) {
+  const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int ncols = q_len * kGroups;
+  const int pos0 = L - q_len;  // position of query 0
+  // LDS offsets of this lane's tile writes (token 8hh + lane/8, chunk lane%8)
+  // and column reads (token n, chunk 4h + c)
+  const int wr = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+  const int rd0 = n * 128 + ((c ^ (n & 7)) << 4);
+  const int rd1 = n * 128 + (((4 + c) ^ (n & 7)) << 4);
+
+  // B operands: column 16t + n, dims 64h + 16c + 8u for step s = 2h + u
+  bf16x8 qb[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + n;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int d = 64 * (s >> 1) + 16 * c + 8 * (s & 1);
+      const uint4 w = col < ncols ? *reinterpret_cast<const uint4*>(iq_seq + (size_t)col * kDim + d)
+                                  : make_uint4(0, 0, 0, 0);
+      qb[t][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  for (int j = jbeg; j < jend; ++j) {
+    if (j >= nbv) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = -INFINITY;
+      continue;
+    }
+    const int64_t page = bt_row[j];
+    const uint8_t* base = idx_pool + page * (kBlock * kDim) + lane * 16;
+    u32x4 kv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 1024 * i));
+    // every column sees the whole block: no mask (wave-uniform)
+    const bool full = (j + 1) * kBlock - 1 <= pos0;
+    int vis[NT];  // tokens of the block visible to this lane's column
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vis[t] = pos0 + (16 * t + n) / kGroups + 1 - j * kBlock;
+    float m[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m[t] = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      uint8_t* buf = lds + (T & 1) * 2048;
+      *reinterpret_cast<u32x4*>(buf + wr) = kv[2 * T];
+      *reinterpret_cast<u32x4*>(buf + 1024 + wr) = kv[2 * T + 1];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const u32x4 r[2] = {*reinterpret_cast<const u32x4*>(buf + rd0), *reinterpret_cast<const u32x4*>(buf + rd1)};
+      bf16x8 ka[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t d[4] = {r[h].x, r[h].y, r[h].z, r[h].w};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x2 p0 = e4m3x2_to_bf16x2<false>(d[2 * u]);
+          const bf16x2 p1 = e4m3x2_to_bf16x2<true>(d[2 * u]);
+          const bf16x2 p2 = e4m3x2_to_bf16x2<false>(d[2 * u + 1]);
+          const bf16x2 p3 = e4m3x2_to_bf16x2<true>(d[2 * u + 1]);
+          ka[2 * h + u] = bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[t][s], acc, 0, 0, 0);
+        if (full) {
+          m[t] = fmaxf(m[t], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[t] = fmaxf(m[t], 16 * T + 4 * c + i < vis[t] ? acc[i] : -INFINITY);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float x = fmaxf(m[t], __shfl_xor(m[t], 16));
+      x = fmaxf(x, __shfl_xor(x, 32));
+      if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = x * idx_scale;
+    }
+    __builtin_amdgcn_wave_barrier();  // the next block rewrites this wave's tiles
+  }
+}
+
+}  // namespace msa

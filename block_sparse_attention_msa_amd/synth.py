@@ -135,22 +135,31 @@ class Workload:
                     block_table=self.block_table.cpu().numpy().astype(np.int32),
                     seq_lens=self.seq_lens.cpu().numpy().astype(np.int32))
 
-    def nbytes_algorithmic(self) -> dict:
-        """Bytes the method must move per layer-step (decode, q_len == 1):
-        every visible token's index key, K+V of the selected tokens only,
-        the used block-table entries, q, iq and the fp32 output."""
+    def nbytes_algorithmic(self, sel=None) -> dict:
+        """Bytes the method must move per layer-step: every visible token's
+        index key, K+V of the selected tokens only, the used block-table
+        entries, q, iq and the fp32 output.  K/V is counted once per (sequence,
+        group, selected block): with q_len > 1 the union of the rows' selections
+        (needs the step's `sel` [rows][groups][16]); without `sel`, 16 blocks
+        per group (exact for q_len 1)."""
         lens = [int(x) for x in self.seq_lens.cpu().tolist()]
         b_idx = IDX_BYTES_PER_TOKEN[self.idx_dtype]
         b_kv_tok = DIM * (0.5 + 1.0 / 16) if self.kv_dtype == "nvfp4" else DIM * 2.0
         scan = sum(lens) * b_idx
         gather = 0.0
         table = 0
-        for L in lens:
+        if sel is not None:
+            sel = sel.cpu().reshape(self.num_seqs, self.q_len, self.num_kv_heads, 16)
+        for b, L in enumerate(lens):
             if L <= 0:
                 continue
             nb = (L - 1) // BLOCK + 1
-            kept = min(nb, 16)
-            gather += self.num_kv_heads * kept * BLOCK * b_kv_tok * 2   # K and V
+            if sel is None:
+                kept = self.num_kv_heads * min(nb, 16)
+            else:
+                kept = sum(int(torch.unique(sel[b, :, g][sel[b, :, g] >= 0]).numel())
+                           for g in range(self.num_kv_heads))
+            gather += kept * BLOCK * b_kv_tok * 2   # K and V
             table += nb * 4
         qio = self.rows * (self.num_q_heads + self.num_kv_heads) * DIM * 2
         out = self.rows * self.num_q_heads * DIM * 4
@@ -337,6 +346,10 @@ CONFIGS = {
     # batch 2 x 256 new query tokens appended causally to a 128K paged context
     "verify_b2_q256_128k": dict(seq_lens=[131072 + 256] * 2, q_len=256, zipf=1.1, layout="paged",
                                 shared_bias_iq=True, seed=4),
+    # speculative verify on the decode path: batch 32, each sequence a 128K
+    # context plus 4 new query tokens (1 + 3 draft tokens, the draft length of
+    # the AMD serving recipe); not one of the five above
+    "spec_b32_q4_128k": dict(seq_lens=[131072 + 4] * 32, q_len=4, zipf=1.1, layout="paged", seed=5),
     # the batch-32 x 128K shape with the index cache in NVFP4 (72 B per token
     # instead of 128 B), the M3.1 production setting; not one of the five above
     "paged_b32_128k_nvfp4_idx": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", idx_dtype="nvfp4",

@@ -236,19 +236,29 @@ def test_paged_permutation_invariance(dev):
 
 
 @pytest.mark.parametrize("kv,idx", [("nvfp4", "fp8"), ("bf16", "bf16")])
-@pytest.mark.parametrize("q_len", [2, 5, 9, 64, 80])
+@pytest.mark.parametrize("q_len", [2, 4, 5, 8, 9, 64, 80])
 def test_multi_query_causal(dev, kv, idx, q_len):
     """q_len > 1 (speculative verify / prefill chunk): every query row has its
     own causal position, block scores, selection and attention; the scan runs
     on MFMA.  Ragged lengths, a sequence made only of the new tokens (its first
     query sees one key), a padded row, rows that do not fill an MFMA tile, and
-    (q_len 80: 320 rows) a partial second 256-row chunk of the scan."""
+    (q_len 80: 320 rows) a partial second 256-row chunk of the scan.  FP8 index
+    keys with q_len <= 8 take the column scan: q_len 2 and 4 one 16-column
+    tile (half and fully used), 5 and 8 two."""
     lens = [q_len, q_len + 1, 127 + q_len, 2177, 0, 16 * 128 + q_len, 5000]
     w = synth.make_workload(seq_lens=lens, q_len=q_len, kv_dtype=kv, idx_dtype=idx, plant=3, layout="paged",
                             seed=30 + q_len, device=dev, max_blocks_per_seq=48)
     out, sel, bs = check_workload(w, label=f"multi-query q_len={q_len} {kv}/{idx}")
     pad = 4 * q_len
     assert (out[pad:pad + q_len] == 0).all() and (sel[pad:pad + q_len] == -1).all()
+
+
+def test_spec_b32_q4_128k_config_sampled(dev):
+    """Speculative verify on the decode path: batch 32 x (128K + 4) with 4 query
+    tokens each, in the bench's launch configuration; sampled rows cover the
+    first and last query of a sequence and different sequences."""
+    w = synth.make_config("spec_b32_q4_128k", device=dev)
+    check_workload(w, rows=[0, 3, 4 * 13 + 1, 4 * 31 + 2, 4 * 31 + 3])
 
 
 def test_verify_b2_q256_128k_config_sampled(dev):
