@@ -268,7 +268,7 @@ def main():
     # the write side of the step, timed apart: the new tokens' K/V/index keys
     # quantised into the pools (msa_kv_insert; not part of `value`)
     insert_us = None
-    if w.idx_dtype != "nvfp4" or w.q_len == 1:
+    if w.idx_dtype != "nvfp4" or w.q_len <= 8:
         gi = torch.Generator(device=dev).manual_seed(11)
         k_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
         v_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
@@ -302,8 +302,9 @@ def main():
         kname = {"fp8": "index scan + block max-pool (FP8 keys, bf16 MFMA)",
                  "nvfp4": "index scan + block max-pool (NVFP4 keys, bf16 MFMA)",
                  "bf16": "index scan + block max-pool (bf16 keys, VALU dot2)"}[w.idx_dtype]
-    elif w.idx_dtype == "fp8" and w.q_len <= 8:
-        kname = f"index scan + causal block max-pool, {4 * w.q_len} (query, group) columns per sequence (bf16 MFMA)"
+    elif w.idx_dtype in ("fp8", "nvfp4") and w.q_len <= 8:
+        kname = (f"index scan + causal block max-pool ({w.idx_dtype.upper()} keys), {4 * w.q_len} (query, group) "
+                 f"columns per sequence (bf16 MFMA)")
     else:
         kname = "multi-query index scan + causal block max-pool (bf16 MFMA)"
     if not mfma_bound:

@@ -81,10 +81,30 @@ __global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_kernel(const
                          block_scores + b * ncols * mbps, mbps, jbeg, jend, idx_scale, lds_t[wave], lane);
 }
 
+// NVFP4 index keys, 2 <= q_len <= 8: the same columns, keys dequantised
+// exactly to bf16 in registers (no LDS).
+template <int NT>
+__global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_nvfp4_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int q_len,
+    int mbps, int pages_per_wave, float idx_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kColsScanWaves][kBlock * 8];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int jbeg = (blockIdx.x * kColsScanWaves + wave) * pages_per_wave;
+  if (jbeg >= mbps) return;
+  const int jend = min(jbeg + pages_per_wave, mbps);
+  const size_t ncols = (size_t)q_len * kGroups;
+  scan_wave_nvfp4_cols<NT>(codes, scales, block_table + (size_t)b * mbps, seq_lens[b], q_len, iq + b * ncols * kDim,
+                           block_scores + b * ncols * mbps, mbps, jbeg, jend, idx_scale, lds_sc[wave], lane);
+}
+
 }  // namespace
 
 hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
-  if (q_len < 1 || q_len > 8 || a.idx_fmt != kIdxFp8) return hipErrorInvalidValue;
+  if (q_len < 1 || q_len > 8 || a.idx_fmt == kIdxBf16 || (a.idx_fmt == kIdxNvfp4 && q_len < 2))
+    return hipErrorInvalidValue;
   // 8-wave workgroups at 4 waves per SIMD; from a sweep on the batch-32 x 128K
   // shape: q_len 1 80.6 us with one page per wave (81.3-81.8 us with 2 or 4),
   // q_len 4 88 us with two (91.5 us with one, 88 us with four); 4- and 16-wave
@@ -94,6 +114,15 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
   dim3 grid((a.mbps + per_wg - 1) / per_wg, a.num_seqs);
   dim3 block(kColsScanWaves * kWave);
   const uint8_t* pool = static_cast<const uint8_t*>(a.idx_pool);
+  if (a.idx_fmt == kIdxNvfp4) {
+    if (q_len <= 4)
+      scan_cols_nvfp4_kernel<1><<<grid, block, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
+                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale);
+    else
+      scan_cols_nvfp4_kernel<2><<<grid, block, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
+                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale);
+    return hipGetLastError();
+  }
   if (q_len <= 4)
     scan_cols_kernel<1><<<grid, block, 0, stream>>>(pool, a.block_table, a.seq_lens, a.iq, a.block_scores, q_len,
                                                      a.mbps, ppw, a.idx_scale);

@@ -32,7 +32,8 @@ struct ScanArgs {
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream);
 // Multi-query (q_len > 1) index scores + causal block max-pool on MFMA.
 hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream);
-// FP8 index keys, 1 <= q_len <= 8: the (query, group) columns on MFMA, pages streamed by waves.
+// FP8 index keys with 1 <= q_len <= 8, NVFP4 with 2 <= q_len <= 8: the (query, group) columns on
+// MFMA, pages streamed by waves.
 hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream);
 
 struct TopkArgs {

@@ -108,6 +108,8 @@ namespace msa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // NVFP4 index keys (E2M1 codes [P][128][64] + E4M3 scales [P][128][8]): block
 // scores of blocks [jbeg, jend) of one sequence, one wave per block.
@@ -326,6 +328,148 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
       if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = x * idx_scale;
     }
     __builtin_amdgcn_wave_barrier();  // the next block rewrites this wave's tiles
+  }
+}
+
+}  // namespace msa
+
+namespace msa {
+
+// NVFP4 index keys, short multi-query batches (2 <= q_len <= 8): block scores
+// of blocks [jbeg, jend) of one sequence for its q_len x 4 (query, group)
+// columns, 16 x NT of them at most, one wave per block.
+//
+// The score contraction runs in f16 on v_mfma_f32_16x16x32_f16 (NVFP4 keys
+// converted straight to FP16 for the indexer's score MMA: "NVIDIA
+// Rubin-optimised MSA" of the vLLM MiniMax-M3.1-Flash post):
+//  * keys: an E2M1 code times its 16-dim group's E4M3 scale has at most 6
+//    significant bits within [2^-10, 2688], so the f16 key is exact: one
+//    conversion and one packed f16 multiply per pair of values;
+//  * queries: each column is scaled by a power of two 2^k so that its largest
+//    |iq| lies in [2^14, 2^15) and converted to f16 (nearest-even).  Every
+//    element within 2^-28 of the column's largest is exact; smaller ones
+//    round to f16 subnormals (absolute error at most 2^-25 x 2^-k).  The
+//    block maximum is multiplied back by 2^-k (exact);
+//  * products are exact in fp32, sums fp32.
+// With 64 B of codes per token one 16-B load per lane holds 16 whole tokens,
+// so lane (c, n) = (lane / 16, lane % 16) loads token n's dims 32c .. 32c + 31
+// (scale groups 2c, 2c + 1) in contiguous 1 KB wave-loads with no transpose;
+// MFMA step s takes dims 32c + 8s + e at K index 8c + e, for A and B alike.
+// The page's 1 KB of scales arrives with one 16-B load per lane into a
+// per-wave LDS copy, from which each lane reads the two bytes of (token,
+// 2c .. 2c + 1) per tile.  Columns, causal limits and the max-pool are those
+// of the FP8 form.
+template <int NT>
+__device__ __forceinline__ void scan_wave_nvfp4_cols(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales,
+                                                     const int32_t* __restrict__ bt_row, int L, int q_len,
+                                                     const uint16_t* __restrict__ iq_seq, float* __restrict__ bs_seq,
+                                                     int mbps, int jbeg, int jend, float idx_scale,
+                                                     uint8_t* lds_sc, int lane) {
+  const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int ncols = q_len * kGroups;
+  const int pos0 = L - q_len;  // position of query 0
+
+  // B operands: column 16t + n, dims 32c + 8s .. + 7 for step s, times 2^k
+  f16x8 qh[NT][4];
+  float unscale[NT];  // 2^-k of the lane's column, times idx_scale
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + n;
+    uint32_t w[4][4];
+    float mx = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 v = col < ncols ? *reinterpret_cast<const uint4*>(iq_seq + (size_t)col * kDim + 32 * c + 8 * s)
+                                  : make_uint4(0, 0, 0, 0);
+      w[s][0] = v.x, w[s][1] = v.y, w[s][2] = v.z, w[s][3] = v.w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        mx = fmaxf(mx, fmaxf(__builtin_fabsf(bf16lo_to_f32(w[s][k])), __builtin_fabsf(bf16hi_to_f32(w[s][k]))));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // mx in [2^(e-1), 2^e): scale by 2^(15 - e), kept within the normal fp32 range
+    const int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 15;
+    const int k = max(-126, min(126, 15 - e));
+    const float up = __builtin_ldexpf(1.0f, k);
+    unscale[t] = __builtin_ldexpf(1.0f, -k) * idx_scale;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        qh[t][s][2 * q] = (_Float16)(bf16lo_to_f32(w[s][q]) * up);
+        qh[t][s][2 * q + 1] = (_Float16)(bf16hi_to_f32(w[s][q]) * up);
+      }
+  }
+
+  for (int j = jbeg; j < jend; ++j) {
+    if (j >= nbv) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = -INFINITY;
+      continue;
+    }
+    const int64_t page = bt_row[j];
+    const uint8_t* kbase = codes + page * (kBlock * kDim / 2) + n * (kDim / 2) + 16 * c;
+    u32x4 kv[8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+      kv[T] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)T * 1024));
+    // the page's scales [token][group] (1 KB) through this wave's LDS copy
+    const u32x4 sc16 =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(scales + page * (kBlock * 8) + lane * 16));
+    *reinterpret_cast<u32x4*>(lds_sc + lane * 16) = sc16;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t sw[8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T) sw[T] = *reinterpret_cast<const uint16_t*>(lds_sc + (16 * T + n) * 8 + 2 * c);
+    const bool full = (j + 1) * kBlock - 1 <= pos0;  // wave-uniform: no mask
+    int vis[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vis[t] = pos0 + (16 * t + n) / kGroups + 1 - j * kBlock;
+    float m[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m[t] = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const uint32_t w[4] = {kv[T].x, kv[T].y, kv[T].z, kv[T].w};
+      const f16x2 sf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[T], 1.0f, false);  // groups 2c, 2c + 1
+      const f16x2 g0 = {sf.x, sf.x}, g1 = {sf.y, sf.y};
+      f16x8 kh[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x2 g = s < 2 ? g0 : g1;
+        const f16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 0) * g;
+        const f16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 1) * g;
+        const f16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 2) * g;
+        const f16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 3) * g;
+        kh[s] = f16x8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[s], qh[t][s], acc, 0, 0, 0);
+        if (full) {
+          m[t] = fmaxf(m[t], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[t] = fmaxf(m[t], 16 * T + 4 * c + i < vis[t] ? acc[i] : -INFINITY);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float x = fmaxf(m[t], __shfl_xor(m[t], 16));
+      x = fmaxf(x, __shfl_xor(x, 32));
+      if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = x * unscale[t];
+    }
+    __builtin_amdgcn_wave_barrier();  // the next page rewrites this wave's scales
   }
 }
 

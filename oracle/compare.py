@@ -11,7 +11,15 @@ readings written out):
     atol = 2e-3, rtol = 1e-2 (fp32 accumulation);
   * block scores: the GPU's fp32 sums of exact products may differ from the
     fp64 value only by fp32 rounding, |d| <= 2 * 130 * 2^-24 * A, where A is the
-    block's largest per-token sum of |iq_d * ik_td| (times idx_scale).
+    block's largest per-token sum of |iq_d * ik_td| (times idx_scale).  With
+    NVFP4 index keys and 2..8 query tokens the score contraction runs in f16
+    (NVFP4 keys converted straight to FP16 for the indexer's score MMA, vLLM
+    MiniMax-M3.1-Flash post, "NVIDIA Rubin-optimised MSA"): each (row, group) index query is scaled by 2^k so that its
+    largest |iq| lies in [2^14, 2^15) and rounded to f16; the bound then adds
+    the block's largest per-token sum of |ik_td| * |iq_d - f16(iq_d 2^k) 2^-k|
+    (times idx_scale; an element that lands among the f16 subnormals counts
+    whole, in case the MFMA flushes it), which is 0 unless some |iq_d| is below
+    2^-28 of its vector's largest.
 """
 from __future__ import annotations
 
@@ -54,11 +62,31 @@ def score_abs_bound(P, row):
     if L == 0:
         return out
     A = (ik[:L].abs() @ iq.abs().T) * P.idx_scale              # [L, G]
+    if P.arrays.get("idx_sf") is not None and P.q_len > 1:
+        A = A * (2.0 * 130.0 * 2.0 ** -24) + (ik[:L].abs() @ f16_query_rounding(iq).T) * P.idx_scale
+    else:
+        A = A * (2.0 * 130.0 * 2.0 ** -24)
     pad = torch.zeros(nb * 128, G, dtype=torch.float64)
     pad[:L] = A
     Ab = pad.reshape(nb, 128, G).amax(dim=1).T.numpy()         # [G, nb]
-    out[:, :nb] = 2.0 * 130.0 * 2.0 ** -24 * Ab + 1e-30
+    out[:, :nb] = Ab + 1e-30
     return out
+
+
+def f16_query_rounding(iq):
+    """|iq - f16(iq 2^k) 2^-k| per element of each [G][128] index query, with
+    2^k the power of two that puts the vector's largest |iq| in [2^14, 2^15)."""
+    x = iq.numpy()
+    out = np.zeros_like(x)
+    for g in range(x.shape[0]):
+        mx = np.abs(x[g]).max()
+        e = int(np.frexp(mx)[1]) if mx > 0 else 15
+        k = max(-126, min(126, 15 - e))
+        y = (x[g] * 2.0 ** k).astype(np.float32)
+        q16 = y.astype(np.float16).astype(np.float64) * 2.0 ** -k
+        # an f16 subnormal may also be flushed to zero inside the MFMA: count it whole
+        out[g] = np.where(np.abs(y) < 2.0 ** -14, np.abs(x[g]), np.abs(x[g] - q16))
+    return torch.from_numpy(out)
 
 
 def _order(bs, r):

@@ -141,11 +141,14 @@ def test_exhaustive_format_codes(dev):
     check_workload(w, label="exhaustive codes")
 
 
-def test_exhaustive_nvfp4_index_codes(dev):
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_exhaustive_nvfp4_index_codes(dev, q_len):
     """NVFP4 index keys: every E2M1 nibble in every position of a token row and
-    every finite E4M3 group scale appear; checks the NVFP4 scan's conversions,
-    nibble order and scale indexing end to end."""
-    w = synth.make_workload(seq_lens=[128 * 37, 128 * 20 + 11], idx_dtype="nvfp4", seed=26, layout="paged", device=dev)
+    every finite E4M3 group scale appear; checks the NVFP4 scans' conversions,
+    nibble order and scale indexing end to end (q_len 1: the decode scan with
+    per-group fp32 scaling; q_len 4: the column scan with exact dequantisation)."""
+    w = synth.make_workload(seq_lens=[128 * 37, 128 * 20 + 11], q_len=q_len, idx_dtype="nvfp4", seed=26,
+                            layout="paged", device=dev)
     codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8, device=dev)
     nib = torch.arange(256, dtype=torch.uint8, device=dev)
     m = w.idx_k.numel()
@@ -253,12 +256,45 @@ def test_multi_query_causal(dev, kv, idx, q_len):
     assert (out[pad:pad + q_len] == 0).all() and (sel[pad:pad + q_len] == -1).all()
 
 
+@pytest.mark.parametrize("q_len", [2, 4, 5, 8])
+def test_multi_query_nvfp4_index_keys(dev, q_len):
+    """NVFP4 index keys with a few query tokens (speculative verify): the keys
+    are dequantised exactly to bf16 for the MFMA column scan; the cases of the
+    multi-query test."""
+    lens = [q_len, q_len + 1, 127 + q_len, 2177, 0, 16 * 128 + q_len, 5000]
+    w = synth.make_workload(seq_lens=lens, q_len=q_len, kv_dtype="nvfp4", idx_dtype="nvfp4", plant=3,
+                            layout="paged", seed=60 + q_len, device=dev, max_blocks_per_seq=48)
+    out, sel, bs = check_workload(w, label=f"multi-query q_len={q_len} nvfp4 index keys")
+    pad = 4 * q_len
+    assert (out[pad:pad + q_len] == 0).all() and (sel[pad:pad + q_len] == -1).all()
+
+
+def test_multi_query_nvfp4_extreme_index_queries(dev):
+    """NVFP4 index keys, q_len 4: index queries with elements 2^-30 below their
+    vector's largest (rounded in the f16 score contraction, covered by the
+    bound's rounding term) and queries of magnitude 1e6 (beyond f16 without
+    the per-vector power-of-two scaling)."""
+    w = synth.make_workload(seq_lens=[4000, 2177, 0, 16 * 128 + 4], q_len=4, kv_dtype="nvfp4", idx_dtype="nvfp4",
+                            plant=3, layout="paged", seed=64, device=dev, max_blocks_per_seq=40)
+    iq = w.iq.float()
+    iq[0:4, :, ::7] *= 2.0 ** -30
+    iq[4:8] *= 1.0e6
+    w.iq.copy_(iq.to(torch.bfloat16))
+    check_workload(w, label="multi-query nvfp4 index keys, extreme index queries")
+
+
 def test_spec_b32_q4_128k_config_sampled(dev):
     """Speculative verify on the decode path: batch 32 x (128K + 4) with 4 query
     tokens each, in the bench's launch configuration; sampled rows cover the
     first and last query of a sequence and different sequences."""
     w = synth.make_config("spec_b32_q4_128k", device=dev)
     check_workload(w, rows=[0, 3, 4 * 13 + 1, 4 * 31 + 2, 4 * 31 + 3])
+
+
+def test_spec_b32_q4_128k_nvfp4_index_sampled(dev):
+    """The same with NVFP4 index keys (the f16 column scan), sampled rows."""
+    w = synth.make_config("spec_b32_q4_128k_nvfp4_idx", device=dev)
+    check_workload(w, rows=[0, 3, 4 * 13 + 1, 4 * 31 + 3])
 
 
 def test_verify_b2_q256_128k_config_sampled(dev):
