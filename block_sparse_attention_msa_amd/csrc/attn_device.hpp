@@ -47,6 +47,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQkTiles = kBlock / 16;   // 16-token MFMA tiles per block
+constexpr int kPRow = kBlock + 16;      // LDS row of softmax weights (halves), padded
 constexpr int kPvSteps = kBlock / 32;   // 32-token MFMA contraction steps per block
 
 // Workgroup shapes: NT = 1024 (16 waves, one kept block each) or NT = 512
@@ -74,8 +75,11 @@ struct AttnSmem {
     SelectSmem<NT> sel;
     MergeSmem<NT> merge;
   } u;
-  uint16_t p[kWaves][kHeadsPerGroup][kBlock];    // 1 KB per wave: softmax weights (f16, or bf16 hi part)
-  uint16_t plo[kWaves][kHeadsPerGroup][kBlock];  // 1 KB per wave: bf16 lo part (bf16 K/V only)
+  // softmax weights per wave: f16 (or the bf16 hi part) and the bf16 lo part
+  // (bf16 K/V only).  Rows padded to 288 B: the 4 head rows' token writes fall
+  // on distinct banks and the PV reads of the 4 heads on distinct 16-B slots.
+  uint16_t p[kWaves][kHeadsPerGroup][kPRow];
+  uint16_t plo[kWaves][kHeadsPerGroup][kPRow];
   uint8_t ksc[kWaves][kBlock * 8];               // 1 KB per wave: K scales [token][group]
   uint8_t vsc[kWaves][kBlock * 8];               // 1 KB per wave: V scales [token pair][group][2]
   int32_t sel[kTopK];
