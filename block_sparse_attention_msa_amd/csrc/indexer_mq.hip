@@ -93,20 +93,22 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
 
   const int h = lane >> 5;   // dim half of the A/B operands; token quarter of the results
   const int col = lane & 31; // A: token of the tile; B and results: row of the tile
+  // this wave's item range, wave-uniform (scalar registers): items
+  // [beg, end) of mbps x ntiles, walked as (block, row tile) without division
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const long long items = (long long)mbps * ntiles;
   const long long nw = (long long)wgs * kMqWaves;
-  const long long gw = (long long)wg * kMqWaves + wave;
-  const long long beg = items * gw / nw, end = items * (gw + 1) / nw;
+  const long long gw = (long long)wg * kMqWaves + wave_u;
+  const int beg = (int)(items * gw / nw), end = (int)(items * (gw + 1) / nw);
 
   bf16x8 a[kTokTiles][8];
   int cur = -1;          // block whose keys are in a[]
   bool seen = false;     // some row of the chunk sees block cur
   bool full = false;     // every row of the chunk sees all of block cur
   int vis0 = 0;          // tokens of block cur visible to query 0
+  int blk = beg / ntiles, rt = beg - (beg / ntiles) * ntiles;
 #pragma unroll 1
-  for (long long it = beg; it < end; ++it) {  // wave-uniform
-    const int blk = (int)(it / ntiles);
-    const int rt = (int)(it % ntiles);
+  for (int it = beg; it < end; ++it, rt = rt + 1 == ntiles ? 0 : rt + 1, blk += rt == 0 ? 1 : 0) {  // wave-uniform
     if (blk != cur) {
       cur = blk;
       seen = blk < nb && (long long)blk * kBlock <= pos_max;
