@@ -9,27 +9,28 @@
 // queries x 4 groups per sequence the scores are a real dense contraction:
 //   S[t][r] = sum_d ik[t][d] * iq[r][d],  t = tokens, r = (query, group) rows.
 //
-// gfx950 design: the index queries stay, the keys stream.
+// gfx950 design: the index queries stay in registers, the keys stream through
+// LDS once per workgroup.
 //  * 512-thread workgroups, one per CU, split evenly over the (sequence,
-//    256-row chunk) groups.  A workgroup stages its chunk's bf16 index queries
-//    (64 KB) once in LDS (rows padded to 272 B: conflict-free 16-byte reads);
-//    they serve as MFMA B operands.
-//  * Each wave walks a contiguous range of (block, 32-row tile) items of its
-//    group; the ranges are equal to one item, so no round of workgroups runs
-//    mostly empty.  For each block it enters: 4 tiles of 32 tokens.  A lane
-//    loads one token's 64 contiguous dims (FP8: 64 B) and converts them in
-//    registers (E4M3 -> bf16, exact) into the A operands of 8 K steps; the
-//    contraction axis is permuted (lane half h, step s, element e -> dim
-//    64h + 8s + e) identically for A and B, so both come from contiguous
-//    bytes.  The whole block's A operands stay in registers while the wave
-//    walks the row tiles, so every B read from LDS feeds four
-//    v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products are exact, fp32
-//    accumulation) and each row tile's block maximum is final at once.
-//  * The epilogue applies the causal mask (row r = 4i + g sees tokens at or
-//    before its query's position) and the max over the block's tokens in
+//    256-row chunk) groups; a workgroup takes a contiguous range of blocks.
+//    Wave w owns row tile w (32 (query, group) rows): its B operands (the
+//    rows' bf16 index queries, 8 K steps) are staged through LDS once and then
+//    stay in 32 VGPRs for the whole range.
+//  * The 8 waves walk their blocks together.  A block's keys (16 KB FP8, 32
+//    KB bf16) are loaded by all waves in contiguous 1 KB wave-loads two blocks
+//    ahead into registers, converted once per workgroup to bf16 (E4M3 ->
+//    bf16, exact) and written to one of two 32 KB LDS buffers with a swizzle
+//    (16-B chunk k of token t at t * 256 + 16 (k ^ (t mod 16))), so that both
+//    the row writes and the MFMA-layout reads are free of bank conflicts; one
+//    barrier per block.
+//  * Per 32-token tile a wave reads its A operands, 8 K steps of its lane's
+//    token, straight from LDS (contraction axis permuted: lane half h, step
+//    s, element e -> dim 64h + 8s + e, identically for A and B) and runs 8
+//    v_mfma_f32_32x32x16_bf16 (exact products, fp32 sums).
+//  * Epilogue: causal mask (row r = 4i + g sees tokens <= its query's
+//    position) only for partly visible blocks, max over the block's tokens in
 //    registers; the score matrix never reaches memory and each (row, block)
-//    score is written once.  Keys are re-read once per row chunk, from the
-//    Infinity Cache after the first chunk.
+//    score is written once.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -48,12 +49,6 @@ constexpr int kLdsRow = kDim * 2 + 16;             // bf16 row + 16 B pad
 // MFMA 32x32x16 bf16 lane layout (gfx950): lane l supplies A[l%32][8(l/32)+e]
 // and B[8(l/32)+e][l%32], e = 0..7; result register q of lane l holds
 // D[8(q/4) + 4(l/32) + q%4][l%32].
-//
-// Work split: a group = (sequence, 256-row chunk) has mbps x ntiles items
-// (block, 32-row tile).  The group's wgs workgroups stage the chunk once each
-// and give every wave one contiguous range of items in block-major order, so
-// the waves of the grid finish within one item of each other and a wave
-// converts a block's keys only when its range enters that block.
 template <bool FP8>
 __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __restrict__ idx_pool,
                                                              const int32_t* __restrict__ block_table,
@@ -61,15 +56,19 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
                                                              const uint16_t* __restrict__ iq,
                                                              float* __restrict__ block_scores, int q_len, int mbps,
                                                              int nchunks, int wgs, float idx_scale) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_q[kRowChunk * kLdsRow];  // 68 KB
-  constexpr int kKeyRow = FP8 ? kDim : kDim * 2;  // bytes per token of an index-key page
+  constexpr int kKeyRow = FP8 ? kDim : kDim * 2;      // bytes per token of an index-key page
+  constexpr int kPage = kBlock * kKeyRow;             // 16 KB or 32 KB
+  constexpr int kLoads = kPage / 1024 / kMqWaves;     // 1 KB wave-loads per wave and block (2 or 4)
+  constexpr int kRowB = kDim * 2;                     // bytes per token of a bf16 key row in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[kRowChunk * kLdsRow];     // 68 KB
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kBlock * kRowB];       // 2 x 32 KB, bf16 keys
   const int grp = blockIdx.x / wgs;
   const int wg = blockIdx.x % wgs;
   const int b = grp / nchunks;
   const int rc = grp % nchunks;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int L = seq_lens[b];
   const int nrows = q_len * kGroups;                 // (query, group) rows of this sequence
   const int row0 = rc * kRowChunk;                   // first row of this chunk
@@ -81,6 +80,9 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
   const int pos0 = L - q_len;                        // position of query 0
   const int pos_min = pos0 + row0 / kGroups;         // first and last query of the chunk
   const int pos_max = pos0 + (row0 + crow - 1) / kGroups;
+  const int32_t* bt_row = block_table + (size_t)b * mbps;
+  // this workgroup's blocks
+  const int jbeg = (int)((long long)mbps * wg / wgs), jend = (int)((long long)mbps * (wg + 1) / wgs);
 
   // ---- stage the chunk's index queries (rows past crow zero-filled)
   for (int i = tid; i < ntiles * 32 * 16; i += kMqThreads) {
@@ -93,97 +95,97 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
 
   const int h = lane >> 5;   // dim half of the A/B operands; token quarter of the results
   const int col = lane & 31; // A: token of the tile; B and results: row of the tile
-  // this wave's item range, wave-uniform (scalar registers): items
-  // [beg, end) of mbps x ntiles, walked as (block, row tile) without division
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const long long items = (long long)mbps * ntiles;
-  const long long nw = (long long)wgs * kMqWaves;
-  const long long gw = (long long)wg * kMqWaves + wave_u;
-  const int beg = (int)(items * gw / nw), end = (int)(items * (gw + 1) / nw);
+  const bool active = wave < ntiles;  // wave-uniform: this wave owns a row tile
+  const int r = 32 * wave + col;      // this lane's row (B column, result column), chunk-local
+  bf16x8 bq[8];
+  {
+    const uint8_t* qrow = lds_q + (active ? r : 0) * kLdsRow + h * kDim;  // dims 64h..
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+  }
 
-  bf16x8 a[kTokTiles][8];
-  int cur = -1;          // block whose keys are in a[]
-  bool seen = false;     // some row of the chunk sees block cur
-  bool full = false;     // every row of the chunk sees all of block cur
-  int vis0 = 0;          // tokens of block cur visible to query 0
-  int blk = beg / ntiles, rt = beg - (beg / ntiles) * ntiles;
-#pragma unroll 1
-  for (int it = beg; it < end; ++it, rt = rt + 1 == ntiles ? 0 : rt + 1, blk += rt == 0 ? 1 : 0) {  // wave-uniform
-    if (blk != cur) {
-      cur = blk;
-      seen = blk < nb && (long long)blk * kBlock <= pos_max;
-      if (seen) {
-        const int64_t page = block_table[(size_t)b * mbps + blk];
-        const uint8_t* kp = idx_pool + page * (kBlock * kKeyRow) + col * kKeyRow + h * (kKeyRow / 2);
-        full = (long long)blk * kBlock + kBlock - 1 <= pos_min;
-        vis0 = pos0 - blk * kBlock + 1;
-        // A operands of the whole block: 4 token tiles x 8 K steps
+  // block j is seen by some row of the chunk (wave-uniform)
+  auto seen = [&](int j) { return j < nb && (long long)j * kBlock <= pos_max; };
+  // this wave's share of block j's keys: kLoads contiguous 1 KB wave-loads
+  auto load_keys = [&](int j, u32x4 (&v)[kLoads]) {
+    if (j < jend && seen(j)) {
+      const uint8_t* src = idx_pool + (int64_t)bt_row[j] * kPage + (size_t)(wave * kLoads) * 1024 + lane * 16;
 #pragma unroll
-        for (int tt = 0; tt < kTokTiles; ++tt) {
-          const uint8_t* src = kp + (size_t)(32 * tt) * kKeyRow;
-          if constexpr (FP8) {
-            u32x4 w[4];
+      for (int i = 0; i < kLoads; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i * 1024));
+    }
+  };
+  // ... written to LDS buffer buf as bf16 (E4M3 -> bf16 exact, converted
+  // once per workgroup), swizzled: 16-B chunk k (dims 8k .. 8k + 7) of token t
+  // at t * 256 + 16 (k ^ (t mod 16))
+  auto lds_chunk = [&](int buf, int t, int k) { return &lds_k[buf][t * kRowB + ((k ^ (t & 15)) << 4)]; };
+  auto store_keys = [&](int j, int buf, const u32x4 (&v)[kLoads]) {
+    if (j < jend && seen(j)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * i));
-            const uint32_t d[16] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w,
-                                    w[2].x, w[2].y, w[2].z, w[2].w, w[3].x, w[3].y, w[3].z, w[3].w};
+      for (int i = 0; i < kLoads; ++i) {
+        const int byte = (wave * kLoads + i) * 1024 + lane * 16;  // offset in the page
+        const int t = byte / kKeyRow, k = (byte % kKeyRow) / 16;  // token, 16-B chunk of the stored row
+        if constexpr (FP8) {  // 16 dims -> bf16 chunks 2k, 2k + 1
+          const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          uint32_t o[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              const bf16x2 p0 = e4m3x2_to_bf16x2<false>(d[2 * s]);
-              const bf16x2 p1 = e4m3x2_to_bf16x2<true>(d[2 * s]);
-              const bf16x2 p2 = e4m3x2_to_bf16x2<false>(d[2 * s + 1]);
-              const bf16x2 p3 = e4m3x2_to_bf16x2<true>(d[2 * s + 1]);
-              a[tt][s] = bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-            }
-          } else {
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-              a[tt][s] = __builtin_bit_cast(bf16x8,
-                                            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * s)));
+          for (int q = 0; q < 4; ++q) {
+            o[2 * q] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(d[q]));
+            o[2 * q + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(d[q]));
           }
+          *reinterpret_cast<u32x4*>(lds_chunk(buf, t, 2 * k)) = u32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<u32x4*>(lds_chunk(buf, t, 2 * k + 1)) = u32x4{o[4], o[5], o[6], o[7]};
+        } else {
+          *reinterpret_cast<u32x4*>(lds_chunk(buf, t, k)) = v[i];
         }
       }
     }
-    const int r = 32 * rt + col;
-    if (!seen) {  // no row of the chunk sees this block
-      if (h == 0 && r < crow) bs[(size_t)r * mbps + blk] = -INFINITY;
-      continue;
-    }
-    // ---- one row tile: 4 accumulators, every B read from LDS feeds 4 MFMAs
-    const uint8_t* qrow = lds_q + (32 * rt + col) * kLdsRow + h * kDim;  // dims 64h..
-    bf16x8 bq[8];
+  };
+
+  u32x4 pf1[kLoads], pf2[kLoads];  // keys of blocks j + 1 and j + 2, in flight
+  load_keys(jbeg, pf1);
+  store_keys(jbeg, 0, pf1);
+  load_keys(jbeg + 1, pf1);
+  __syncthreads();
+#pragma unroll 1
+  for (int j = jbeg; j < jend; ++j) {  // wave-uniform
+    const int buf = (j - jbeg) & 1;
+    load_keys(j + 2, pf2);
+    if (!seen(j)) {  // no row of the chunk sees this block
+      if (active && h == 0 && r < crow) bs[(size_t)r * mbps + j] = -INFINITY;
+    } else if (active) {
+      const bool full = (long long)j * kBlock + kBlock - 1 <= pos_min;  // every row sees the whole block
+      const int vis = pos0 + (row0 + r) / kGroups + 1 - j * kBlock;     // tokens this lane's row sees
+      float m = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) bq[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
-    f32x16 acc[kTokTiles];
+      for (int tt = 0; tt < kTokTiles; ++tt) {
+        // A operands of token 32tt + col: bf16 dims 64h + 8s .. + 7 from LDS
+        const int t = 32 * tt + col;
+        bf16x8 a[8];
 #pragma unroll
-    for (int tt = 0; tt < kTokTiles; ++tt) acc[tt] = f32x16{};
+        for (int s = 0; s < 8; ++s) a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds_chunk(buf, t, 8 * h + s)));
+        f32x16 acc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bq[s], acc, 0, 0, 0);
+        if (full) {
 #pragma unroll
-      for (int tt = 0; tt < kTokTiles; ++tt)
-        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tt][s], bq[s], acc[tt], 0, 0, 0);
-      // keep the four independent accumulator chains interleaved: a chain's
-      // next MFMA then issues only after the other three
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    float m = -INFINITY;
-    if (full) {  // wave-uniform: no mask
+          for (int q = 0; q < 16; ++q) m = fmaxf(m, acc[q]);
+        } else {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) m = fmaxf(m, fmaxf(fmaxf(acc[0][q], acc[1][q]), fmaxf(acc[2][q], acc[3][q])));
-    } else {
-      // this lane's row (column of D) sees tokens < vis of the block
-      const int vis = vis0 + (row0 + r) / kGroups;
-#pragma unroll
-      for (int tt = 0; tt < kTokTiles; ++tt)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int tok = 32 * tt + 8 * (q >> 2) + 4 * h + (q & 3);
-          m = fmaxf(m, tok < vis ? acc[tt][q] : -INFINITY);
+          for (int q = 0; q < 16; ++q) {
+            const int tok = 32 * tt + 8 * (q >> 2) + 4 * h + (q & 3);
+            m = fmaxf(m, tok < vis ? acc[q] : -INFINITY);
+          }
         }
+      }
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (h == 0 && r < crow) bs[(size_t)r * mbps + j] = m * idx_scale;
     }
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (h == 0 && r < crow) bs[(size_t)r * mbps + blk] = m * idx_scale;
+    // the next block's keys into the other buffer (read by nobody since the
+    // last barrier), then the barrier that publishes them
+    store_keys(j + 1, buf ^ 1, pf1);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) pf1[i] = pf2[i];
+    __syncthreads();
   }
 }
 
