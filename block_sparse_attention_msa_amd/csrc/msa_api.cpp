@@ -80,6 +80,7 @@ msa_status check_cache(const msa_shape* s, const msa_cache* c, bool need_idx, bo
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t rows_of(const msa_shape* s) { return (size_t)s->num_seqs * (size_t)s->q_len; }
 size_t scores_bytes(const msa_shape* s) { return rows_of(s) * MSA_NUM_KV_HEADS * (size_t)s->max_blocks_per_seq * 4; }
+size_t sel_bytes(const msa_shape* s) { return rows_of(s) * MSA_NUM_KV_HEADS * (size_t)MSA_TOPK * 4; }
 
 msa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -150,7 +151,7 @@ size_t msa_attn_workspace_size(const msa_shape* shape) {
 
 size_t msa_workspace_size(const msa_shape* shape) {
   if (check_shape(shape) != MSA_OK) return 0;
-  return align256(scores_bytes(shape));
+  return align256(scores_bytes(shape)) + align256(sel_bytes(shape));
 }
 
 msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, const void* idx_q, float* block_scores,
@@ -213,13 +214,25 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   }
   if (shape->num_seqs == 0) return ok();
 
-  // 2 launches: index scan fused with the block max-pool, then selection
-  // fused with attention (each attention workgroup selects its (row, group)).
+  // Index scan fused with the block max-pool, then either the selection fused
+  // with the attention (each attention workgroup selects its (row, group): 2
+  // launches), or, when the attention workgroups run in more than one round
+  // (more (row, group) pairs than two per CU), the selection as a launch of
+  // its own between them (3 launches), so that the per-workgroup selection
+  // latency is not paid once per round.
   float* scores = static_cast<float*>(workspace);
   hipError_t e = launch_scan(shape, scan_args(shape, cache, idx_q, scores), stream);
   if (e != hipSuccess) return hip_status(e, "index scan");
-  e = msa::launch_sparse_attn(attn_args(shape, cache, q, scores, nullptr, sel_blocks, out), stream);
-  return hip_status(e, "selection + sparse attention");
+  const long long pairs = (long long)rows_of(shape) * shape->num_kv_heads;
+  if (pairs <= 2LL * msa::device_cus())
+    return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, scores, nullptr, sel_blocks, out), stream),
+                      "selection + sparse attention");
+  int32_t* sel = sel_blocks ? sel_blocks
+                            : reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)));
+  msa::TopkArgs ta{cache->seq_lens, scores, sel, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};
+  if ((e = msa::launch_block_topk(ta, stream)) != hipSuccess) return hip_status(e, "block top-k");
+  return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, nullptr, sel, nullptr, out), stream),
+                    "sparse attention");
 }
 
 msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const void* k_new, const void* v_new,

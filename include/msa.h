@@ -108,8 +108,10 @@ typedef struct {
 } msa_cache;
 
 /* Bytes of device workspace msa_decode needs for this shape: the fp32 block
- * scores [rows][num_kv_heads][max_blocks_per_seq], 256-B aligned.  Its
- * contents need no initialisation.  Returns 0 for an invalid shape (see
+ * scores [rows][num_kv_heads][max_blocks_per_seq], then the int32 selected
+ * ids [rows][num_kv_heads][16] (used when sel_blocks is NULL and the
+ * selection runs as a launch of its own), each 256-B aligned.  Its contents
+ * need no initialisation.  Returns 0 for an invalid shape (see
  * msa_last_error()).  msa_attn_workspace_size() is 0: the stand-alone
  * attention merges its split work on chip and needs no workspace. */
 size_t msa_workspace_size(const msa_shape* shape);
@@ -152,9 +154,12 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
                                   const int32_t* sel_blocks, float* out, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
-/* The fused path: steps 1-4 in one call (two launches: the index scan fused
- * with the block max-pool, then the selection fused with the attention), no
- * host synchronisation.
+/* The fused path: steps 1-4 in one call, no host synchronisation: the index
+ * scan fused with the block max-pool, then the selection fused with the
+ * attention (two launches), or, when there are more (row, group) pairs than
+ * two per compute unit (the attention workgroups would run in several
+ * rounds), the selection as a launch of its own before the attention (three
+ * launches).  Results are the same either way.
  *   sel_blocks int32 [rows][num_kv_heads][16], or NULL if not wanted.
  *   workspace  >= msa_workspace_size(shape) bytes, 256-B aligned. */
 msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,

@@ -124,7 +124,8 @@ def test_workspace_size_and_too_small():
     assert need >= scores and need % 256 == 0
     assert _decode(s, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in msa.last_error()
-    assert need == scores   # the fused path's workspace is the block scores only
+    ids = 32 * 4 * 16 * 4
+    assert need == scores + ids  # the block scores, then the selected ids (256-B aligned each)
     assert L.msa_attn_workspace_size(ctypes.byref(s)) == 0
 
 
@@ -143,7 +144,8 @@ def test_other_entry_points_validate():
     s = _shape()
     assert L.msa_indexer_score(ctypes.byref(s), ctypes.byref(_cache()), None, FAKE, None) == \
         msa.MSA_ERR_INVALID_ARGUMENT
-    assert L.msa_workspace_size(ctypes.byref(_shape(q_len=256))) == 2 * 256 * 4 * 8 * 4  # multi-query rows
+    rows = 2 * 256  # multi-query rows: scores [rows][4][8 blocks] + ids [rows][4][16]
+    assert L.msa_workspace_size(ctypes.byref(_shape(q_len=256))) == rows * 4 * 8 * 4 + rows * 4 * 16 * 4
     assert L.msa_block_topk(ctypes.byref(s), None, FAKE, FAKE, None) == msa.MSA_ERR_INVALID_ARGUMENT
     assert L.msa_sparse_attn_decode(ctypes.byref(s), ctypes.byref(_cache(v=None)), FAKE, FAKE, FAKE, FAKE, 1 << 30,
                                     None) == msa.MSA_ERR_INVALID_ARGUMENT

@@ -6,6 +6,7 @@ configuration the bench times and compared on sampled rows.  Rules (ids
 bit-exact except near ties, out within 2e-3 + 1e-2|ref|, block scores within
 the fp32 rounding bound) are in oracle/compare.py.
 """
+import ctypes
 import math
 import sys
 
@@ -320,6 +321,29 @@ def test_workspace_reuse_across_calls_and_shapes(dev):
         o, s_ = out.cpu().numpy(), sel.cpu().numpy()
         for row in range(w.rows):
             check_row(P, row, o[row], s_[row])
+
+
+@pytest.mark.parametrize("q_len", [1, 64])
+def test_decode_without_selected_ids_output(dev, q_len):
+    """msa_decode with sel_blocks NULL: the same outputs as with it, both when
+    the selection is fused into the attention (q_len 1: 32 (row, group)
+    pairs) and when it runs as its own launch with its ids in the workspace
+    (q_len 64: 2,048 pairs, more than two per compute unit)."""
+    msa = _msa()
+    lens = [9000, 4000 + q_len, 129 + q_len, 3000, 0, 2500, 7000, 128 * 9 + q_len]
+    w = synth.make_workload(seq_lens=lens, q_len=q_len, plant=3, layout="paged", seed=70 + q_len, device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    out, sel = msa.alloc_outputs(w)
+    ws = torch.full((msa.lib().msa_workspace_size(ctypes.byref(shape)),), 0x7F, dtype=torch.uint8, device=dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+    out2 = torch.empty_like(out)
+    msa.msa_decode(shape, cache, w.q, w.iq, out2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    P = oracle.Problem.from_workload(w)
+    o, s_ = out2.cpu().numpy(), sel.cpu().numpy()
+    for row in range(0, w.rows, max(1, w.rows // 24)):
+        check_row(P, row, o[row], s_[row])
 
 
 def test_graph_capture_replays(dev):
