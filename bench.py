@@ -106,10 +106,15 @@ def traffic_file(config: str) -> str:
 
 
 def scan_source_hash() -> str:
+    """Hash of the scan kernels' sources and of the compiler flags they are
+    built with: a traffic record stays valid only for the same code."""
     import hashlib
+    from block_sparse_attention_msa_amd import build as hip_build
     h = hashlib.sha256()
     for name in SCAN_SOURCES:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_msa_amd", "csrc", name), "rb").read())
+        if name.endswith(".hip"):
+            h.update(" ".join(hip_build.FLAGS + hip_build.FILE_FLAGS.get(name, [])).encode())
     return h.hexdigest()
 
 
