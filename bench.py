@@ -46,11 +46,10 @@ def cpu_model() -> str:
 def scan_bytes(w) -> float:
     """Algorithmic bytes of one index-scan launch: every visible token's index
     key, the used block-table entries, the index queries, the block scores."""
-    from block_sparse_attention_msa_amd.synth import IDX_BYTES_PER_TOKEN
     lens = [int(x) for x in w.seq_lens.cpu().tolist()]
-    key_b = IDX_BYTES_PER_TOKEN[w.idx_dtype]
     nbs = [((L - 1) // 128 + 1) if L > 0 else 0 for L in lens]
-    return (sum(lens) * key_b + sum(nbs) * 4 + w.rows * w.num_kv_heads * 128 * 2
+    # index keys: every visible token's, a shared-prefix page once for its group
+    return (w.nbytes_algorithmic()["scan"] + sum(nbs) * 4 + w.rows * w.num_kv_heads * 128 * 2
             + w.rows * w.num_kv_heads * w.max_blocks_per_seq * 4)
 
 
@@ -70,7 +69,8 @@ def scan_flops(w) -> float:
 def clone_workload(w):
     import copy
     w2 = copy.copy(w)
-    for name in ("q", "iq", "idx_k", "idx_sf", "k", "v", "k_sf", "v_sf", "block_table", "seq_lens"):
+    for name in ("q", "iq", "idx_k", "idx_sf", "k", "v", "k_sf", "v_sf", "block_table", "seq_lens",
+                 "share_members", "share_blocks", "seq_shared_blocks"):
         t = getattr(w, name)
         setattr(w2, name, None if t is None else t.clone())
     return w2
@@ -152,25 +152,45 @@ def write_traffic(config: str, fetch_dir: str, write_dir: str):
     traffic record of the config's scan: each counter is scaled by what it
     read for the plain copy of COPY_BYTES in the same runs."""
     fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
-    scan = [k for k in fetch if re.search(r"scan_(decode|cols)", k)]
-    if len(scan) != 1:
-        raise SystemExit(f"expected one scan kernel in {fetch_dir}, found {scan}")
-    scan = scan[0]
-    # the calibration kernel: torch's negation of COPY_BYTES, once per scan launch
-    copy = [k for k in write if "neg" in k.lower() and k in fetch and write[k][1] == fetch[scan][1]]
+    # the scan's kernels (two with prefix sharing: the sequences' own blocks,
+    # then the shared ones), each dispatched once per scan call
+    scans = sorted(k for k in fetch if re.search(r"scan_(decode|cols|shared)", k))
+    if not scans or len({fetch[k][1] for k in scans}) != 1 or any(k not in write for k in scans):
+        raise SystemExit(f"expected the scan kernels once per call in {fetch_dir}, found {scans}")
+    n = fetch[scans[0]][1]
+    # the calibration kernel: torch's negation of COPY_BYTES, once per scan call
+    copy = [k for k in write if "neg" in k.lower() and k in fetch and write[k][1] == n]
     if len(copy) != 1:
         raise SystemExit(f"expected one calibration kernel in {write_dir}, found {copy}")
     copy = copy[0]
     fs, ws = COPY_BYTES / (fetch[copy][0] * 1024.0), COPY_BYTES / (write[copy][0] * 1024.0)
-    fb, wb = fetch[scan][0] * 1024.0 * fs, write[scan][0] * 1024.0 * ws
-    rec = {"kernel": re.search(r"scan_(?:decode|cols)\w*(?:<[^>]*>)?", scan).group(0), "workload": config, "source_sha256": scan_source_hash(),
-           "fetch_kib_per_dispatch_raw": fetch[scan][0], "write_kib_per_dispatch_raw": write[scan][0],
+    fraw, wraw = sum(fetch[k][0] for k in scans), sum(write[k][0] for k in scans)
+    fb, wb = fraw * 1024.0 * fs, wraw * 1024.0 * ws
+    names = [re.search(r"scan_(?:decode|cols|shared)\w*(?:<[^>]*>)?", k).group(0) for k in scans]
+    rec = {"kernel": " + ".join(names), "workload": config, "source_sha256": scan_source_hash(),
+           "fetch_kib_per_dispatch_raw": fraw, "write_kib_per_dispatch_raw": wraw,
            "copy_fetch_kib_raw": fetch[copy][0], "copy_write_kib_raw": write[copy][0], "copy_bytes": COPY_BYTES,
            "fetch_scale": fs, "write_scale": ws, "fetch_bytes": fb, "write_bytes": wb,
-           "bytes_per_launch": int(round(fb + wb)), "dispatches": fetch[scan][1]}
+           "bytes_per_launch": int(round(fb + wb)), "dispatches": n}
     with open(traffic_file(config), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def scan_call(msa, shape, cache, c, bs, stream):
+    """The index scan of workload copy c (the shared-prefix call when it has groups)."""
+    if c.share_members is not None:
+        msa.msa_indexer_score_shared(shape, cache, msa.MsaPrefixShare.from_workload(c), c.iq, bs, stream)
+    else:
+        msa.msa_indexer_score(shape, cache, c.iq, bs, stream)
+
+
+def decode_call(msa, shape, cache, c, out, sel, ws, stream):
+    """One msa_decode step of workload copy c (msa_decode_shared when it has groups)."""
+    if c.share_members is not None:
+        msa.msa_decode_shared(shape, cache, msa.MsaPrefixShare.from_workload(c), c.q, c.iq, out, sel, ws, stream)
+    else:
+        msa.msa_decode(shape, cache, c.q, c.iq, out, sel, ws, stream)
 
 
 def run_counter_pass(args, w, copies, shape, caches):
@@ -186,7 +206,7 @@ def run_counter_pass(args, w, copies, shape, caches):
     dst = torch.empty_like(src)
     for i in range(args.steps):
         c = copies[i % len(copies)]
-        msa.msa_indexer_score(shape, caches[i % len(copies)], c.iq, bs)
+        scan_call(msa, shape, caches[i % len(copies)], c, bs, None)
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log(f"[bench] counters pass: {args.steps} scan launches ({scan_bytes(w)} algorithmic B each), "
@@ -239,7 +259,7 @@ def main():
 
     def step(i):
         c = copies[i % len(copies)]
-        msa.msa_decode(shape, caches[i % len(copies)], c.q, c.iq, out, sel, ws, stream)
+        decode_call(msa, shape, caches[i % len(copies)], c, out, sel, ws, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -260,12 +280,12 @@ def main():
     bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
     for i in range(args.warmup):
         c = copies[i % len(copies)]
-        msa.msa_indexer_score(shape, caches[i % len(copies)], c.iq, bs, stream)
+        scan_call(msa, shape, caches[i % len(copies)], c, bs, stream)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
         c = copies[i % len(copies)]
-        msa.msa_indexer_score(shape, caches[i % len(copies)], c.iq, bs, stream)
+        scan_call(msa, shape, caches[i % len(copies)], c, bs, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     scan_us = e0.elapsed_time(e1) / args.steps * 1e3
@@ -303,7 +323,9 @@ def main():
     # little arithmetic per byte; long ones are a dense contraction.
     fl = scan_flops(w) if w.q_len > 1 else 0.0
     mfma_bound = fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > sb / (HBM_PEAK_GBPS * 1e9)
-    if w.q_len == 1:
+    if w.share_members is not None:
+        kname = "index scan + block max-pool, each shared-prefix page read once per group (FP8 keys, bf16 MFMA)"
+    elif w.q_len == 1:
         kname = {"fp8": "index scan + block max-pool (FP8 keys, bf16 MFMA)",
                  "nvfp4": "index scan + block max-pool (NVFP4 keys, bf16 MFMA)",
                  "bf16": "index scan + block max-pool (bf16 keys, VALU dot2)"}[w.idx_dtype]

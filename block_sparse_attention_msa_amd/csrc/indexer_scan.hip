@@ -76,9 +76,49 @@ __global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_kernel(const
   const int jbeg = (blockIdx.x * kColsScanWaves + wave) * pages_per_wave;
   if (jbeg >= mbps) return;
   const int jend = min(jbeg + pages_per_wave, mbps);
-  const size_t ncols = (size_t)q_len * kGroups;
-  scan_wave_fp8_mfma<NT>(idx_pool, block_table + (size_t)b * mbps, seq_lens[b], q_len, iq + b * ncols * kDim,
-                         block_scores + b * ncols * mbps, mbps, jbeg, jend, idx_scale, lds_t[wave], lane);
+  const int L = seq_lens[b];
+  const int ncols = q_len * kGroups;
+  const SeqCols cm{iq + (size_t)b * ncols * kDim, block_scores + (size_t)b * ncols * mbps, mbps, ncols, L - q_len,
+                   L > 0 ? (L - 1) / kBlock + 1 : 0};
+  scan_wave_fp8_mfma<NT>(idx_pool, block_table + (size_t)b * mbps, cm, jbeg, jend, idx_scale, lds_t[wave], lane);
+}
+
+// Prefix sharing (FP8 index keys, q_len 1) in one launch: grid rows y <
+// num_groups are the shared pass, one wave per (sharing group, shared block):
+// the group leader's page is read once and scored against the index queries
+// of all the group's members (up to 8: 32 MFMA columns); rows y >= num_groups
+// are the sequences' own blocks (the column scan, the shared blocks skipped).
+// The shared rows come first in dispatch order, so the two parts overlap.
+__global__ __launch_bounds__(kColsScanWaves * kWave, 4) void scan_shared_kernel(
+    const uint8_t* __restrict__ idx_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores,
+    const int32_t* __restrict__ members, const int32_t* __restrict__ shared_blocks,
+    const int32_t* __restrict__ seq_shared_blocks, int num_groups, int mbps, float idx_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t[kColsScanWaves][2 * 2048];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int j = blockIdx.x * kColsScanWaves + wave;
+  if ((int)blockIdx.y >= num_groups) {  // a sequence's own blocks
+    const int b = blockIdx.y - num_groups;
+    if (j >= mbps || j < seq_shared_blocks[b]) return;
+    const int L = seq_lens[b];
+    const SeqCols cm{iq + (size_t)b * kGroups * kDim, block_scores + (size_t)b * kGroups * mbps, mbps, kGroups, L - 1,
+                     L > 0 ? (L - 1) / kBlock + 1 : 0};
+    scan_wave_fp8_mfma<1>(idx_pool, block_table + (size_t)b * mbps, cm, j, j + 1, idx_scale, lds_t[wave], lane);
+    return;
+  }
+  const int gi = blockIdx.y;
+  if (j >= min(shared_blocks[gi], mbps)) return;
+  const int32_t* mem = members + (size_t)gi * kShareMax;
+  int nmem = 0, pos0 = 0x7fffffff;
+  for (int k = 0; k < kShareMax; ++k) {  // wave-uniform
+    if (mem[k] < 0) break;
+    ++nmem;
+    pos0 = min(pos0, seq_lens[mem[k]] - 1);
+  }
+  if (nmem == 0) return;
+  const ShareCols cm{mem, seq_lens, iq, block_scores, mbps, nmem * kGroups, pos0, 0x7fffffff};
+  scan_wave_fp8_mfma<2>(idx_pool, block_table + (size_t)mem[0] * mbps, cm, j, j + 1, idx_scale, lds_t[wave], lane);
 }
 
 // NVFP4 index keys, 2 <= q_len <= 8: the same columns, keys dequantised
@@ -129,6 +169,16 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
   else
     scan_cols_kernel<2><<<grid, block, 0, stream>>>(pool, a.block_table, a.seq_lens, a.iq, a.block_scores, q_len,
                                                      a.mbps, ppw, a.idx_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_shared(const ScanArgs& a, const int32_t* members, const int32_t* shared_blocks,
+                              const int32_t* seq_shared_blocks, int num_groups, hipStream_t stream) {
+  if (a.idx_fmt != kIdxFp8 || num_groups + a.num_seqs > 65535) return hipErrorInvalidValue;
+  dim3 grid((a.mbps + kColsScanWaves - 1) / kColsScanWaves, num_groups + a.num_seqs);
+  scan_shared_kernel<<<grid, dim3(kColsScanWaves * kWave), 0, stream>>>(
+      static_cast<const uint8_t*>(a.idx_pool), a.block_table, a.seq_lens, a.iq, a.block_scores, members,
+      shared_blocks, seq_shared_blocks, num_groups, a.mbps, a.idx_scale);
   return hipGetLastError();
 }
 

@@ -135,6 +135,31 @@ hipError_t launch_scan(const msa_shape* s, const msa::ScanArgs& a, hipStream_t s
   return msa::launch_scan_mq(a, s->q_len, stream);
 }
 
+static_assert(msa::kShareMax == MSA_SHARE_MAX, "one member limit on both sides of the boundary");
+
+msa_status check_share(const msa_shape* s, const msa_prefix_share* sh) {
+  if (!sh) return fail(MSA_ERR_INVALID_ARGUMENT, "share is NULL");
+  if (sh->num_groups < 0) return fail(MSA_ERR_INVALID_ARGUMENT, "share num_groups = %d < 0", sh->num_groups);
+  if (sh->num_groups == 0) return MSA_OK;
+  if (!sh->members || !sh->shared_blocks || !sh->seq_shared_blocks)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "share members / shared_blocks / seq_shared_blocks is NULL");
+  if (s->q_len != 1) return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with q_len = %d (supported for q_len 1)", s->q_len);
+  if (s->idx_dtype != MSA_IDX_FP8_E4M3)
+    return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with index-key dtype %d (supported for FP8)", (int)s->idx_dtype);
+  if ((long long)sh->num_groups + s->num_seqs > 65535)
+    return fail(MSA_ERR_UNSUPPORTED, "share num_groups + num_seqs = %lld > 65535", (long long)sh->num_groups + s->num_seqs);
+  return MSA_OK;
+}
+
+// The index scan, with prefix sharing when share has groups (one launch: each
+// group's shared blocks once, every sequence's own blocks).
+hipError_t launch_scan_any(const msa_shape* s, const msa::ScanArgs& a, const msa_prefix_share* share,
+                           hipStream_t stream) {
+  if (!share || share->num_groups == 0) return launch_scan(s, a, stream);
+  return msa::launch_scan_shared(a, share->members, share->shared_blocks, share->seq_shared_blocks,
+                                 share->num_groups, stream);
+}
+
 msa_status check_aligned(const void* p, size_t a, const char* what) {
   if (((uintptr_t)p) % a) return fail(MSA_ERR_INVALID_ARGUMENT, "%s must be %zu-byte aligned", what, a);
   return MSA_OK;
@@ -154,16 +179,28 @@ size_t msa_workspace_size(const msa_shape* shape) {
   return align256(scores_bytes(shape)) + align256(sel_bytes(shape));
 }
 
-msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, const void* idx_q, float* block_scores,
-                             hipStream_t stream) {
+static msa_status indexer_impl(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
+                               const void* idx_q, float* block_scores, hipStream_t stream) {
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;
   if ((st = check_cache(shape, cache, true, false)) != MSA_OK) return st;
+  if (share && (st = check_share(shape, share)) != MSA_OK) return st;
   if (!idx_q || !block_scores) return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q / block_scores is NULL");
   if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
   if ((st = check_aligned(idx_q, 16, "idx_q")) != MSA_OK) return st;
   if (shape->num_seqs == 0) return ok();
-  return hip_status(launch_scan(shape, scan_args(shape, cache, idx_q, block_scores), stream), "index scan");
+  return hip_status(launch_scan_any(shape, scan_args(shape, cache, idx_q, block_scores), share, stream), "index scan");
+}
+
+msa_status msa_indexer_score(const msa_shape* shape, const msa_cache* cache, const void* idx_q, float* block_scores,
+                             hipStream_t stream) {
+  return indexer_impl(shape, cache, nullptr, idx_q, block_scores, stream);
+}
+
+msa_status msa_indexer_score_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
+                                    const void* idx_q, float* block_scores, hipStream_t stream) {
+  if (!share) return fail(MSA_ERR_INVALID_ARGUMENT, "share is NULL");
+  return indexer_impl(shape, cache, share, idx_q, block_scores, stream);
 }
 
 msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const float* block_scores,
@@ -194,11 +231,13 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
                     "sparse attention");
 }
 
-msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
-                      int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
+                              const void* q, const void* idx_q, float* out, int32_t* sel_blocks, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;
   if ((st = check_cache(shape, cache, true, true)) != MSA_OK) return st;
+  if (share && (st = check_share(shape, share)) != MSA_OK) return st;
   if (!q || !idx_q || !out) return fail(MSA_ERR_INVALID_ARGUMENT, "q / idx_q / out is NULL");
   if ((st = check_aligned(q, 16, "q")) != MSA_OK) return st;
   if ((st = check_aligned(idx_q, 16, "idx_q")) != MSA_OK) return st;
@@ -221,7 +260,7 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   // its own between them (3 launches), so that the per-workgroup selection
   // latency is not paid once per round.
   float* scores = static_cast<float*>(workspace);
-  hipError_t e = launch_scan(shape, scan_args(shape, cache, idx_q, scores), stream);
+  hipError_t e = launch_scan_any(shape, scan_args(shape, cache, idx_q, scores), share, stream);
   if (e != hipSuccess) return hip_status(e, "index scan");
   const long long pairs = (long long)rows_of(shape) * shape->num_kv_heads;
   if (pairs <= 2LL * msa::device_cus())
@@ -233,6 +272,18 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
   if ((e = msa::launch_block_topk(ta, stream)) != hipSuccess) return hip_status(e, "block top-k");
   return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, nullptr, sel, nullptr, out), stream),
                     "sparse attention");
+}
+
+msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
+                      int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(shape, cache, nullptr, q, idx_q, out, sel_blocks, workspace, workspace_bytes, stream);
+}
+
+msa_status msa_decode_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
+                             const void* q, const void* idx_q, float* out, int32_t* sel_blocks, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!share) return fail(MSA_ERR_INVALID_ARGUMENT, "share is NULL");
+  return decode_impl(shape, cache, share, q, idx_q, out, sel_blocks, workspace, workspace_bytes, stream);
 }
 
 msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const void* k_new, const void* v_new,

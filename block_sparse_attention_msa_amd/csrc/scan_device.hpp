@@ -235,17 +235,52 @@ namespace msa {
 //    the causal limit of the lane's column (query i sees tokens at or before
 //    position seq_len - q_len + i), then 2 cross-lane steps per block.
 // Products are exact in fp32, sums fp32 (the MFMA's accumulation).
-template <int NT>
+//
+// Which index query each column holds, where its block scores go and which
+// tokens it sees come from a column map:
+//   ncols            columns in use
+//   pos0             smallest query position over the columns
+//   nbv              blocks j >= nbv hold no visible token (scores -inf)
+//   iq(col), bs(col) the column's index query and block-score row
+//   last_pos(col)    the column's query position (tokens at or before it count)
+struct SeqCols {  // one sequence's q_len x 4 (query, group) columns: col = 4 i + g
+  const uint16_t* iq_seq;  // [q_len][4][128]
+  float* bs_seq;           // [q_len][4][mbps]
+  int mbps, ncols, pos0, nbv;
+  __device__ const uint16_t* iq(int col) const { return iq_seq + (size_t)col * kDim; }
+  __device__ float* bs(int col) const { return bs_seq + (size_t)col * mbps; }
+  __device__ int last_pos(int col) const { return pos0 + col / kGroups; }
+};
+struct ShareCols {  // a sharing group's members x 4 (member, group) columns, q_len 1: col = 4 k + g
+  const int32_t* members;  // [8] sequence ids of the group (-1 padded)
+  const int32_t* seq_lens;
+  const uint16_t* iq_all;  // [num_seqs][4][128]
+  float* bs_all;           // [num_seqs][4][mbps]
+  int mbps, ncols, pos0, nbv;
+  __device__ size_t row(int col) const { return (size_t)members[col / kGroups] * kGroups + col % kGroups; }
+  __device__ const uint16_t* iq(int col) const { return iq_all + row(col) * kDim; }
+  __device__ float* bs(int col) const { return bs_all + row(col) * mbps; }
+  __device__ int last_pos(int col) const { return seq_lens[members[col / kGroups]] - 1; }
+};
+
+template <int NT, class Cols>
 __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ idx_pool,
-                                                   const int32_t* __restrict__ bt_row, int L, int q_len,
-                                                   const uint16_t* __restrict__ iq_seq, float* __restrict__ bs_seq,
-                                                   int mbps, int jbeg, int jend, float idx_scale, uint8_t* lds,
-                                                   int lane) {
-  const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
+                                                   const int32_t* __restrict__ bt_row, const Cols& cm, int jbeg,
+                                                   int jend, float idx_scale, uint8_t* lds, int lane) {
+  const int nbv = cm.nbv;
   const int c = lane >> 4;
   const int n = lane & 15;
-  const int ncols = q_len * kGroups;
-  const int pos0 = L - q_len;  // position of query 0
+  const int ncols = cm.ncols;
+  const int pos0 = cm.pos0;  // smallest query position of the columns
+  // this lane's columns 16t + n: block-score rows and query positions
+  float* bsp[NT];
+  int lastp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + n;
+    bsp[t] = col < ncols ? cm.bs(col) : nullptr;
+    lastp[t] = col < ncols ? cm.last_pos(col) : 0;
+  }
   // LDS offsets of this lane's tile writes (token 8hh + lane/8, chunk lane%8)
   // and column reads (token n, chunk 4h + c)
   const int wr = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
@@ -260,8 +295,7 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int d = 64 * (s >> 1) + 16 * c + 8 * (s & 1);
-      const uint4 w = col < ncols ? *reinterpret_cast<const uint4*>(iq_seq + (size_t)col * kDim + d)
-                                  : make_uint4(0, 0, 0, 0);
+      const uint4 w = col < ncols ? *reinterpret_cast<const uint4*>(cm.iq(col) + d) : make_uint4(0, 0, 0, 0);
       qb[t][s] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -270,7 +304,7 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
     if (j >= nbv) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = -INFINITY;
+        if (c == 0 && 16 * t + n < ncols) bsp[t][j] = -INFINITY;
       continue;
     }
     const int64_t page = bt_row[j];
@@ -282,7 +316,7 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
     const bool full = (j + 1) * kBlock - 1 <= pos0;
     int vis[NT];  // tokens of the block visible to this lane's column
 #pragma unroll
-    for (int t = 0; t < NT; ++t) vis[t] = pos0 + (16 * t + n) / kGroups + 1 - j * kBlock;
+    for (int t = 0; t < NT; ++t) vis[t] = lastp[t] + 1 - j * kBlock;
     float m[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) m[t] = -INFINITY;
@@ -325,7 +359,7 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
     for (int t = 0; t < NT; ++t) {
       float x = fmaxf(m[t], __shfl_xor(m[t], 16));
       x = fmaxf(x, __shfl_xor(x, 32));
-      if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = x * idx_scale;
+      if (c == 0 && 16 * t + n < ncols) bsp[t][j] = x * idx_scale;
     }
     __builtin_amdgcn_wave_barrier();  // the next block rewrites this wave's tiles
   }

@@ -20,7 +20,8 @@ MSA_KV_BF16, MSA_KV_NVFP4 = 0, 1
 MSA_IDX_BF16, MSA_IDX_FP8_E4M3, MSA_IDX_NVFP4 = 0, 1, 2
 _IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
-            "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_status_string", "msa_last_error")
+            "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_indexer_score_shared", "msa_decode_shared",
+            "msa_status_string", "msa_last_error")
 
 
 class MsaError(RuntimeError):
@@ -65,6 +66,29 @@ class MsaCache(ctypes.Structure):
                                 seq_lens=w.seq_lens, idx_sf=w.idx_sf)
 
 
+class MsaPrefixShare(ctypes.Structure):
+    """Prefix-sharing groups (msa_prefix_share): device int32 arrays."""
+    _fields_ = [("num_groups", ctypes.c_int32), ("members", ctypes.c_void_p), ("shared_blocks", ctypes.c_void_p),
+                ("seq_shared_blocks", ctypes.c_void_p)]
+
+    @classmethod
+    def from_tensors(cls, *, members, shared_blocks, seq_shared_blocks) -> "MsaPrefixShare":
+        for name, t in (("members", members), ("shared_blocks", shared_blocks),
+                        ("seq_shared_blocks", seq_shared_blocks)):
+            if t.dtype != torch.int32:
+                raise TypeError(f"{name} must be int32")
+        c = cls(int(shared_blocks.numel()), _ptr(members), _ptr(shared_blocks), _ptr(seq_shared_blocks))
+        c._keep = (members, shared_blocks, seq_shared_blocks)
+        return c
+
+    @classmethod
+    def from_workload(cls, w) -> "MsaPrefixShare":
+        if w.share_members is None:
+            return cls(0, None, None, None)
+        return cls.from_tensors(members=w.share_members, shared_blocks=w.share_blocks,
+                                seq_shared_blocks=w.seq_shared_blocks)
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -97,7 +121,11 @@ def lib():
         L.msa_sparse_attn_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_kv_insert.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp]
-        for f in ("msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert"):
+        L.msa_indexer_score_shared.argtypes = [P(MsaShape), P(MsaCache), P(MsaPrefixShare), vp, vp, vp]
+        L.msa_decode_shared.argtypes = [P(MsaShape), P(MsaCache), P(MsaPrefixShare), vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+        for f in ("msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert",
+                  "msa_indexer_score_shared", "msa_decode_shared"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -157,6 +185,18 @@ def msa_decode(shape, cache, q, idx_q, out, sel_blocks, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().msa_decode(ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(idx_q), _ptr(out),
                             _ptr(sel_blocks), _ptr(workspace), nbytes, _stream(stream)), "msa_decode")
+
+
+def msa_indexer_score_shared(shape, cache, share, idx_q, block_scores, stream=None):
+    _check(lib().msa_indexer_score_shared(ctypes.byref(shape), ctypes.byref(cache), ctypes.byref(share), _ptr(idx_q),
+                                          _ptr(block_scores), _stream(stream)), "msa_indexer_score_shared")
+
+
+def msa_decode_shared(shape, cache, share, q, idx_q, out, sel_blocks, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().msa_decode_shared(ctypes.byref(shape), ctypes.byref(cache), ctypes.byref(share), _ptr(q),
+                                   _ptr(idx_q), _ptr(out), _ptr(sel_blocks), _ptr(workspace), nbytes,
+                                   _stream(stream)), "msa_decode_shared")
 
 
 def msa_kv_insert(shape, cache, k_new, v_new, idx_new, stream=None):

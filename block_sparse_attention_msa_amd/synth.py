@@ -113,6 +113,12 @@ class Workload:
     seq_lens: torch.Tensor
     meta: dict = field(default_factory=dict)
     idx_sf: Optional[torch.Tensor] = None   # NVFP4 index keys: E4M3 group scales [P][128][8]
+    # prefix sharing (None without): int32 [groups][8] member sequence ids
+    # (-1 padded, the first is the leader whose pages the members share),
+    # int32 [groups] shared leading blocks, int32 [S] per-sequence shared blocks
+    share_members: Optional[torch.Tensor] = None
+    share_blocks: Optional[torch.Tensor] = None
+    seq_shared_blocks: Optional[torch.Tensor] = None
 
     @property
     def rows(self) -> int:
@@ -146,6 +152,10 @@ class Workload:
         b_idx = IDX_BYTES_PER_TOKEN[self.idx_dtype]
         b_kv_tok = DIM * (0.5 + 1.0 / 16) if self.kv_dtype == "nvfp4" else DIM * 2.0
         scan = sum(lens) * b_idx
+        if self.seq_shared_blocks is not None:  # a shared page's keys are read once for its group
+            ssb = [int(x) for x in self.seq_shared_blocks.cpu().tolist()]
+            leaders = set(int(m[0]) for m in self.share_members.cpu().tolist())
+            scan -= sum(ssb[b] * BLOCK * b_idx for b in range(len(lens)) if b not in leaders)
         gather = 0.0
         table = 0
         if sel is not None:
@@ -173,7 +183,7 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
                   idx_dist: str = "normal", shared_bias_iq: bool = False, seed: int = 0,
                   device="cpu", num_q_heads: int = 16, num_kv_heads: int = 4,
                   sm_scale: Optional[float] = None, idx_scale: float = 1.0,
-                  kv_chunk_pages: int = 1024) -> Workload:
+                  kv_chunk_pages: int = 1024, share: Optional[tuple] = None) -> Workload:
     """Seeded synthetic workload.
 
     seq_lens: visible tokens per sequence (including the q_len new tokens);
@@ -187,6 +197,10 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     unit direction added.  idx_dist: "normal" N(0,1) or "uniform" U(-1,1).
     shared_bias_iq: (q_len > 1) index queries are u_{b,g} + N(0,1), with u the
     bias direction shared by the chunk.
+    share (group_size, shared_blocks): consecutive sequences form groups of
+    group_size (at most 8) whose first shared_blocks logical blocks map to the
+    leader's (the group's first sequence's) pages: a shared prefix, keys and
+    K/V included.  Every member must see all shared tokens.
     Index-key rows past a sequence's end are filled with a poison value that
     scores high, so an unmasked tail would show up in the selection.
     """
@@ -198,7 +212,23 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     mbps = max_blocks_per_seq if max_blocks_per_seq is not None else max([1] + nbs)
     assert all(nb <= mbps for nb in nbs)
     assert all(L == 0 or L >= q_len for L in seq_lens)
-    P = sum(nbs) + spare_pages
+    # ---- prefix sharing: owned[b] = first logical block with a page of b's own
+    owned = [0] * S
+    groups = []
+    if share is not None:
+        gsize, sblocks = int(share[0]), int(share[1])
+        assert 1 <= gsize <= 8 and sblocks >= 0
+        for g0 in range(0, S, gsize):
+            members = list(range(g0, min(S, g0 + gsize)))
+            if len(members) < 2:  # a group of one shares nothing
+                continue
+            for b in members:
+                assert seq_lens[b] == 0 or sblocks * BLOCK <= seq_lens[b] - q_len + 1, "shared tokens must be visible"
+                assert seq_lens[b] > 0, "padded rows cannot share"
+            groups.append(members)
+            for b in members[1:]:
+                owned[b] = sblocks
+    P = sum(nb - o for nb, o in zip(nbs, owned)) + spare_pages
     P = max(P, 1)
     rows = S * q_len
 
@@ -211,8 +241,12 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     bt = torch.zeros(S, mbps, dtype=torch.int32)
     off = 0
     for b, nb in enumerate(nbs):
-        bt[b, :nb] = perm[off:off + nb].to(torch.int32)
-        off += nb
+        n_own = nb - owned[b]
+        bt[b, owned[b]:nb] = perm[off:off + n_own].to(torch.int32)
+        off += n_own
+    for members in groups:
+        for b in members[1:]:
+            bt[b, :owned[b]] = bt[members[0], :owned[b]]
 
     # ---- queries
     gq = _gen(dev, seed * 7919 + 2)
@@ -273,18 +307,21 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
         idx_pool = torch.zeros(P, BLOCK, DIM // 2, dtype=torch.uint8, device=dev)
         idx_sf = torch.zeros(P, BLOCK, DIM // 16, dtype=torch.uint8, device=dev)
         for b, keys in index_keys():
-            pages = bt[b, :nbs[b]].long().to(dev)
-            idx_pool[pages], idx_sf[pages] = quant_nvfp4(keys, idx_gs)
+            o = owned[b]
+            pages = bt[b, o:nbs[b]].long().to(dev)
+            idx_pool[pages], idx_sf[pages] = quant_nvfp4(keys[o:], idx_gs)
         idx_scale = idx_scale * idx_gs
     elif idx_dtype in ("fp8", "bf16"):
         bidx = 1 if idx_dtype == "fp8" else 2
         idx_pool = torch.zeros(P, BLOCK, DIM * bidx, dtype=torch.uint8, device=dev)
         for b, keys in index_keys():
+            o = owned[b]
+            keys = keys[o:]
             if idx_dtype == "fp8":
                 kb = quant_e4m3(keys)
             else:
-                kb = keys.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(nbs[b], BLOCK, DIM * 2)
-            idx_pool[bt[b, :nbs[b]].long().to(dev)] = kb
+                kb = keys.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(nbs[b] - o, BLOCK, DIM * 2)
+            idx_pool[bt[b, o:nbs[b]].long().to(dev)] = kb
         if idx_dtype == "bf16":
             idx_pool = idx_pool.view(torch.bfloat16).reshape(P, BLOCK, DIM)
     else:
@@ -325,8 +362,24 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
                     q=q, iq=iq, idx_k=idx_pool, k=k, v=v, k_sf=k_sf, v_sf=v_sf,
                     block_table=bt.to(dev), seq_lens=torch.tensor(seq_lens, dtype=torch.int32, device=dev),
                     meta=dict(seed=seed, layout=layout, plant=plant, zipf=zipf, idx_dist=idx_dist,
-                              planted=planted),
-                    idx_sf=idx_sf)
+                              planted=planted, share=share),
+                    idx_sf=idx_sf, **_share_tensors(groups, share, S, dev))
+
+
+def _share_tensors(groups, share, S, dev) -> dict:
+    """The prefix-sharing descriptors of make_workload(share=...)."""
+    if share is None:
+        return {}
+    members = torch.full((len(groups), 8), -1, dtype=torch.int32)
+    for gi, mem in enumerate(groups):
+        members[gi, :len(mem)] = torch.tensor(mem, dtype=torch.int32)
+    sblocks = int(share[1])
+    per_seq = torch.zeros(S, dtype=torch.int32)
+    for mem in groups:
+        per_seq[mem] = sblocks
+    return dict(share_members=members.to(dev),
+                share_blocks=torch.full((len(groups),), sblocks, dtype=torch.int32, device=dev),
+                seq_shared_blocks=per_seq.to(dev))
 
 
 # The five workloads the method is evaluated on.  Every config uses 4 KV heads
@@ -350,6 +403,10 @@ CONFIGS = {
     # context plus 4 new query tokens (1 + 3 draft tokens, the draft length of
     # the AMD serving recipe); not one of the five above
     "spec_b32_q4_128k": dict(seq_lens=[131072 + 4] * 32, q_len=4, zipf=1.1, layout="paged", seed=5),
+    # batch 32 x 128K in groups of 8 sequences sharing a 96K-token prefix
+    # (768 blocks: system prompt and agent context), own 32K each; not one of
+    # the five above
+    "shared_b32_128k": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", share=(8, 768), seed=6),
     # the same with the index cache in NVFP4: the AMD serving setting of the
     # pages (NVFP4 indexer cache and 3 draft tokens)
     "spec_b32_q4_128k_nvfp4_idx": dict(seq_lens=[131072 + 4] * 32, q_len=4, zipf=1.1, layout="paged",

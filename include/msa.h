@@ -185,6 +185,41 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
 msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const void* k_new, const void* v_new,
                          const void* idx_new, hipStream_t stream);
 
+/* Prefix sharing ("NVFP4 MSA kernel" of the vLLM MiniMax-M3.1-Flash post: a
+ * shared-prefix page is dequantised once for up to 64 requests that share
+ * it; here the index scan reads such a page once for the group's members and
+ * scores it against all their index queries).  Sequences form sharing groups
+ * of at most MSA_SHARE_MAX; in a group, the first shared_blocks[g] logical
+ * blocks of every member map to the same physical pages as the first
+ * member's (its leader's) block_table row.  Device arrays, read by the
+ * kernels, unchecked like seq_lens (preconditions):
+ *   members           int32 [num_groups][MSA_SHARE_MAX] sequence ids, -1 padded
+ *                     after the last member; a sequence is in at most one group
+ *   shared_blocks     int32 [num_groups], each 0 ..
+ *                     (seq_lens[b] - q_len + 1) / 128 for every member b: every
+ *                     shared token is visible to the member's query
+ *   seq_shared_blocks int32 [num_seqs]: shared_blocks of the sequence's group,
+ *                     0 for a sequence in no group
+ * num_groups 0 means no sharing (the arrays may then be NULL).  Block scores,
+ * selection and outputs equal those of the unshared calls bit for bit. */
+#define MSA_SHARE_MAX 8
+typedef struct {
+  int32_t num_groups;
+  const int32_t* members;
+  const int32_t* shared_blocks;
+  const int32_t* seq_shared_blocks;
+} msa_prefix_share;
+
+/* msa_indexer_score and msa_decode with prefix sharing (one scan launch that
+ * scores each group's shared blocks once and every sequence's own blocks).
+ * Supported for q_len 1 with FP8 index keys (MSA_ERR_UNSUPPORTED otherwise);
+ * other arguments as in the unshared calls. */
+msa_status msa_indexer_score_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
+                                    const void* idx_q, float* block_scores, hipStream_t stream);
+msa_status msa_decode_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
+                             const void* q, const void* idx_q, float* out, int32_t* sel_blocks, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 const char* msa_status_string(msa_status status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* msa_last_error(void);

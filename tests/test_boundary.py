@@ -103,6 +103,30 @@ def test_nvfp4_index_keys_validation():
     assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=8))) > 0
 
 
+def test_prefix_share_validation():
+    """The shared entry points: a NULL descriptor, a negative group count or a
+    missing array is INVALID_ARGUMENT; sharing beyond q_len 1 or FP8 index
+    keys is UNSUPPORTED; zero groups behaves as the unshared call (which then
+    reaches its own checks: here the short workspace)."""
+    L = msa.lib()
+    s = _shape()
+    sh = msa.MsaPrefixShare(2, FAKE, FAKE, FAKE)
+
+    def dec(shape, share, nbytes=1 << 30):
+        return L.msa_decode_shared(ctypes.byref(shape), ctypes.byref(_cache()), share, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   nbytes, None)
+
+    assert dec(s, None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert dec(s, ctypes.byref(msa.MsaPrefixShare(-1, FAKE, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert dec(s, ctypes.byref(msa.MsaPrefixShare(2, None, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert "members" in msa.last_error()
+    assert dec(_shape(q_len=2), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
+    assert dec(_shape(idx_dtype=msa.MSA_IDX_BF16), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
+    assert dec(s, ctypes.byref(msa.MsaPrefixShare(0, None, None, None)), nbytes=16) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert L.msa_indexer_score_shared(ctypes.byref(s), ctypes.byref(_cache()), None, FAKE, FAKE, None) == \
+        msa.MSA_ERR_INVALID_ARGUMENT
+
+
 def test_kv_insert_validation():
     """msa_kv_insert validates like the other entry points, before any HIP call."""
     L = msa.lib()

@@ -346,6 +346,58 @@ def test_decode_without_selected_ids_output(dev, q_len):
         check_row(P, row, o[row], s_[row])
 
 
+@pytest.mark.parametrize("group,shared", [(8, 20), (3, 7), (2, 0)])
+def test_prefix_sharing_matches_unshared(dev, group, shared):
+    """Prefix sharing (groups whose first blocks map to the leader's pages):
+    the shared scan's block scores, the selection and the outputs equal the
+    unshared calls' bit for bit (each MFMA column is computed alone), and
+    sampled rows match the oracle.  Ragged lengths, a last group shorter than
+    the others, and shared = 0 (groups that share nothing)."""
+    msa = _msa()
+    lens = [2600, 9000, 4000, 2561, 7000, 3333, 5000, 2700, 6000, 2900, 4400]
+    w = synth.make_workload(seq_lens=lens, share=(group, shared), zipf=1.1, layout="paged", seed=80 + group,
+                            device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_workload(w)
+    bs1 = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    bs2 = torch.full_like(bs1, float("nan"))
+    msa.msa_indexer_score(shape, cache, w.iq, bs1)
+    msa.msa_indexer_score_shared(shape, cache, share, w.iq, bs2)
+    out1, sel1 = msa.alloc_outputs(w)
+    out2, sel2 = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out1, sel1, ws)
+    msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out2, sel2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bs1, bs2)
+    assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
+    P = oracle.Problem.from_workload(w)
+    o, s_, b_ = out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy()
+    for row in (0, 1, 7, 8, 10):
+        check_row(P, row, o[row], s_[row], b_[row])
+
+
+def test_shared_b32_128k_config_sampled(dev):
+    """Batch 32 x 128K in groups of 8 sharing a 96K prefix, through the shared
+    path in the bench's launch configuration: bit-equal to the unshared path
+    and sampled rows checked against the oracle."""
+    msa = _msa()
+    w = synth.make_config("shared_b32_128k", device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_workload(w)
+    out1, sel1 = msa.alloc_outputs(w)
+    out2, sel2 = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out1, sel1, ws)
+    msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out2, sel2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
+    P = oracle.Problem.from_workload(w)
+    o, s_ = out2.cpu().numpy(), sel2.cpu().numpy()
+    for row in (0, 7, 8, 31):
+        check_row(P, row, o[row], s_[row])
+
+
 def test_graph_capture_replays(dev):
     """msa_decode captured in a HIP graph: every replay (with eager work and
     synchronisation in between) equals the eager result bit for bit."""
