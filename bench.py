@@ -66,6 +66,58 @@ def scan_flops(w) -> float:
     return 2.0 * 128 * total
 
 
+CEILING_LIB = os.path.join(ROOT, "block_sparse_attention_msa_amd", "libmsa_ceiling.so")
+
+
+def read_ceiling(w, copies, stream, steps: int, warmup: int):
+    """The practical HBM ceiling of the index scan on this machine: a read-only
+    kernel (libmsa_ceiling.so) walks the same index-key pages through the same
+    block table with the scan's load pattern and computes nothing.  Returns
+    (us per launch, bytes read per launch), or None where the scan is not a
+    page stream (more than 8 query rows per sequence: the multi-query scan)."""
+    import ctypes
+    import torch
+    if w.q_len > 8:
+        return None
+    kb0, kb1 = {"fp8": (16, 0), "bf16": (32, 0), "nvfp4": (8, 1)}[w.idx_dtype]
+    lib = ctypes.CDLL(CEILING_LIB)
+    fn = lib.msa_ceiling_read_pages
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lens = [int(x) for x in w.seq_lens.cpu().tolist()]
+    first = [0] * w.num_seqs
+    if w.seq_shared_blocks is not None:  # a shared page once, by its group's leader
+        leaders = set(int(m[0]) for m in w.share_members.cpu().tolist())
+        first = [0 if b in leaders else int(x) for b, x in enumerate(w.seq_shared_blocks.cpu().tolist())]
+    first_t = torch.tensor(first, dtype=torch.int32, device=w.seq_lens.device)
+    pages = sum(max(0, min((L + 127) // 128, w.max_blocks_per_seq) - f) for L, f in zip(lens, first))
+    sink = torch.zeros(1, dtype=torch.int32, device=w.seq_lens.device)
+    for c in copies:  # the pools hold exactly kb0 (kb1) KiB per page
+        assert c.idx_k.is_contiguous() and c.idx_k.numel() * c.idx_k.element_size() == w.num_pages * kb0 * 1024
+        assert kb1 == 0 or c.idx_sf.numel() * c.idx_sf.element_size() == w.num_pages * kb1 * 1024
+        assert tuple(c.block_table.shape) == (w.num_seqs, w.max_blocks_per_seq) and c.block_table.is_contiguous()
+
+    def launch(i):
+        c = copies[i % len(copies)]
+        rc = fn(c.idx_k.data_ptr(), kb0, c.idx_sf.data_ptr() if kb1 else None, kb1, c.block_table.data_ptr(),
+                c.seq_lens.data_ptr(), first_t.data_ptr(), w.num_seqs, w.max_blocks_per_seq, sink.data_ptr(),
+                stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"msa_ceiling_read_pages failed: {rc}")
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3, pages * (kb0 + kb1) * 1024
+
+
 def clone_workload(w):
     import copy
     w2 = copy.copy(w)
@@ -276,6 +328,19 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     us_step = ms_per_step * 1e3
 
+    # spread of single steps (a second pass with an event pair per step; the
+    # reported value is the one above, over the K steps as a whole)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+
+    def pct(p):
+        return round(per_step[min(len(per_step) - 1, int(p / 100.0 * len(per_step)))], 2)
+
     # dominant kernel: the index scan alone, same launch configuration, same rotation
     bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
     for i in range(args.warmup):
@@ -289,6 +354,8 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     scan_us = e0.elapsed_time(e1) / args.steps * 1e3
+
+    ceiling = read_ceiling(w, copies, stream, args.steps, args.warmup)
 
     # the write side of the step, timed apart: the new tokens' K/V/index keys
     # quantised into the pools (msa_kv_insert; not part of `value`)
@@ -345,6 +412,14 @@ def main():
                     "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                     "launch_us": round(scan_us, 2), "algorithmic_flops": int(fl)}
+    read_ceil = None
+    if ceiling is not None:
+        c_us, c_bytes = ceiling
+        read_ceil = {"kernel": "read-only walk of the scan's index pages, same block table and load pattern",
+                     "us": round(c_us, 2), "bytes": int(c_bytes), "GBps": round(c_bytes / (c_us * 1e-6) / 1e9, 1),
+                     "scan_us_over_ceiling_us": round(scan_us / c_us, 4)}
+        log(f"[bench] read ceiling {c_us:.1f} us ({read_ceil['GBps']:.0f} GB/s, {c_bytes / 1e6:.1f} MB): "
+            f"the scan takes {scan_us / c_us:.3f}x the pure read of its pages")
     if fl:
         log(f"[bench] multi-query scan {fl / 1e9:.1f} GFLOP, {fl / (scan_us * 1e-6) / 1e12:.0f} TFLOP/s, "
             f"{'mfma' if mfma_bound else 'hbm'}-bound")
@@ -376,7 +451,9 @@ def main():
         "bytes_per_step": int(nb["total"]),
         "bytes_per_ctx_token": round(per_tok, 1),
         "vs_dense_fp8_kv_per_token": round(per_tok / 1024.0, 4),
+        "step_us_p10_p50_p90": [pct(10), pct(50), pct(90)],
         "roofline": roofline,
+        "read_ceiling": read_ceil,
         "cpu_baseline": cpu,
         "kv_insert_us": None if insert_us is None else round(insert_us, 2),
     }

@@ -175,3 +175,22 @@ def test_other_entry_points_validate():
                                     None) == msa.MSA_ERR_INVALID_ARGUMENT
     for st in range(5):
         assert msa.status_string(st).startswith("MSA_")
+
+
+def test_read_ceiling_library_exports_and_validates():
+    """The benchmark's read-ceiling kernel library (not part of the MSA path)
+    loads, exports its entry point and rejects bad arguments before any HIP
+    call."""
+    path = os.path.join(os.path.dirname(msa.LIB_PATH), "libmsa_ceiling.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.msa_ceiling_read_pages
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+    assert fn(None, 16, None, 0, fake, fake, None, 1, 1, fake, None) == -1       # no pool
+    assert fn(fake, 16, fake, 0, fake, fake, None, 1, 1, fake, None) == -1       # pool1 without kb1
+    assert fn(fake, 8, None, 1, fake, fake, None, 1, 1, fake, None) == -1        # kb1 without pool1
+    assert fn(fake, 12, None, 0, fake, fake, None, 1, 1, fake, None) == -1       # unsupported page size
+    assert fn(fake, 16, None, 0, fake, fake, None, 0, 1, fake, None) == -1       # no sequences
+    assert fn(fake, 16, None, 0, fake, fake, None, 70000, 1, fake, None) == -1   # grid rows past 65535
