@@ -359,21 +359,19 @@ def main():
 
     # the write side of the step, timed apart: the new tokens' K/V/index keys
     # quantised into the pools (msa_kv_insert; not part of `value`)
-    insert_us = None
-    if w.idx_dtype != "nvfp4" or w.q_len <= 8:
-        gi = torch.Generator(device=dev).manual_seed(11)
-        k_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
-        v_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
-        x_new = torch.randn(w.rows, 128, generator=gi, device=dev).to(torch.bfloat16)
-        for i in range(args.warmup):
-            msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        insert_us = e0.elapsed_time(e1) / args.steps * 1e3
+    gi = torch.Generator(device=dev).manual_seed(11)
+    k_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
+    v_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
+    x_new = torch.randn(w.rows, 128, generator=gi, device=dev).to(torch.bfloat16)
+    for i in range(args.warmup):
+        msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    insert_us = e0.elapsed_time(e1) / args.steps * 1e3
 
     nb = w.nbytes_algorithmic(sel if w.q_len > 1 else None)
     step_gbps = nb["total"] / (us_step * 1e-6) / 1e9

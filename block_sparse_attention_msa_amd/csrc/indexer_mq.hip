@@ -17,9 +17,11 @@
 //    rows' bf16 index queries, 8 K steps) are staged through LDS once and then
 //    stay in 32 VGPRs for the whole range.
 //  * The 8 waves walk their blocks together.  A block's keys (16 KB FP8, 32
-//    KB bf16) are loaded by all waves in contiguous 1 KB wave-loads two blocks
-//    ahead into registers, converted once per workgroup to bf16 (E4M3 ->
-//    bf16, exact) and written to one of two 32 KB LDS buffers with a swizzle
+//    KB bf16, 8 KB of NVFP4 codes + 1 KB of group scales) are loaded by all
+//    waves in contiguous 1 KB wave-loads two blocks ahead into registers,
+//    converted once per workgroup to bf16 (E4M3 -> bf16; E2M1 code x E4M3
+//    group scale, at most 6 significant bits; both exact) and written to one
+//    of two 32 KB LDS buffers with a swizzle
 //    (16-B chunk k of token t at t * 256 + 16 (k ^ (t mod 16))), so that both
 //    the row writes and the MFMA-layout reads are free of bank conflicts; one
 //    barrier per block.
@@ -49,16 +51,19 @@ constexpr int kLdsRow = kDim * 2 + 16;             // bf16 row + 16 B pad
 // MFMA 32x32x16 bf16 lane layout (gfx950): lane l supplies A[l%32][8(l/32)+e]
 // and B[8(l/32)+e][l%32], e = 0..7; result register q of lane l holds
 // D[8(q/4) + 4(l/32) + q%4][l%32].
-template <bool FP8>
+template <int FMT>
 __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __restrict__ idx_pool,
+                                                             const uint8_t* __restrict__ idx_sf,
                                                              const int32_t* __restrict__ block_table,
                                                              const int32_t* __restrict__ seq_lens,
                                                              const uint16_t* __restrict__ iq,
                                                              float* __restrict__ block_scores, int q_len, int mbps,
                                                              int nchunks, int wgs, float idx_scale) {
-  constexpr int kKeyRow = FP8 ? kDim : kDim * 2;      // bytes per token of an index-key page
-  constexpr int kPage = kBlock * kKeyRow;             // 16 KB or 32 KB
-  constexpr int kLoads = kPage / 1024 / kMqWaves;     // 1 KB wave-loads per wave and block (2 or 4)
+  // bytes per token of an index-key page: E4M3, bf16, or E2M1 codes (NVFP4,
+  // whose 8 group scales per token sit in idx_sf, 1 KB per page)
+  constexpr int kKeyRow = FMT == kIdxFp8 ? kDim : FMT == kIdxBf16 ? kDim * 2 : kDim / 2;
+  constexpr int kPage = kBlock * kKeyRow;             // 16, 32 or 8 KB
+  constexpr int kLoads = kPage / 1024 / kMqWaves;     // 1 KB wave-loads per wave and block (2, 4 or 1)
   constexpr int kRowB = kDim * 2;                     // bytes per token of a bf16 key row in LDS
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[kRowChunk * kLdsRow];     // 68 KB
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kBlock * kRowB];       // 2 x 32 KB, bf16 keys
@@ -107,24 +112,53 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
   // block j is seen by some row of the chunk (wave-uniform)
   auto seen = [&](int j) { return j < nb && (long long)j * kBlock <= pos_max; };
   // this wave's share of block j's keys: kLoads contiguous 1 KB wave-loads
-  auto load_keys = [&](int j, u32x4 (&v)[kLoads]) {
+  // (NVFP4: plus the two group scales of the lane's 32 dims, 2 bytes)
+  auto load_keys = [&](int j, u32x4 (&v)[kLoads], uint32_t& sf) {
     if (j < jend && seen(j)) {
-      const uint8_t* src = idx_pool + (int64_t)bt_row[j] * kPage + (size_t)(wave * kLoads) * 1024 + lane * 16;
+      const int64_t page = bt_row[j];
+      const uint8_t* src = idx_pool + page * kPage + (size_t)(wave * kLoads) * 1024 + lane * 16;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i * 1024));
+      if constexpr (FMT == kIdxNvfp4) {
+        const int byte = wave * 1024 + lane * 16;  // token byte / 64, dims 32 ((byte % 64) / 16) ..
+        sf = *reinterpret_cast<const uint16_t*>(idx_sf + page * (kBlock * 8) + (byte / 64) * 8 + ((byte % 64) / 16) * 2);
+      }
     }
   };
-  // ... written to LDS buffer buf as bf16 (E4M3 -> bf16 exact, converted
-  // once per workgroup), swizzled: 16-B chunk k (dims 8k .. 8k + 7) of token t
-  // at t * 256 + 16 (k ^ (t mod 16))
+  // ... written to LDS buffer buf as bf16 (exact, converted once per
+  // workgroup), swizzled: 16-B chunk k (dims 8k .. 8k + 7) of token t at
+  // t * 256 + 16 (k ^ (t mod 16))
   auto lds_chunk = [&](int buf, int t, int k) { return &lds_k[buf][t * kRowB + ((k ^ (t & 15)) << 4)]; };
-  auto store_keys = [&](int j, int buf, const u32x4 (&v)[kLoads]) {
+  auto store_keys = [&](int j, int buf, const u32x4 (&v)[kLoads], uint32_t sf) {
     if (j < jend && seen(j)) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int byte = (wave * kLoads + i) * 1024 + lane * 16;  // offset in the page
         const int t = byte / kKeyRow, k = (byte % kKeyRow) / 16;  // token, 16-B chunk of the stored row
-        if constexpr (FP8) {  // 16 dims -> bf16 chunks 2k, 2k + 1
+        if constexpr (FMT == kIdxNvfp4) {  // 32 dims (groups 2k, 2k + 1) -> bf16 chunks 4k .. 4k + 3
+          const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          const float s0 = e4m3_to_f32(sf & 0xFFu), s1 = e4m3_to_f32((sf >> 8) & 0xFFu);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {  // dims 32k + 8q .. + 7, group 2k + q / 2
+            const float sc = q < 2 ? s0 : s1;
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              f32x2 x;
+              switch (e) {
+                case 0: x = e2m1x2_to_f32x2<0>(d[q]); break;
+                case 1: x = e2m1x2_to_f32x2<1>(d[q]); break;
+                case 2: x = e2m1x2_to_f32x2<2>(d[q]); break;
+                default: x = e2m1x2_to_f32x2<3>(d[q]); break;
+              }
+              // code x scale: at most 6 significant bits, so the product and
+              // its bf16 conversion are exact
+              const bf16x2 y = {(__bf16)(x.x * sc), (__bf16)(x.y * sc)};
+              o[e] = __builtin_bit_cast(uint32_t, y);
+            }
+            *reinterpret_cast<u32x4*>(lds_chunk(buf, t, 4 * k + q)) = u32x4{o[0], o[1], o[2], o[3]};
+          }
+        } else if constexpr (FMT == kIdxFp8) {  // 16 dims -> bf16 chunks 2k, 2k + 1
           const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
           uint32_t o[8];
 #pragma unroll
@@ -142,14 +176,15 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
   };
 
   u32x4 pf1[kLoads], pf2[kLoads];  // keys of blocks j + 1 and j + 2, in flight
-  load_keys(jbeg, pf1);
-  store_keys(jbeg, 0, pf1);
-  load_keys(jbeg + 1, pf1);
+  uint32_t sf1 = 0, sf2 = 0;       // their group scales (NVFP4)
+  load_keys(jbeg, pf1, sf1);
+  store_keys(jbeg, 0, pf1, sf1);
+  load_keys(jbeg + 1, pf1, sf1);
   __syncthreads();
 #pragma unroll 1
   for (int j = jbeg; j < jend; ++j) {  // wave-uniform
     const int buf = (j - jbeg) & 1;
-    load_keys(j + 2, pf2);
+    load_keys(j + 2, pf2, sf2);
     if (!seen(j)) {  // no row of the chunk sees this block
       if (active && h == 0 && r < crow) bs[(size_t)r * mbps + j] = -INFINITY;
     } else if (active) {
@@ -182,9 +217,10 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
     }
     // the next block's keys into the other buffer (read by nobody since the
     // last barrier), then the barrier that publishes them
-    store_keys(j + 1, buf ^ 1, pf1);
+    store_keys(j + 1, buf ^ 1, pf1, sf1);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) pf1[i] = pf2[i];
+    sf1 = sf2;
     __syncthreads();
   }
 }
@@ -200,14 +236,16 @@ hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream) {
   const int cus = device_cus();
   const int wgs = (int)(groups >= cus ? 1 : cus / groups);
   dim3 grid((unsigned)(groups * wgs));
+  const uint8_t* pool = static_cast<const uint8_t*>(a.idx_pool);
   if (a.idx_fmt == kIdxFp8)
-    scan_mq_kernel<true><<<grid, kMqThreads, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                           a.seq_lens, a.iq, a.block_scores, q_len, a.mbps, nchunks, wgs,
-                                                           a.idx_scale);
+    scan_mq_kernel<kIdxFp8><<<grid, kMqThreads, 0, stream>>>(pool, nullptr, a.block_table, a.seq_lens, a.iq,
+                                                              a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale);
+  else if (a.idx_fmt == kIdxNvfp4)
+    scan_mq_kernel<kIdxNvfp4><<<grid, kMqThreads, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
+                                                                a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale);
   else
-    scan_mq_kernel<false><<<grid, kMqThreads, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                            a.seq_lens, a.iq, a.block_scores, q_len, a.mbps, nchunks, wgs,
-                                                            a.idx_scale);
+    scan_mq_kernel<kIdxBf16><<<grid, kMqThreads, 0, stream>>>(pool, nullptr, a.block_table, a.seq_lens, a.iq,
+                                                               a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale);
   return hipGetLastError();
 }
 

@@ -51,8 +51,6 @@ msa_status check_shape(const msa_shape* s) {
     return fail(MSA_ERR_UNSUPPORTED, "kv_dtype = %d", s->kv_dtype);
   if (s->idx_dtype != MSA_IDX_BF16 && s->idx_dtype != MSA_IDX_FP8_E4M3 && s->idx_dtype != MSA_IDX_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "idx_dtype = %d", s->idx_dtype);
-  if (s->idx_dtype == MSA_IDX_NVFP4 && s->q_len > 8)
-    return fail(MSA_ERR_UNSUPPORTED, "NVFP4 index keys with q_len = %d (supported for q_len <= 8)", s->q_len);
   if (!finite_pos(s->sm_scale) || !finite_pos(s->k_scale) || !finite_pos(s->v_scale) || !finite_pos(s->idx_scale))
     return fail(MSA_ERR_INVALID_ARGUMENT, "scales must be finite and > 0 (sm %g, k %g, v %g, idx %g)",
                 (double)s->sm_scale, (double)s->k_scale, (double)s->v_scale, (double)s->idx_scale);
@@ -128,7 +126,7 @@ msa::ScanArgs scan_args(const msa_shape* s, const msa_cache* c, const void* idx_
 // q_len == 1: the decode scan; FP8 or NVFP4 index keys with q_len <= 8: pages
 // streamed by waves with the few (query, group) columns on MFMA; otherwise
 // the multi-query scan (query rows staged in LDS, keys streamed per row
-// chunk; FP8 or bf16 keys).
+// chunk and converted to bf16 once per workgroup).
 hipError_t launch_scan(const msa_shape* s, const msa::ScanArgs& a, hipStream_t stream) {
   if (s->q_len == 1) return msa::launch_scan_decode(a, stream);
   if (a.idx_fmt != msa::kIdxBf16 && s->q_len <= 8) return msa::launch_scan_cols(a, s->q_len, stream);

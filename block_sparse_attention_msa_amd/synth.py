@@ -411,6 +411,10 @@ CONFIGS = {
     # pages (NVFP4 indexer cache and 3 draft tokens)
     "spec_b32_q4_128k_nvfp4_idx": dict(seq_lens=[131072 + 4] * 32, q_len=4, zipf=1.1, layout="paged",
                                        idx_dtype="nvfp4", seed=5),
+    # the multi-query verify chunk with the index cache in NVFP4; not one of
+    # the five above
+    "verify_b2_q256_128k_nvfp4_idx": dict(seq_lens=[131072 + 256] * 2, q_len=256, zipf=1.1, layout="paged",
+                                          shared_bias_iq=True, idx_dtype="nvfp4", seed=4),
     # the batch-32 x 128K shape with the index cache in NVFP4 (72 B per token
     # instead of 128 B), the M3.1 production setting; not one of the five above
     "paged_b32_128k_nvfp4_idx": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", idx_dtype="nvfp4",

@@ -40,8 +40,7 @@
  *           M3.1 post: the index cache in NVFP4, 72 B per token): uint8
  *           [num_pages][128 tokens][64] (element 2i in the low nibble of byte
  *           i, E2M1) plus idx_sf uint8 E4M3 [num_pages][128 tokens][8];
- *           value = e2m1 x scale x idx_scale.  NVFP4 index keys are
- *           supported for q_len <= 8 (MSA_ERR_UNSUPPORTED otherwise).
+ *           value = e2m1 x scale x idx_scale.
  *  - k, v   NVFP4: uint8 [num_pages][num_kv_heads][128 tokens][64], element 2i
  *           in the low nibble of byte i (E2M1), plus k_sf / v_sf uint8 E4M3
  *           [num_pages][num_kv_heads][128 tokens][8] (one scale per 16

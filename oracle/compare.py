@@ -62,7 +62,7 @@ def score_abs_bound(P, row):
     if L == 0:
         return out
     A = (ik[:L].abs() @ iq.abs().T) * P.idx_scale              # [L, G]
-    if P.arrays.get("idx_sf") is not None and P.q_len > 1:
+    if P.arrays.get("idx_sf") is not None and 1 < P.q_len <= 8:  # the f16 column scan
         A = A * (2.0 * 130.0 * 2.0 ** -24) + (ik[:L].abs() @ f16_query_rounding(iq).T) * P.idx_scale
     else:
         A = A * (2.0 * 130.0 * 2.0 ** -24)

@@ -94,12 +94,12 @@ def test_null_and_pointer_validation():
 
 
 def test_nvfp4_index_keys_validation():
-    """NVFP4 index keys need their scale array and are supported for q_len <= 8."""
+    """NVFP4 index keys need their scale array; every q_len takes them."""
     s = _shape(idx_dtype=msa.MSA_IDX_NVFP4)
     assert _decode(s, cache=_cache(idx_sf=None)) == msa.MSA_ERR_INVALID_ARGUMENT
     assert "idx_sf" in msa.last_error()
-    assert _decode(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=9)) == msa.MSA_ERR_UNSUPPORTED
-    assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=9))) == 0
+    assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=9))) > 0
+    assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=256))) > 0
     assert msa.lib().msa_workspace_size(ctypes.byref(_shape(idx_dtype=msa.MSA_IDX_NVFP4, q_len=8))) > 0
 
 

@@ -257,11 +257,13 @@ def test_multi_query_causal(dev, kv, idx, q_len):
     assert (out[pad:pad + q_len] == 0).all() and (sel[pad:pad + q_len] == -1).all()
 
 
-@pytest.mark.parametrize("q_len", [2, 4, 5, 8])
+@pytest.mark.parametrize("q_len", [2, 4, 5, 8, 9, 64, 80])
 def test_multi_query_nvfp4_index_keys(dev, q_len):
-    """NVFP4 index keys with a few query tokens (speculative verify): the keys
-    are dequantised exactly to bf16 for the MFMA column scan; the cases of the
-    multi-query test."""
+    """NVFP4 index keys with several query tokens: q_len 2-8 (speculative
+    verify) take the f16 column scan; longer chunks the multi-query scan, which
+    dequantises each page exactly to bf16 in LDS (its block scores held to the
+    exact-product bound, with no query-rounding term).  The cases of the
+    multi-query test, q_len 80 with a partial second 256-row chunk."""
     lens = [q_len, q_len + 1, 127 + q_len, 2177, 0, 16 * 128 + q_len, 5000]
     w = synth.make_workload(seq_lens=lens, q_len=q_len, kv_dtype="nvfp4", idx_dtype="nvfp4", plant=3,
                             layout="paged", seed=60 + q_len, device=dev, max_blocks_per_seq=48)
@@ -302,6 +304,26 @@ def test_verify_b2_q256_128k_config_sampled(dev):
     """The multi-query verify chunk: 2 sequences x 256 new tokens on 128K."""
     w = synth.make_config("verify_b2_q256_128k", device=dev)
     check_workload(w, rows=[0, 1, 2, 130, 255, 256, 300, 511])
+
+
+def test_verify_b2_q256_128k_nvfp4_index_sampled(dev):
+    """The multi-query verify chunk with the index cache in NVFP4, sampled rows."""
+    w = synth.make_config("verify_b2_q256_128k_nvfp4_idx", device=dev)
+    check_workload(w, rows=[0, 2, 255, 256, 383, 511])
+
+
+def test_multi_query_nvfp4_extreme_index_queries_long_chunk(dev):
+    """NVFP4 index keys, q_len 12 (the multi-query scan): index queries with
+    elements 2^-30 below their vector's largest and queries of magnitude 1e6;
+    with keys dequantised to bf16 every product stays exact, so the exact-product
+    bound holds with no rounding term."""
+    w = synth.make_workload(seq_lens=[4000, 2177, 0, 16 * 128 + 12], q_len=12, kv_dtype="nvfp4", idx_dtype="nvfp4",
+                            plant=3, layout="paged", seed=65, device=dev, max_blocks_per_seq=40)
+    iq = w.iq.float()
+    iq[0:12, :, ::7] *= 2.0 ** -30
+    iq[12:24] *= 1.0e6
+    w.iq.copy_(iq.to(torch.bfloat16))
+    check_workload(w, label="multi-query (q_len 12) nvfp4 index keys, extreme index queries")
 
 
 def test_workspace_reuse_across_calls_and_shapes(dev):
@@ -441,7 +463,8 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("kv,idx,q_len", [("nvfp4", "fp8", 1), ("nvfp4", "nvfp4", 1), ("bf16", "bf16", 1),
-                                          ("nvfp4", "bf16", 3), ("nvfp4", "fp8", 3), ("bf16", "fp8", 3)])
+                                          ("nvfp4", "bf16", 3), ("nvfp4", "fp8", 3), ("bf16", "fp8", 3),
+                                          ("nvfp4", "nvfp4", 12)])
 def test_kv_insert_matches_oracle(dev, kv, idx, q_len):
     """msa_kv_insert writes exactly the oracle's bytes (every pool, bit for
     bit: the quantiser's integer decisions are taken in the same fp32 steps),
