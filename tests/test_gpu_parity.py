@@ -213,14 +213,16 @@ def test_fused_selection_on_ties(dev):
             assert sel[row, g].tolist() == want, (row, g, sel[row, g])
 
 
-def test_max_context_fused(dev):
+@pytest.mark.parametrize("idx", ["fp8", "nvfp4"])
+def test_max_context_fused(dev, idx):
     """The largest supported row: 16,384 blocks (2M tokens) next to a short
-    one.  The fused selection then runs 16 active waves, takes the maximum of
-    their thresholds and ranks the merged candidates; checked on every row
-    against the oracle (block scores, ids, outputs)."""
+    one, with FP8 or NVFP4 index keys.  The fused selection then runs 16
+    active waves, takes the maximum of their thresholds and ranks the merged
+    candidates; checked on every row against the oracle (block scores, ids,
+    outputs)."""
     w = synth.make_workload(seq_lens=[16384 * 128 - 5, 3000], max_blocks_per_seq=16384, plant=8, zipf=1.1,
-                            layout="paged", seed=45, device=dev)
-    check_workload(w, label="max context 16,384 blocks")
+                            layout="paged", idx_dtype=idx, seed=45, device=dev)
+    check_workload(w, label=f"max context 16,384 blocks, {idx} index keys")
 
 
 def test_paged_permutation_invariance(dev):
