@@ -28,7 +28,8 @@
 //  * Per 32-token tile a wave reads its A operands, 8 K steps of its lane's
 //    token, straight from LDS (contraction axis permuted: lane half h, step
 //    s, element e -> dim 64h + 8s + e, identically for A and B) and runs 8
-//    v_mfma_f32_32x32x16_bf16 (exact products, fp32 sums).
+//    v_mfma_f32_32x32x16_bf16 (exact products, fp32 sums); in wholly visible
+//    blocks the next tile's reads overlap the current tile's MFMAs.
 //  * Epilogue: causal mask (row r = 4i + g sees tokens <= its query's
 //    position) only for partly visible blocks, max over the block's tokens in
 //    registers; the score matrix never reaches memory and each (row, block)
@@ -191,20 +192,53 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
       const bool full = (long long)j * kBlock + kBlock - 1 <= pos_min;  // every row sees the whole block
       const int vis = pos0 + (row0 + r) / kGroups + 1 - j * kBlock;     // tokens this lane's row sees
       float m = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < kTokTiles; ++tt) {
-        // A operands of token 32tt + col: bf16 dims 64h + 8s .. + 7 from LDS
+      // A operands of token 32tt + col: bf16 dims 64h + 8s .. + 7 from LDS
+      auto read_a = [&](int tt, bf16x8 (&a)[8]) {
         const int t = 32 * tt + col;
-        bf16x8 a[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds_chunk(buf, t, 8 * h + s)));
+        for (int s = 0; s < 8; ++s)
+          a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds_chunk(buf, t, 8 * h + s)));
+      };
+      auto mfma8 = [&](const bf16x8 (&a)[8]) {
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bq[s], acc, 0, 0, 0);
-        if (full) {
+        return acc;
+      };
+      if (full) {
+        // Every row sees the whole block: no masks.  Two operand sets and two
+        // accumulators alternate, so tile tt + 1's LDS reads are interleaved
+        // with tile tt's MFMAs (one read per MFMA, by scheduling groups) and
+        // tile tt's max runs behind tile tt + 1's MFMAs.
+        bf16x8 a0[8], a1[8];
+        f32x16 c0, c1;
+        auto max16 = [&](const f32x16& c) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) m = fmaxf(m, acc[q]);
-        } else {
+          for (int q = 0; q < 16; ++q) m = fmaxf(m, c[q]);
+        };
+        read_a(0, a0);
+#pragma unroll
+        for (int tt = 0; tt < kTokTiles; ++tt) {
+          bf16x8 (&cur)[8] = (tt & 1) ? a1 : a0;
+          bf16x8 (&nxt)[8] = (tt & 1) ? a0 : a1;
+          if (tt + 1 < kTokTiles) read_a(tt + 1, nxt);
+          ((tt & 1) ? c1 : c0) = mfma8(cur);
+          if (tt + 1 < kTokTiles) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            }
+          }
+          if (tt > 0) max16((tt & 1) ? c0 : c1);
+        }
+        max16((kTokTiles & 1) ? c0 : c1);
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < kTokTiles; ++tt) {
+          bf16x8 a[8];
+          read_a(tt, a);
+          const f32x16 acc = mfma8(a);
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             const int tok = 32 * tt + 8 * (q >> 2) + 4 * h + (q & 3);
