@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_HIP = range(5)
 MSA_KV_BF16, MSA_KV_NVFP4 = 0, 1
 MSA_IDX_BF16, MSA_IDX_FP8_E4M3, MSA_IDX_NVFP4 = 0, 1, 2
+MSA_SHARE_MAX = 8  # members per prefix-sharing group
 _IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
             "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_indexer_score_shared", "msa_decode_shared",

@@ -370,7 +370,7 @@ def _share_tensors(groups, share, S, dev) -> dict:
     """The prefix-sharing descriptors of make_workload(share=...)."""
     if share is None:
         return {}
-    members = torch.full((len(groups), 8), -1, dtype=torch.int32)
+    members = torch.full((len(groups), 8), -1, dtype=torch.int32)   # MSA_SHARE_MAX slots
     for gi, mem in enumerate(groups):
         members[gi, :len(mem)] = torch.tensor(mem, dtype=torch.int32)
     sblocks = int(share[1])

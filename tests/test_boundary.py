@@ -194,3 +194,14 @@ def test_read_ceiling_library_exports_and_validates():
     assert fn(fake, 12, None, 0, fake, fake, None, 1, 1, fake, None) == -1       # unsupported page size
     assert fn(fake, 16, None, 0, fake, fake, None, 0, 1, fake, None) == -1       # no sequences
     assert fn(fake, 16, None, 0, fake, fake, None, 70000, 1, fake, None) == -1   # grid rows past 65535
+
+
+def test_binding_constants_match_header():
+    """The binding's enum values and limits are the header's."""
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "msa.h")).read()
+    defines = dict(re.findall(r"#define (MSA_[A-Z_]+) (\d+)", hdr))
+    assert int(defines["MSA_SHARE_MAX"]) == msa.MSA_SHARE_MAX
+    for name in ("MSA_KV_BF16", "MSA_KV_NVFP4", "MSA_IDX_BF16", "MSA_IDX_FP8_E4M3", "MSA_IDX_NVFP4", "MSA_OK",
+                 "MSA_ERR_INVALID_ARGUMENT", "MSA_ERR_UNSUPPORTED", "MSA_ERR_WORKSPACE_TOO_SMALL", "MSA_ERR_HIP"):
+        m = re.search(name + r" = (\d+)", hdr)
+        assert m and int(m.group(1)) == getattr(msa, name), name

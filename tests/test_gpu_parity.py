@@ -401,6 +401,50 @@ def test_prefix_sharing_matches_unshared(dev, group, shared):
         check_row(P, row, o[row], s_[row], b_[row])
 
 
+def test_prefix_sharing_general_descriptors(dev):
+    """Sharing descriptors the generator never makes: members out of index
+    order with the leader last in id, a one-member group, a member whose whole
+    context is the shared prefix (seq_len = shared_blocks x 128), sequences in
+    no group, a padded row.  The members' block-table rows are pointed at the
+    leader's pages for the shared blocks, then the shared and the unshared
+    calls must agree bit for bit, and sampled rows match the oracle."""
+    msa = _msa()
+    lens = [3000, 5000, 0, 4200, 12 * 128, 6100, 2300]
+    w = synth.make_workload(seq_lens=lens, zipf=1.1, layout="paged", seed=88, device=dev)
+    groups = [([5, 1, 4, 3], 12), ([6], 9)]   # (members, leader first; shared blocks)
+    bt = w.block_table.clone()
+    members = torch.full((len(groups), msa.MSA_SHARE_MAX), -1, dtype=torch.int32)
+    shared = torch.zeros(len(groups), dtype=torch.int32)
+    per_seq = torch.zeros(len(lens), dtype=torch.int32)
+    for gi, (mem, sb) in enumerate(groups):
+        assert all(sb * 128 <= lens[b] for b in mem)
+        members[gi, :len(mem)] = torch.tensor(mem, dtype=torch.int32)
+        shared[gi] = sb
+        for b in mem:
+            bt[b, :sb] = bt[mem[0], :sb]
+            per_seq[b] = sb
+    w.block_table = bt
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_tensors(members=members.to(dev), shared_blocks=shared.to(dev),
+                                            seq_shared_blocks=per_seq.to(dev))
+    bs1 = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    bs2 = torch.full_like(bs1, float("nan"))
+    msa.msa_indexer_score(shape, cache, w.iq, bs1)
+    msa.msa_indexer_score_shared(shape, cache, share, w.iq, bs2)
+    out1, sel1 = msa.alloc_outputs(w)
+    out2, sel2 = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out1, sel1, ws)
+    msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out2, sel2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bs1, bs2)
+    assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
+    P = oracle.Problem.from_workload(w)
+    o, s_, b_ = out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy()
+    for row in range(len(lens)):
+        check_row(P, row, o[row], s_[row], b_[row])
+
+
 def test_shared_b32_128k_config_sampled(dev):
     """Batch 32 x 128K in groups of 8 sharing a 96K prefix, through the shared
     path in the bench's launch configuration: bit-equal to the unshared path
