@@ -286,7 +286,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the MSA decode step; runs on more than one GPU are not "
-              "part of this build (decode context parallelism across GPUs is design-only)", file=sys.stderr)
+              "supported (decode context parallelism across GPUs is design-only)", file=sys.stderr)
         sys.exit(2)
 
     import torch
