@@ -166,7 +166,10 @@ def scan_source_hash() -> str:
     for name in SCAN_SOURCES:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_msa_amd", "csrc", name), "rb").read())
         if name.endswith(".hip"):
-            h.update(" ".join(hip_build.FLAGS + hip_build.FILE_FLAGS.get(name, [])).encode())
+            # flags as written, with the checkout's own path taken out (the
+            # include directory is absolute and differs between machines)
+            flags = [f.replace(hip_build.ROOT, "<root>") for f in hip_build.FLAGS + hip_build.FILE_FLAGS.get(name, [])]
+            h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 
