@@ -5,8 +5,9 @@ One step = one call of msa_decode (index scan + block max-pool, top-16 with
 the recent block, sparse GQA attention over NVFP4 K/V) for the whole batch:
 batch 32, 128K-token contexts, paged pool with a random block table, FP8 index
 keys (the headline workload).  Inputs are resident in HBM before timing; the
-step alternates between two copies of the inputs so that a step never reads
-what the previous one left in the 256 MB Infinity Cache.
+steps rotate through copies of the inputs, enough of them that more than
+1.25 x the 256 MB Infinity Cache of other inputs is read between two uses of
+one copy, so that no step reads what an earlier one left in that cache.
 
 Prints ONE JSON line.  Extra detail goes to stderr.
 """
@@ -116,6 +117,18 @@ def read_ceiling(w, copies, stream, steps: int, warmup: int):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps * 1e3, pages * (kb0 + kb1) * 1024
+
+
+MALL_BYTES = 256 << 20   # MI355X Infinity Cache
+
+
+def auto_copies(w) -> int:
+    """Input copies for the step rotation: between two uses of one copy the
+    other copies' step bytes (at least 1.25 x the Infinity Cache) pass
+    through, so a step never finds its inputs there; 2 to 64."""
+    import math
+    step = w.nbytes_algorithmic()["total"]
+    return max(2, min(64, 1 + math.ceil(1.25 * MALL_BYTES / step)))
 
 
 def clone_workload(w):
@@ -274,7 +287,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="paged_b32_128k")
-    ap.add_argument("--copies", type=int, default=2, help="input copies the steps rotate through")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="input copies the steps rotate through (0: enough that more than 1.25 x the 256 MB "
+                         "Infinity Cache of other inputs is read between two uses of one copy)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
@@ -298,7 +313,8 @@ def main():
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     w = synth.make_config(args.config, device=dev)
-    copies = [w] + [clone_workload(w) for _ in range(max(0, args.copies - 1))]
+    ncopies = args.copies or auto_copies(w)
+    copies = [w] + [clone_workload(w) for _ in range(max(0, ncopies - 1))]
     torch.cuda.synchronize()
     log(f"[bench] generated {args.config} x{len(copies)} in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.get_device_name(0)})")
