@@ -1,6 +1,8 @@
 // sparse_attn.hip - the sparse attention kernel (selection fused in the
 // decode path, ids given in the stand-alone entry point); the body is
 // attn_device.hpp.  One workgroup per (query row, group, output part).
+#include <atomic>
+
 #include "attn_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -72,15 +74,17 @@ void launch2(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 int device_cus() {
-  static int cached[64] = {0};
+  // per device, filled on first use; calls from several host threads may
+  // race to fill an entry, which they do with the same value
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
