@@ -289,6 +289,13 @@ __device__ __forceinline__ void attn_workgroup(
     //      of tokens 32s + 8c + e
     [[maybe_unused]] uint32_t vw[kPvSteps][8];
     [[maybe_unused]] uint4 vb[FP4 ? 1 : 8];
+    if constexpr (!FP4 && kLaneDims == 2) {  // bf16 V, 2 dims per lane: all 4 steps' words fit 32 VGPRs
+#pragma unroll
+      for (int s = 0; s < kPvSteps; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vw[s][e] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + 2 * d0);
+    }
     if constexpr (FP4) {
 #pragma unroll
       for (int s = 0; s < kPvSteps; ++s)
@@ -395,7 +402,7 @@ __device__ __forceinline__ void attn_workgroup(
             const uint2 t2 = *reinterpret_cast<const uint2*>(src);
             vb[e] = make_uint4(t2.x, t2.y, 0, 0);
           } else {
-            vb[e] = make_uint4(*reinterpret_cast<const uint32_t*>(src), 0, 0, 0);
+            vb[e] = make_uint4(vw[s][e], 0, 0, 0);  // issued before the softmax
           }
           if (tok >= nvis) vb[e] = make_uint4(0, 0, 0, 0);
         }
