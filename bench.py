@@ -408,7 +408,8 @@ def main():
     fl = scan_flops(w) if w.q_len > 1 else 0.0
     mfma_bound = fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > sb / (HBM_PEAK_GBPS * 1e9)
     if w.share_members is not None:
-        kname = "index scan + block max-pool, each shared-prefix page read once per group (FP8 keys, bf16 MFMA)"
+        kname = (f"index scan + block max-pool, each shared-prefix page read once per group "
+                 f"({w.idx_dtype.upper()} keys, bf16 MFMA)")
     elif w.q_len == 1:
         kname = {"fp8": "index scan + block max-pool (FP8 keys, bf16 MFMA)",
                  "nvfp4": "index scan + block max-pool (NVFP4 keys, bf16 MFMA)",

@@ -121,6 +121,41 @@ __global__ __launch_bounds__(kColsScanWaves * kWave, 4) void scan_shared_kernel(
   scan_wave_fp8_mfma<2>(idx_pool, block_table + (size_t)mem[0] * mbps, cm, j, j + 1, idx_scale, lds_t[wave], lane);
 }
 
+// The same with NVFP4 index keys: the shared rows dequantise each shared page
+// exactly to bf16 once for the group's members (up to 32 (member, group)
+// columns); the own rows are the NVFP4 decode scan's, so those scores equal
+// the unshared call's.
+__global__ __launch_bounds__(kColsScanWaves * kWave, 4) void scan_shared_nvfp4_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores,
+    const int32_t* __restrict__ members, const int32_t* __restrict__ shared_blocks,
+    const int32_t* __restrict__ seq_shared_blocks, int num_groups, int mbps, float idx_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kColsScanWaves][kBlock * 8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int j = blockIdx.x * kColsScanWaves + wave;
+  if ((int)blockIdx.y >= num_groups) {  // a sequence's own blocks
+    const int b = blockIdx.y - num_groups;
+    if (j >= mbps || j < seq_shared_blocks[b]) return;
+    scan_wave_nvfp4(codes, scales, block_table + (size_t)b * mbps, seq_lens[b], iq + (size_t)b * kGroups * kDim,
+                    block_scores + (size_t)b * kGroups * mbps, mbps, j, j + 1, idx_scale, lds_sc[wave], lane);
+    return;
+  }
+  const int gi = blockIdx.y;
+  if (j >= min(shared_blocks[gi], mbps)) return;
+  const int32_t* mem = members + (size_t)gi * kShareMax;
+  int nmem = 0, pos0 = 0x7fffffff;
+  for (int k = 0; k < kShareMax; ++k) {  // wave-uniform
+    if (mem[k] < 0) break;
+    ++nmem;
+    pos0 = min(pos0, seq_lens[mem[k]] - 1);
+  }
+  if (nmem == 0) return;
+  const ShareCols cm{mem, seq_lens, iq, block_scores, mbps, nmem * kGroups, pos0, 0x7fffffff};
+  scan_wave_nvfp4_exact_cols<2>(codes, scales, block_table + (size_t)mem[0] * mbps, cm, j, j + 1, idx_scale,
+                                lds_sc[wave], lane);
+}
+
 // NVFP4 index keys, 2 <= q_len <= 8: the same columns, keys dequantised
 // exactly to bf16 in registers (no LDS).
 template <int NT>
@@ -174,8 +209,14 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
 
 hipError_t launch_scan_shared(const ScanArgs& a, const int32_t* members, const int32_t* shared_blocks,
                               const int32_t* seq_shared_blocks, int num_groups, hipStream_t stream) {
-  if (a.idx_fmt != kIdxFp8 || num_groups + a.num_seqs > 65535) return hipErrorInvalidValue;
+  if (a.idx_fmt == kIdxBf16 || num_groups + a.num_seqs > 65535) return hipErrorInvalidValue;
   dim3 grid((a.mbps + kColsScanWaves - 1) / kColsScanWaves, num_groups + a.num_seqs);
+  if (a.idx_fmt == kIdxNvfp4) {
+    scan_shared_nvfp4_kernel<<<grid, dim3(kColsScanWaves * kWave), 0, stream>>>(
+        static_cast<const uint8_t*>(a.idx_pool), a.idx_sf, a.block_table, a.seq_lens, a.iq, a.block_scores, members,
+        shared_blocks, seq_shared_blocks, num_groups, a.mbps, a.idx_scale);
+    return hipGetLastError();
+  }
   scan_shared_kernel<<<grid, dim3(kColsScanWaves * kWave), 0, stream>>>(
       static_cast<const uint8_t*>(a.idx_pool), a.block_table, a.seq_lens, a.iq, a.block_scores, members,
       shared_blocks, seq_shared_blocks, num_groups, a.mbps, a.idx_scale);

@@ -142,8 +142,8 @@ msa_status check_share(const msa_shape* s, const msa_prefix_share* sh) {
   if (!sh->members || !sh->shared_blocks || !sh->seq_shared_blocks)
     return fail(MSA_ERR_INVALID_ARGUMENT, "share members / shared_blocks / seq_shared_blocks is NULL");
   if (s->q_len != 1) return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with q_len = %d (supported for q_len 1)", s->q_len);
-  if (s->idx_dtype != MSA_IDX_FP8_E4M3)
-    return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with index-key dtype %d (supported for FP8)", (int)s->idx_dtype);
+  if (s->idx_dtype == MSA_IDX_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with bf16 index keys (supported for FP8 and NVFP4)");
   if ((long long)sh->num_groups + s->num_seqs > 65535)
     return fail(MSA_ERR_UNSUPPORTED, "share num_groups + num_seqs = %lld > 65535", (long long)sh->num_groups + s->num_seqs);
   return MSA_OK;

@@ -35,7 +35,7 @@ hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream);
 // FP8 index keys with 1 <= q_len <= 8, NVFP4 with 2 <= q_len <= 8: the (query, group) columns on
 // MFMA, pages streamed by waves.
 hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream);
-// Index scan with prefix sharing (FP8 index keys, q_len 1), one launch: each
+// Index scan with prefix sharing (FP8 or NVFP4 index keys, q_len 1), one launch: each
 // sharing group's shared pages read once for all its members (at most
 // kShareMax), the sequences' own blocks as in the column scan.
 constexpr int kShareMax = 8;

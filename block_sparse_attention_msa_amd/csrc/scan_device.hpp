@@ -507,4 +507,109 @@ __device__ __forceinline__ void scan_wave_nvfp4_cols(const uint8_t* __restrict__
   }
 }
 
+// NVFP4 index keys with the columns of a column map (the members of a
+// prefix-sharing group, q_len 1): the page's codes arrive as in
+// scan_wave_nvfp4_cols, but each code x E4M3 group scale is converted exactly
+// to bf16 (E2M1 -> f32, times the scale in f32, -> bf16: at most 6
+// significant bits, so every step is exact) and the scores run on bf16 MFMAs
+// against the bf16 index queries as they are: exact products, fp32 sums, no
+// query rounding.  The conversion (4 VALU operations per 2 values) is paid
+// once per page for all the columns.
+template <int NT, class Cols>
+__device__ __forceinline__ void scan_wave_nvfp4_exact_cols(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const int32_t* __restrict__ bt_row, const Cols& cm,
+                                                           int jbeg, int jend, float idx_scale, uint8_t* lds_sc,
+                                                           int lane) {
+  const int nbv = cm.nbv;
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int ncols = cm.ncols;
+  const int pos0 = cm.pos0;  // smallest query position of the columns
+  float* bsp[NT];
+  int lastp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + n;
+    bsp[t] = col < ncols ? cm.bs(col) : nullptr;
+    lastp[t] = col < ncols ? cm.last_pos(col) : 0;
+  }
+  // B operands: column 16t + n, dims 32c + 8s .. + 7 for step s (the A side's
+  // K order: dims 32c + 8s + e at K index 8c + e)
+  bf16x8 qb[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + n;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 w = col < ncols ? *reinterpret_cast<const uint4*>(cm.iq(col) + 32 * c + 8 * s) : make_uint4(0, 0, 0, 0);
+      qb[t][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  for (int j = jbeg; j < jend; ++j) {
+    if (j >= nbv) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (c == 0 && 16 * t + n < ncols) bsp[t][j] = -INFINITY;
+      continue;
+    }
+    const int64_t page = bt_row[j];
+    const uint8_t* kbase = codes + page * (kBlock * kDim / 2) + n * (kDim / 2) + 16 * c;
+    u32x4 kv[8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+      kv[T] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)T * 1024));
+    const u32x4 sc16 =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(scales + page * (kBlock * 8) + lane * 16));
+    *reinterpret_cast<u32x4*>(lds_sc + lane * 16) = sc16;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t sw[8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T) sw[T] = *reinterpret_cast<const uint16_t*>(lds_sc + (16 * T + n) * 8 + 2 * c);
+    const bool full = (j + 1) * kBlock - 1 <= pos0;  // wave-uniform: no mask
+    int vis[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vis[t] = lastp[t] + 1 - j * kBlock;
+    float m[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m[t] = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const uint32_t w[4] = {kv[T].x, kv[T].y, kv[T].z, kv[T].w};
+      const f32x2 sf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[T], 1.0f, false);  // groups 2c, 2c + 1
+      bf16x8 ka[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float g = s < 2 ? sf.x : sf.y;
+        const f32x2 e0 = e2m1x2_to_f32x2<0>(w[s]), e1 = e2m1x2_to_f32x2<1>(w[s]);
+        const f32x2 e2 = e2m1x2_to_f32x2<2>(w[s]), e3 = e2m1x2_to_f32x2<3>(w[s]);
+        ka[s] = bf16x8{(__bf16)(e0.x * g), (__bf16)(e0.y * g), (__bf16)(e1.x * g), (__bf16)(e1.y * g),
+                       (__bf16)(e2.x * g), (__bf16)(e2.y * g), (__bf16)(e3.x * g), (__bf16)(e3.y * g)};
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[t][s], acc, 0, 0, 0);
+        if (full) {
+          m[t] = fmaxf(m[t], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[t] = fmaxf(m[t], 16 * T + 4 * c + i < vis[t] ? acc[i] : -INFINITY);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float x = fmaxf(m[t], __shfl_xor(m[t], 16));
+      x = fmaxf(x, __shfl_xor(x, 32));
+      if (c == 0 && 16 * t + n < ncols) bsp[t][j] = x * idx_scale;
+    }
+    __builtin_amdgcn_wave_barrier();  // the next page rewrites this wave's scales
+  }
+}
+
 }  // namespace msa

@@ -407,6 +407,9 @@ CONFIGS = {
     # (768 blocks: system prompt and agent context), own 32K each; not one of
     # the five above
     "shared_b32_128k": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", share=(8, 768), seed=6),
+    # the same with the index cache in NVFP4
+    "shared_b32_128k_nvfp4_idx": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", share=(8, 768),
+                                      idx_dtype="nvfp4", seed=6),
     # the same with the index cache in NVFP4: the AMD serving setting of the
     # pages (NVFP4 indexer cache and 3 draft tokens)
     "spec_b32_q4_128k_nvfp4_idx": dict(seq_lens=[131072 + 4] * 32, q_len=4, zipf=1.1, layout="paged",

@@ -200,7 +200,8 @@ msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const v
  *   seq_shared_blocks int32 [num_seqs]: shared_blocks of the sequence's group,
  *                     0 for a sequence in no group
  * num_groups 0 means no sharing (the arrays may then be NULL).  Block scores,
- * selection and outputs equal those of the unshared calls bit for bit. */
+ * selection and outputs equal those of the unshared calls bit for bit (FP8
+ * index keys; NVFP4 keys: see below). */
 #define MSA_SHARE_MAX 8
 typedef struct {
   int32_t num_groups;
@@ -211,7 +212,11 @@ typedef struct {
 
 /* msa_indexer_score and msa_decode with prefix sharing (one scan launch that
  * scores each group's shared blocks once and every sequence's own blocks).
- * Supported for q_len 1 with FP8 index keys (MSA_ERR_UNSUPPORTED otherwise);
+ * Supported for q_len 1 with FP8 or NVFP4 index keys (MSA_ERR_UNSUPPORTED
+ * otherwise).  With NVFP4 keys the shared pages are dequantised exactly to
+ * bf16 for the group's members (exact products, fp32 sums), a summation order
+ * other than the unshared scan's: those block scores agree with the unshared
+ * call's to fp32 rounding, the sequences' own blocks bit for bit;
  * other arguments as in the unshared calls. */
 msa_status msa_indexer_score_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
                                     const void* idx_q, float* block_scores, hipStream_t stream);

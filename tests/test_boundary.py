@@ -105,9 +105,9 @@ def test_nvfp4_index_keys_validation():
 
 def test_prefix_share_validation():
     """The shared entry points: a NULL descriptor, a negative group count or a
-    missing array is INVALID_ARGUMENT; sharing beyond q_len 1 or FP8 index
-    keys is UNSUPPORTED; zero groups behaves as the unshared call (which then
-    reaches its own checks: here the short workspace)."""
+    missing array is INVALID_ARGUMENT; sharing beyond q_len 1 or with bf16
+    index keys is UNSUPPORTED; FP8 and NVFP4 keys pass on to the next check
+    (here the short workspace), and so do zero groups (the unshared call)."""
     L = msa.lib()
     s = _shape()
     sh = msa.MsaPrefixShare(2, FAKE, FAKE, FAKE)
@@ -122,6 +122,8 @@ def test_prefix_share_validation():
     assert "members" in msa.last_error()
     assert dec(_shape(q_len=2), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
     assert dec(_shape(idx_dtype=msa.MSA_IDX_BF16), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
+    for idx in (msa.MSA_IDX_FP8_E4M3, msa.MSA_IDX_NVFP4):
+        assert dec(_shape(idx_dtype=idx), ctypes.byref(sh), nbytes=16) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
     assert dec(s, ctypes.byref(msa.MsaPrefixShare(0, None, None, None)), nbytes=16) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
     assert L.msa_indexer_score_shared(ctypes.byref(s), ctypes.byref(_cache()), None, FAKE, FAKE, None) == \
         msa.MSA_ERR_INVALID_ARGUMENT

@@ -401,6 +401,57 @@ def test_prefix_sharing_matches_unshared(dev, group, shared):
         check_row(P, row, o[row], s_[row], b_[row])
 
 
+@pytest.mark.parametrize("group,shared", [(8, 20), (3, 7)])
+def test_prefix_sharing_nvfp4_index_keys(dev, group, shared):
+    """Prefix sharing with NVFP4 index keys: the shared pages are dequantised
+    exactly to bf16 once per group (a summation order other than the unshared
+    scan's), so every row is checked against the oracle (block scores within
+    the exact-product bound, ids, outputs), and the sequences' own blocks,
+    scored by the unshared scan's code, equal the unshared call's bit for bit."""
+    msa = _msa()
+    lens = [2600, 9000, 4000, 2561, 7000, 3333, 5000, 2700, 6000, 2900, 4400]
+    w = synth.make_workload(seq_lens=lens, share=(group, shared), zipf=1.1, layout="paged", idx_dtype="nvfp4",
+                            seed=90 + group, device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_workload(w)
+    bs1 = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    bs2 = torch.full_like(bs1, float("nan"))
+    msa.msa_indexer_score(shape, cache, w.iq, bs1)
+    msa.msa_indexer_score_shared(shape, cache, share, w.iq, bs2)
+    out2, sel2 = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out2, sel2, ws)
+    torch.cuda.synchronize()
+    # blocks at or past a sequence's shared count come from the unshared code
+    # (a leader's shared blocks, like its members', from the group rows)
+    for b, own in enumerate(w.seq_shared_blocks.cpu().tolist()):
+        assert torch.equal(bs1[b, :, own:], bs2[b, :, own:]), b
+    P = oracle.Problem.from_workload(w)
+    o, s_, b_ = out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy()
+    for row in range(len(lens)):
+        check_row(P, row, o[row], s_[row], b_[row])
+
+
+def test_shared_b32_128k_nvfp4_index_sampled(dev):
+    """Batch 32 x 128K in groups of 8 sharing a 96K prefix with NVFP4 index
+    keys, through the shared path in the bench's launch configuration; sampled
+    rows checked against the oracle."""
+    msa = _msa()
+    w = synth.make_config("shared_b32_128k_nvfp4_idx", device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_workload(w)
+    out, sel = msa.alloc_outputs(w)
+    bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out, sel, ws)
+    msa.msa_indexer_score_shared(shape, cache, share, w.iq, bs)
+    torch.cuda.synchronize()
+    P = oracle.Problem.from_workload(w)
+    o, s_, b_ = out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy()
+    for row in (0, 7, 8, 31):
+        check_row(P, row, o[row], s_[row], b_[row])
+
+
 def test_prefix_sharing_general_descriptors(dev):
     """Sharing descriptors the generator never makes: members out of index
     order with the leader last in id, a one-member group, a member whose whole
