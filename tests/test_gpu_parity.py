@@ -370,6 +370,31 @@ def test_decode_without_selected_ids_output(dev, q_len):
         check_row(P, row, o[row], s_[row])
 
 
+@pytest.mark.parametrize("idx,share", [("fp8", None), ("fp8", (8, 12)), ("nvfp4", (5, 9))])
+def test_large_decode_batch_three_launches(dev, idx, share):
+    """q_len 1 with 160 sequences: 640 (row, group) pairs, more than two per
+    compute unit, so msa_decode runs the selection as its own launch between
+    the scan and the attention; also through the shared entry point with
+    prefix sharing (FP8 and NVFP4 index keys).  Every row against the oracle."""
+    msa = _msa()
+    lens = [1700 + (97 * i) % 2500 for i in range(160)]
+    w = synth.make_workload(seq_lens=lens, share=share, zipf=1.1, layout="paged", idx_dtype=idx, seed=95,
+                            device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    assert w.rows * 4 > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    out, sel = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    if share is None:
+        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+    else:
+        msa.msa_decode_shared(shape, cache, msa.MsaPrefixShare.from_workload(w), w.q, w.iq, out, sel, ws)
+    torch.cuda.synchronize()
+    P = oracle.Problem.from_workload(w)
+    o, s_ = out.cpu().numpy(), sel.cpu().numpy()
+    for row in range(w.rows):
+        check_row(P, row, o[row], s_[row])
+
+
 @pytest.mark.parametrize("group,shared", [(8, 20), (3, 7), (2, 0)])
 def test_prefix_sharing_matches_unshared(dev, group, shared):
     """Prefix sharing (groups whose first blocks map to the leader's pages):
