@@ -180,7 +180,10 @@ msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void
  * operation in that order.  FP8 index keys: E4M3 nearest-even of
  * x / idx_scale clamped to +-448, sign kept on zero.  bf16 pools: bf16
  * nearest-even of x / scale.  Calls that write the same pages must be
- * ordered; with msa_decode on the same stream the insert comes first. */
+ * ordered; with msa_decode on the same stream the insert comes first.  Rows
+ * whose new tokens map to the same physical slot (a shared-prefix page, see
+ * msa_prefix_share) write it concurrently: the caller passes such a token
+ * once, or the same values for every row that maps it. */
 msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const void* k_new, const void* v_new,
                          const void* idx_new, hipStream_t stream);
 
