@@ -1,8 +1,12 @@
 """GPU parity on seeded random cases: batch size, ragged and padded lengths,
 q_len, K/V and index-key dtypes, layout, score structure and prefix sharing
-drawn from one seeded generator, every case through the fused step (the
+drawn from seeded generators, every case through the fused step (the
 shared entry point when the case shares a prefix), the stand-alone index scan
-and, without sharing, the unfused trio; every row against the fp64 oracle."""
+and, without sharing, the unfused trio; rows against the fp64 oracle (every
+row, or 66 sampled rows of a case with more than 96).  The second generator
+reaches the larger shapes: chunks of 17-300 query tokens, decode batches of
+100-200 short rows (more (row, group) pairs than two per compute unit) and
+contexts up to 300K tokens."""
 import random
 import sys
 
@@ -48,17 +52,63 @@ def _case(i):
     return kw
 
 
+def _wide_case(i):
+    """The i-th case of the wider generator (deterministic)."""
+    rng = random.Random(50000 + i)
+    kv = rng.choice(["nvfp4", "nvfp4", "bf16"])
+    idx = rng.choice(["fp8", "fp8", "nvfp4", "bf16"])
+    kind = rng.random()
+    if kind < 0.3:  # a long multi-query chunk
+        q_len = rng.choice([17, 33, 64, 100, 128, 256, 300])
+        S = rng.randint(1, 3)
+        cap = max(q_len, min(60000, 10_000_000 // (q_len * S)))
+        lens = [rng.randint(q_len, cap) for _ in range(S)]
+    elif kind < 0.55:  # a large batch of short rows
+        q_len = rng.choice([1, 1, 2, 4])
+        S = rng.randint(100, 200)
+        lens = [0 if rng.random() < 0.05 else rng.randint(q_len, 4000) for _ in range(S)]
+    elif kind < 0.75:  # long contexts
+        q_len = rng.choice([1, 1, 2, 4, 8])
+        S = rng.randint(1, 4)
+        lens = [rng.randint(q_len, 300_000) for _ in range(S)]
+    else:
+        q_len = rng.choice([1, 2, 3, 5, 8, 9, 16])
+        S = rng.randint(1, 12)
+        lens = [0 if rng.random() < 0.1 else rng.randint(q_len, 30000) for _ in range(S)]
+    if all(L == 0 for L in lens):
+        lens[0] = rng.randint(q_len, 5000)
+    kw = dict(seq_lens=lens, q_len=q_len, kv_dtype=kv, idx_dtype=idx, layout=rng.choice(["paged", "identity"]),
+              seed=60000 + i, spare_pages=rng.randint(0, 3))
+    r = rng.random()
+    if r < 0.4:
+        kw["zipf"] = 1.1
+    elif r < 0.7:
+        kw["plant"] = rng.randint(1, 6)
+    if q_len > 1 and rng.random() < 0.5:
+        kw["shared_bias_iq"] = True
+    if q_len == 1 and idx in ("fp8", "nvfp4") and S >= 2 and rng.random() < 0.5:
+        hi = 4000 if S > 20 else 40000
+        lens[:] = [rng.randint(1500, hi) for _ in range(S)]
+        kw["share"] = (rng.randint(2, min(8, S)), rng.randint(0, min(lens) // 128))
+        kw["layout"] = "paged"
+    kw["max_blocks_per_seq"] = max(1, max((L + 127) // 128 for L in lens)) + rng.randint(0, 5)
+    return kw
+
+
+# two to four of each kind: long chunks, long contexts, large batches with and
+# without sharing, mixed small cases with and without sharing
+WIDE_CASES = [0, 7, 8, 9, 2, 4, 5, 10, 21, 22, 28, 18, 38, 61, 67, 88, 1, 3]
+
+
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available()
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_case(dev, i):
+def _run_case(dev, kw, label):
     from block_sparse_attention_msa_amd import msa  # raises if libmsa.so is missing
-    kw = _case(i)
-    print(f"[random] case {i}: {kw}", file=sys.stderr, flush=True)
+    print(f"[random] {label}: {kw}", file=sys.stderr, flush=True)
     w = synth.make_workload(device=dev, **kw)
     shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
     out, sel = msa.alloc_outputs(w)
@@ -81,5 +131,18 @@ def test_random_case(dev, i):
     P = oracle.Problem.from_workload(w)
     o, s_, b_ = out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy()
     assert np.isfinite(o).all()
-    for row in range(w.rows):
+    rows = list(range(w.rows))
+    if w.rows > 96:
+        rows = sorted(set(random.Random(w.rows).sample(rows, 64) + [0, w.rows - 1]))
+    for row in rows:
         check_row(P, row, o[row], s_[row], b_[row])
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(dev, i):
+    _run_case(dev, _case(i), f"case {i}")
+
+
+@pytest.mark.parametrize("i", WIDE_CASES)
+def test_random_wide_case(dev, i):
+    _run_case(dev, _wide_case(i), f"wide case {i}")
