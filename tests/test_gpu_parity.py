@@ -225,6 +225,30 @@ def test_max_context_fused(dev, idx):
     check_workload(w, label=f"max context 16,384 blocks, {idx} index keys")
 
 
+def test_long_table_batch_1024_thread_form(dev):
+    """40 rows (160 (row, group) pairs: more than one per two compute units, at
+    most two per unit) with block-table rows of 9,000 entries, more than the 512-thread
+    attention's selection holds: the fused selection then feeds the
+    1024-thread attention without an output-dims split.  NVFP4 K/V, FP8 index
+    keys; every row against the oracle (block scores, ids, outputs)."""
+    msa = _msa()
+    lens = [1000 + (331 * i) % 6000 for i in range(40)]
+    w = synth.make_workload(seq_lens=lens, max_blocks_per_seq=9000, zipf=1.1, layout="paged", seed=47, device=dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert cus < 2 * (w.rows * 4) and w.rows * 4 <= 2 * cus
+    _say(f"[parity] long table batch: seqs={w.num_seqs} mbps={w.max_blocks_per_seq}")
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    out, sel = msa.alloc_outputs(w)
+    msa.msa_decode(shape, cache, w.q, w.iq, out, sel, msa.alloc_workspace(shape, dev))
+    bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    msa.msa_indexer_score(shape, cache, w.iq, bs)
+    torch.cuda.synchronize()
+    P = oracle.Problem.from_workload(w)
+    o, s_, b_ = out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy()
+    for row in range(w.rows):
+        check_row(P, row, o[row], s_[row], b_[row])
+
+
 def test_paged_permutation_invariance(dev):
     """Physical page permutation leaves ids and outputs bitwise unchanged."""
     w = synth.make_workload(seq_lens=[7000, 4100, 300], plant=3, seed=24, spare_pages=3, device=dev)
