@@ -96,8 +96,11 @@ def _wide_case(i):
 
 
 # two to four of each kind: long chunks, long contexts, large batches with and
-# without sharing, mixed small cases with and without sharing
-WIDE_CASES = [0, 7, 8, 9, 2, 4, 5, 10, 21, 22, 28, 18, 38, 61, 67, 88, 1, 3]
+# without sharing, mixed small cases with and without sharing; then cases that
+# give every attention launch form (output dims split in 4 or 2, 512- or
+# 1024-thread workgroups, selection fused or its own launch) with both K/V
+# dtypes
+WIDE_CASES = [0, 7, 8, 9, 2, 4, 5, 10, 21, 22, 28, 18, 38, 61, 67, 88, 1, 3, 35, 12, 37, 23, 13]
 
 
 @pytest.fixture(scope="module")
