@@ -163,6 +163,18 @@ msa_status check_aligned(const void* p, size_t a, const char* what) {
   return MSA_OK;
 }
 
+// The group-scale arrays are read with 16-byte vector loads (a page's scales
+// are whole 1 KB runs), so their base pointers must be 16-byte aligned.
+msa_status check_scale_alignment(const msa_shape* s, const msa_cache* c, bool need_idx, bool need_kv) {
+  msa_status st = MSA_OK;
+  if (need_kv && s->kv_dtype == MSA_KV_NVFP4) {
+    if ((st = check_aligned(c->k_sf, 16, "k_sf")) != MSA_OK) return st;
+    if ((st = check_aligned(c->v_sf, 16, "v_sf")) != MSA_OK) return st;
+  }
+  if (need_idx && s->idx_dtype == MSA_IDX_NVFP4 && (st = check_aligned(c->idx_sf, 16, "idx_sf")) != MSA_OK) return st;
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +198,7 @@ static msa_status indexer_impl(const msa_shape* shape, const msa_cache* cache, c
   if (!idx_q || !block_scores) return fail(MSA_ERR_INVALID_ARGUMENT, "idx_q / block_scores is NULL");
   if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
   if ((st = check_aligned(idx_q, 16, "idx_q")) != MSA_OK) return st;
+  if ((st = check_scale_alignment(shape, cache, true, false)) != MSA_OK) return st;
   if (shape->num_seqs == 0) return ok();
   return hip_status(launch_scan_any(shape, scan_args(shape, cache, idx_q, block_scores), share, stream), "index scan");
 }
@@ -224,6 +237,7 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
   if ((st = check_aligned(q, 16, "q")) != MSA_OK) return st;
   if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
+  if ((st = check_scale_alignment(shape, cache, false, true)) != MSA_OK) return st;
   if (shape->num_seqs == 0) return ok();
   return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, nullptr, sel_blocks, nullptr, out), stream),
                     "sparse attention");
@@ -242,6 +256,7 @@ static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, co
   if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
+  if ((st = check_scale_alignment(shape, cache, true, true)) != MSA_OK) return st;
   const size_t need = msa_workspace_size(shape);
   if (shape->num_seqs > 0) {
     if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
@@ -294,6 +309,7 @@ msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const v
   const char* names[] = {"k_new", "v_new", "idx_new", "k", "v", "idx_k"};
   for (int i = 0; i < 6; ++i)
     if ((st = check_aligned(aligned16[i], 16, names[i])) != MSA_OK) return st;
+  if ((st = check_scale_alignment(shape, cache, true, true)) != MSA_OK) return st;
   if (shape->num_seqs == 0) return ok();
   msa::InsertArgs a;
   // the pools are written: the cache's pointers are taken as writable

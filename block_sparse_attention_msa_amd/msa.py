@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmsa.so")
+# the in-tree build; MSA_LIB_PATH names another build of the same sources (the
+# sanitizer run's instrumented copy)
+LIB_PATH = os.environ.get("MSA_LIB_PATH") or os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_HIP = range(5)
 MSA_KV_BF16, MSA_KV_NVFP4 = 0, 1

@@ -16,6 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "msa_oracle.c")
 _LIB = os.path.join(_HERE, "libmsa_oracle.so")
+_LIB_OVERRIDE = os.environ.get("MSA_ORACLE_LIB")  # another build of msa_oracle.c (the sanitizer run's)
 _lib = None
 
 
@@ -46,8 +47,11 @@ class _Problem(ctypes.Structure):
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
         lib.msa_oracle_bf16.restype = ctypes.c_double
         lib.msa_oracle_bf16.argtypes = [ctypes.c_uint16]
         lib.msa_oracle_e4m3.restype = ctypes.c_double
@@ -64,6 +68,8 @@ def _load():
         lib.msa_oracle_e4m3_rne.restype = ctypes.c_uint8
         lib.msa_oracle_e4m3_rne.argtypes = [ctypes.c_float]
         lib.msa_oracle_e2m1_rne.restype = ctypes.c_uint8
+        lib.msa_oracle_bf16_rne.restype = ctypes.c_uint16
+        lib.msa_oracle_bf16_rne.argtypes = [ctypes.c_float]
         lib.msa_oracle_e2m1_rne.argtypes = [ctypes.c_float]
         lib.msa_oracle_quant_nvfp4_group.restype = None
         lib.msa_oracle_quant_nvfp4_group.argtypes = [ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
@@ -169,6 +175,11 @@ def e4m3_rne(y: float) -> int:
 
 def e2m1_rne(y: float) -> int:
     return int(_load().msa_oracle_e2m1_rne(float(y)))
+
+
+def bf16_rne(y: float) -> int:
+    """bf16 bits of the float32 value y rounded to nearest, ties to even."""
+    return int(_load().msa_oracle_bf16_rne(float(y)))
 
 
 def quant_nvfp4_group(x16, gs: float):

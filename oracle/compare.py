@@ -53,23 +53,47 @@ def _ik_dense(P, b):
 
 
 def score_abs_bound(P, row):
-    """[G][mbps] bound on |gpu - oracle| block scores of one decode row."""
-    b = row // P.q_len
-    ik, L, nb = _ik_dense(P, b)
-    iq = torch.from_numpy(P.arrays["iq"][row].view(np.int16)).view(torch.bfloat16).to(torch.float64)
-    G = iq.shape[0]
-    out = np.zeros((G, P.max_blocks_per_seq))
-    if L == 0:
-        return out
-    A = (ik[:L].abs() @ iq.abs().T) * P.idx_scale              # [L, G]
-    if P.arrays.get("idx_sf") is not None and 1 < P.q_len <= 8:  # the f16 column scan
-        A = A * (2.0 * 130.0 * 2.0 ** -24) + (ik[:L].abs() @ f16_query_rounding(iq).T) * P.idx_scale
-    else:
-        A = A * (2.0 * 130.0 * 2.0 ** -24)
-    pad = torch.zeros(nb * 128, G, dtype=torch.float64)
-    pad[:L] = A
-    Ab = pad.reshape(nb, 128, G).amax(dim=1).T.numpy()         # [G, nb]
-    out[:, :nb] = Ab + 1e-30
+    """[G][mbps] bound on |gpu - oracle| block scores of one query row."""
+    return score_abs_bounds(P, [row])[row]
+
+
+def score_abs_bounds(P, rows, chunk_cols=256):
+    """{row: [G][mbps] bound on |gpu - oracle| block scores} for many query
+    rows, decoding each sequence's index keys once (rows of one sequence share
+    them) and taking the per-token sums for up to chunk_cols (row, group)
+    index queries per matrix product.  The per-token sums run over every token
+    of the sequence's blocks, so a multi-query row's bound on its recent block
+    also counts tokens past its position: larger, still a bound."""
+    rows = sorted(set(int(r) for r in rows))
+    G, mb = P.num_kv_heads, P.max_blocks_per_seq
+    f16_term = P.arrays.get("idx_sf") is not None and 1 < P.q_len <= 8   # the f16 column scan
+    by_seq = {}
+    for row in rows:
+        by_seq.setdefault(row // P.q_len, []).append(row)
+    out = {}
+    for b, rs in by_seq.items():
+        L = int(P.arrays["seq_lens"][b])
+        if L == 0:
+            for row in rs:
+                out[row] = np.zeros((G, mb))
+            continue
+        ik, L, nb = _ik_dense(P, b)
+        ika = ik[:L].abs()
+        iq_all = torch.from_numpy(P.arrays["iq"][rs].view(np.int16)).view(torch.bfloat16).to(torch.float64)
+        iq_all = iq_all.reshape(len(rs) * G, -1)                             # [(row, g)][128]
+        for c0 in range(0, iq_all.shape[0], chunk_cols):
+            iq = iq_all[c0:c0 + chunk_cols]
+            A = (ika @ iq.abs().T) * (P.idx_scale * 2.0 * 130.0 * 2.0 ** -24)   # [L, cols]
+            if f16_term:
+                A = A + (ika @ f16_query_rounding(iq).T) * P.idx_scale
+            pad = torch.zeros(nb * 128, A.shape[1], dtype=torch.float64)
+            pad[:L] = A
+            Ab = pad.reshape(nb, 128, -1).amax(dim=1).T.numpy()                # [cols, nb]
+            for k in range(Ab.shape[0] // G):
+                row = rs[(c0 + k * G) // G]
+                o = np.zeros((G, mb))
+                o[:, :nb] = Ab[k * G:(k + 1) * G] + 1e-30
+                out[row] = o
     return out
 
 
@@ -94,15 +118,42 @@ def _order(bs, r):
     return ids[np.lexsort((ids, -bs[:r]))]
 
 
-def check_row(P, row, gpu_out, gpu_sel, gpu_bs=None, *, atol=ATOL, rtol=RTOL, tie_rel=TIE_REL, oracle_row=None):
-    """Compares one query row; returns a dict of findings (raises on failure)."""
+def _row_position(P, row):
+    """(pos, recent block r, visible blocks nbv) of a query row; pos -1 for a padded row."""
+    L = int(P.arrays["seq_lens"][row // P.q_len])
+    if L <= 0:
+        return -1, -1, 0
+    pos = L - P.q_len + row % P.q_len
+    return pos, pos // 128, pos // 128 + 1
+
+
+def check_selection_valid(gpu_sel_g, r, nbv, where=""):
+    """What every selection must be, whatever the scores: min(nbv, 16) distinct
+    ids in strictly ascending order, each a visible block (0 <= id < nbv), the
+    recent block r among them, -1 only as trailing padding."""
+    ids = np.asarray(gpu_sel_g)
+    keep = min(nbv, 16)
+    assert ids.shape == (16,), f"{where}: {ids.shape} ids"
+    assert (ids[keep:] == -1).all(), f"{where}: ids past the first {keep} must be -1 padding: {ids}"
+    kept = ids[:keep]
+    assert (kept >= 0).all() and (kept < nbv).all(), f"{where}: id outside the visible blocks 0..{nbv - 1}: {ids}"
+    assert (np.diff(kept) > 0).all(), f"{where}: ids not strictly ascending (duplicate or out of order): {ids}"
+    assert keep == 0 or r in kept.tolist(), f"{where}: the recent block {r} is missing: {ids}"
+
+
+def check_row(P, row, gpu_out, gpu_sel, gpu_bs=None, *, atol=ATOL, rtol=RTOL, tie_rel=TIE_REL, oracle_row=None,
+              bound=None):
+    """Compares one query row; returns a dict of findings (raises on failure).
+    oracle_row: this row's (bs, sel, out) from a batched oracle call, each with
+    a leading axis of 1; bound: its block-score bound, from score_abs_bounds."""
     bs_o, sel_o, out_o = oracle_row if oracle_row is not None else P.decode(row, row + 1)
     bs_o, sel_o, out_o = bs_o[0], sel_o[0], out_o[0]
     G = sel_o.shape[0]
     hpg = out_o.shape[0] // G
+    pos, r, nbv = _row_position(P, row)
     info = dict(row=row, near_ties=0, max_abs_err=0.0)
     if gpu_bs is not None:
-        bound = score_abs_bound(P, row)
+        bound = score_abs_bound(P, row) if bound is None else bound
         fin = np.isfinite(bs_o)
         assert np.array_equal(np.isneginf(gpu_bs), np.isneginf(bs_o)), f"row {row}: -inf pattern of block scores"
         err = np.abs(gpu_bs[fin].astype(np.float64) - bs_o[fin])
@@ -110,16 +161,21 @@ def check_row(P, row, gpu_out, gpu_sel, gpu_bs=None, *, atol=ATOL, rtol=RTOL, ti
     for g in range(G):
         ref_out = out_o[g * hpg:(g + 1) * hpg]
         if not np.array_equal(gpu_sel[g], sel_o[g]):
-            kept_o = sel_o[g][sel_o[g] >= 0]
-            r = int(kept_o.max())
+            where = f"row {row} g {g}"
+            check_selection_valid(gpu_sel[g], r, nbv, where)
+            # near tie (R20): with the non-recent blocks in oracle order, the
+            # 15th and 16th are within tie_rel; the GPU may then swap blocks
+            # of that band only, as many in as out
             order = _order(bs_o[g], r)
-            assert len(order) >= 16, f"row {row} g {g}: sets differ with <= 16 candidates"
+            assert len(order) >= 16, f"{where}: sets differ with <= 16 candidates"
             c, c2 = bs_o[g][order[14]], bs_o[g][order[15]]
             near = abs(c - c2) < tie_rel * max(abs(c), abs(c2))
-            diff = set(gpu_sel[g].tolist()) ^ set(sel_o[g].tolist())
-            assert near, f"row {row} g {g}: selection differs without a near tie: gpu {gpu_sel[g]} oracle {sel_o[g]}"
-            assert all(abs(bs_o[g][j] - c) <= tie_rel * abs(c) for j in diff if j >= 0), \
-                f"row {row} g {g}: differing block not within the tie band"
+            assert near, f"{where}: selection differs without a near tie: gpu {gpu_sel[g]} oracle {sel_o[g]}"
+            got, want = set(gpu_sel[g].tolist()) - {-1}, set(sel_o[g].tolist()) - {-1}
+            added, dropped = got - want, want - got
+            assert len(added) == len(dropped), f"{where}: {len(added)} blocks added, {len(dropped)} dropped"
+            assert all(abs(bs_o[g][j] - c) <= tie_rel * abs(c) for j in added | dropped), \
+                f"{where}: differing block not within the tie band"
             info["near_ties"] += 1
             ref_out = P.attend(row, g, gpu_sel[g])
         got = gpu_out[g * hpg:(g + 1) * hpg].astype(np.float64)
@@ -128,3 +184,23 @@ def check_row(P, row, gpu_out, gpu_sel, gpu_bs=None, *, atol=ATOL, rtol=RTOL, ti
         assert not bad.any(), f"row {row} g {g}: output error {err.max()} (ref {ref_out.flat[np.argmax(err)]})"
         info["max_abs_err"] = max(info["max_abs_err"], float(err.max()))
     return info
+
+
+def check_rows(P, gpu_out, gpu_sel, gpu_bs=None, rows=None, **kw):
+    """Every given row (default: all) against one batched oracle call over the
+    row range they span (OpenMP over (row, group) pairs), block-score bounds
+    taken per sequence.  Returns (near ties, worst abs output error)."""
+    rows = list(range(P.rows)) if rows is None else sorted(int(x) for x in rows)
+    if not rows:
+        return 0, 0.0
+    lo, hi = rows[0], rows[-1] + 1
+    bs_o, sel_o, out_o = P.decode(lo, hi, want_scores=True)
+    bounds = score_abs_bounds(P, rows) if gpu_bs is not None else {}
+    ties, worst = 0, 0.0
+    for row in rows:
+        k = row - lo
+        info = check_row(P, row, gpu_out[row], gpu_sel[row], None if gpu_bs is None else gpu_bs[row],
+                         oracle_row=(bs_o[k:k + 1], sel_o[k:k + 1], out_o[k:k + 1]), bound=bounds.get(row), **kw)
+        ties += info["near_ties"]
+        worst = max(worst, info["max_abs_err"])
+    return ties, worst

@@ -218,7 +218,8 @@ int msa_oracle_select(const double* bs, int nbv, int32_t* sel) {
 
 /* out[hh][d] for the heads hh of group g (head = g * heads_per_group + hh):
  * softmax over the keys t <= pos of the selected blocks, two-pass in fp64.
- * A padded row or an empty selection gives zeros.  Returns the key count. */
+ * Ids outside the visible blocks 0 .. pos/128 are ignored.  A padded row or
+ * an empty selection gives zeros.  Returns the key count. */
 int msa_oracle_attend(const oracle_problem* p, int row, int g, const int32_t* sel, double* out) {
   int hpg = p->num_q_heads / p->num_kv_heads;
   int b;
@@ -231,7 +232,8 @@ int msa_oracle_attend(const oracle_problem* p, int row, int g, const int32_t* se
   int nk = 0;
   for (int k = 0; k < OR_TOPK; ++k) {
     int j = sel[k];
-    if (j < 0) continue;
+    /* ids that name no visible block contribute nothing (and index no table entry) */
+    if (j < 0 || j >= p->max_blocks_per_seq || (int64_t)j * OR_BLOCK > pos) continue;
     int64_t page = p->block_table[(int64_t)b * p->max_blocks_per_seq + j];
     for (int tok = 0; tok < OR_BLOCK; ++tok) {
       if ((int64_t)j * OR_BLOCK + tok > pos) break;
@@ -364,13 +366,22 @@ void msa_oracle_quant_nvfp4_group(const float* x, float gs, uint8_t* packed, uin
   *scale = s;
 }
 
-/* bf16 nearest-even of a float (finite). */
-static uint16_t or_bf16_rne(float f) {
+/* bf16 nearest-even of a finite float, from the definition: of the two bf16
+ * values that bracket x (x with its low 16 bits cleared, and the next bf16
+ * away from zero) take the one nearer in exact (double) arithmetic; on a tie
+ * the one whose last kept bit is 0.  A value beyond the largest finite bf16
+ * by at least half a unit rounds to infinity, as IEEE rounding does. */
+uint16_t msa_oracle_bf16_rne(float x) {
   uint32_t w;
-  memcpy(&w, &f, sizeof w);
-  uint32_t lsb = (w >> 16) & 1u;
-  w += 0x7FFFu + lsb;
-  return (uint16_t)(w >> 16);
+  memcpy(&w, &x, sizeof w);
+  uint16_t lo = (uint16_t)(w >> 16);     /* toward zero */
+  uint16_t hi = (uint16_t)(lo + 1u);     /* away from zero (0x7F80 = inf past the top) */
+  double a = fabs((double)x);
+  double dlo = a - fabs(msa_oracle_bf16(lo));
+  double dhi = ((hi & 0x7FFFu) == 0x7F80u) ? ldexp(1.0, 128) - a : fabs(msa_oracle_bf16(hi)) - a;
+  if (dlo < dhi) return lo;
+  if (dhi < dlo) return hi;
+  return (lo & 1u) ? hi : lo;
 }
 
 /* Quantise the new tokens of every query row into the pools of p (whose
@@ -402,7 +413,7 @@ int msa_oracle_kv_insert(const oracle_problem* p, const float* k_new, const floa
           for (int c = 0; c < OR_DIM / 16; ++c)
             msa_oracle_quant_nvfp4_group(x + 16 * c, gs, (uint8_t*)pool + r * (OR_DIM / 2) + 8 * c, sf + r * (OR_DIM / 16) + c);
         } else {
-          for (int d = 0; d < OR_DIM; ++d) ((uint16_t*)pool)[r * OR_DIM + d] = or_bf16_rne(x[d] / gs);
+          for (int d = 0; d < OR_DIM; ++d) ((uint16_t*)pool)[r * OR_DIM + d] = msa_oracle_bf16_rne(x[d] / gs);
         }
       }
     }
@@ -419,7 +430,7 @@ int msa_oracle_kv_insert(const oracle_problem* p, const float* k_new, const floa
         ((uint8_t*)p->idx_k)[r * OR_DIM + d] = msa_oracle_e4m3_rne(fmaxf(-448.0f, fminf(448.0f, y)));
       }
     } else {
-      for (int d = 0; d < OR_DIM; ++d) ((uint16_t*)p->idx_k)[r * OR_DIM + d] = or_bf16_rne(x[d] / is);
+      for (int d = 0; d < OR_DIM; ++d) ((uint16_t*)p->idx_k)[r * OR_DIM + d] = msa_oracle_bf16_rne(x[d] / is);
     }
   }
   return 0;

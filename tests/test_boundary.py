@@ -93,6 +93,31 @@ def test_null_and_pointer_validation():
         msa.MSA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_scale_arrays_must_be_16_byte_aligned():
+    """The E4M3 group-scale arrays are read with 16-byte loads: a misaligned
+    k_sf / v_sf (NVFP4 K/V) or idx_sf (NVFP4 index keys) is rejected by every
+    entry point that reads or writes it, before any HIP call; with bf16 K/V or
+    FP8 index keys the arrays are not used and their alignment is free."""
+    L = msa.lib()
+    nv_idx = _shape(idx_dtype=msa.MSA_IDX_NVFP4)
+    cases = [(_shape(), dict(k_sf=FAKE + 4), "k_sf"), (_shape(), dict(v_sf=FAKE + 1), "v_sf"),
+             (nv_idx, dict(idx_sf=FAKE + 8), "idx_sf")]
+    for s, kw, name in cases:
+        c = _cache(**kw)
+        assert _decode(s, cache=c) == msa.MSA_ERR_INVALID_ARGUMENT and name in msa.last_error()
+        assert L.msa_kv_insert(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, FAKE, None) == \
+            msa.MSA_ERR_INVALID_ARGUMENT and name in msa.last_error()
+        if name == "idx_sf":
+            assert L.msa_indexer_score(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, None) == \
+                msa.MSA_ERR_INVALID_ARGUMENT and name in msa.last_error()
+        else:
+            assert L.msa_sparse_attn_decode(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, FAKE, None, 0, None) == \
+                msa.MSA_ERR_INVALID_ARGUMENT and name in msa.last_error()
+    # unused arrays: validation proceeds to the workspace check
+    assert _decode(_shape(kv_dtype=msa.MSA_KV_BF16), cache=_cache(k_sf=FAKE + 4, v_sf=FAKE + 2, idx_sf=FAKE + 1),
+                   nbytes=0) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_nvfp4_index_keys_validation():
     """NVFP4 index keys need their scale array; every q_len takes them."""
     s = _shape(idx_dtype=msa.MSA_IDX_NVFP4)

@@ -1,8 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
-Small and ragged cases are compared on every row; the full-size workloads
-(batch 32 x 128K paged, batch 4 x 512K paged) are run in the same launch
-configuration the bench times and compared on sampled rows.  Rules (ids
+Every workload is compared on every query row, the full-size ones (batch
+32 x 128K paged, batch 4 x 512K paged, the 2 x 256-token chunk on 128K, the
+speculative-verify and prefix-sharing batches) included, each in the launch
+configuration the bench times.  Rules (ids
 bit-exact except near ties, out within 2e-3 + 1e-2|ref|, block scores within
 the fp32 rounding bound) are in oracle/compare.py.
 """
@@ -15,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.compare import check_row
+from oracle.compare import check_row, check_rows
 from block_sparse_attention_msa_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -49,20 +50,18 @@ def run_all(w):
 
 
 def check_workload(w, rows=None, label=""):
-    _say(f"[parity] {label or w.name}: seqs={w.num_seqs} mbps={w.max_blocks_per_seq} kv={w.kv_dtype} idx={w.idx_dtype}")
+    """Runs the fused path and the unfused trio, then compares the given rows
+    (default: every row) with one batched oracle call."""
+    _say(f"[parity] {label or w.name}: seqs={w.num_seqs} q_len={w.q_len} mbps={w.max_blocks_per_seq} "
+         f"kv={w.kv_dtype} idx={w.idx_dtype}")
     out, sel, bs, out2, sel2 = run_all(w)
     # the unfused trio runs the same kernels: identical results
     assert np.array_equal(sel, sel2)
     assert np.array_equal(out, out2)
     P = oracle.Problem.from_workload(w)
-    rows = range(w.rows) if rows is None else rows
-    ties = 0
-    worst = 0.0
-    for row in rows:
-        info = check_row(P, row, out[row], sel[row], bs[row])
-        ties += info["near_ties"]
-        worst = max(worst, info["max_abs_err"])
-    _say(f"[parity] {label or w.name}: rows={len(list(rows))} near_ties={ties} max_abs_err={worst:.3g}")
+    rows = list(range(w.rows)) if rows is None else list(rows)
+    ties, worst = check_rows(P, out, sel, bs, rows=rows)
+    _say(f"[parity] {label or w.name}: rows={len(rows)} of {w.rows} near_ties={ties} max_abs_err={worst:.3g}")
     return out, sel, bs
 
 
@@ -87,15 +86,15 @@ def test_decode_b8_32k_config(dev):
             assert set(w.meta["planted"][(b, g)]) <= set(sel[b, g].tolist())
 
 
-def test_paged_b32_128k_config_sampled(dev):
+def test_paged_b32_128k_config(dev):
     w = synth.make_config("paged_b32_128k", device=dev)
-    check_workload(w, rows=[0, 9, 22, 31])
+    check_workload(w)
 
 
-def test_paged_b4_512k_config_sampled(dev):
+def test_paged_b4_512k_config(dev):
     w = synth.make_config("paged_b4_512k", device=dev)
-    _, sel, _ = check_workload(w, rows=[0, 3])
-    for b in (0, 3):
+    _, sel, _ = check_workload(w)
+    for b in range(4):
         for g in range(4):
             assert set(w.meta["planted"][(b, g)]) <= set(sel[b, g].tolist())
 
@@ -162,11 +161,11 @@ def test_exhaustive_nvfp4_index_codes(dev, q_len):
     check_workload(w, label="exhaustive NVFP4 index codes")
 
 
-def test_paged_b32_128k_nvfp4_index_sampled(dev):
+def test_paged_b32_128k_nvfp4_index(dev):
     """The headline shape with NVFP4 index keys, in the bench's launch
-    configuration, checked on sampled rows."""
+    configuration, every row."""
     w = synth.make_config("paged_b32_128k_nvfp4_idx", device=dev)
-    check_workload(w, rows=[0, 13, 31])
+    check_workload(w)
 
 
 def test_selection_kernel_exact_on_ties(dev):
@@ -244,9 +243,7 @@ def test_long_table_batch_1024_thread_form(dev):
     msa.msa_indexer_score(shape, cache, w.iq, bs)
     torch.cuda.synchronize()
     P = oracle.Problem.from_workload(w)
-    o, s_, b_ = out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy()
-    for row in range(w.rows):
-        check_row(P, row, o[row], s_[row], b_[row])
+    check_rows(P, out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy())
 
 
 def test_paged_permutation_invariance(dev):
@@ -312,30 +309,30 @@ def test_multi_query_nvfp4_extreme_index_queries(dev):
     check_workload(w, label="multi-query nvfp4 index keys, extreme index queries")
 
 
-def test_spec_b32_q4_128k_config_sampled(dev):
+def test_spec_b32_q4_128k_config(dev):
     """Speculative verify on the decode path: batch 32 x (128K + 4) with 4 query
-    tokens each, in the bench's launch configuration; sampled rows cover the
-    first and last query of a sequence and different sequences."""
+    tokens each, in the bench's launch configuration, all 128 rows."""
     w = synth.make_config("spec_b32_q4_128k", device=dev)
-    check_workload(w, rows=[0, 3, 4 * 13 + 1, 4 * 31 + 2, 4 * 31 + 3])
+    check_workload(w)
 
 
-def test_spec_b32_q4_128k_nvfp4_index_sampled(dev):
-    """The same with NVFP4 index keys (the f16 column scan), sampled rows."""
+def test_spec_b32_q4_128k_nvfp4_index(dev):
+    """The same with NVFP4 index keys (the f16 column scan), all 128 rows."""
     w = synth.make_config("spec_b32_q4_128k_nvfp4_idx", device=dev)
-    check_workload(w, rows=[0, 3, 4 * 13 + 1, 4 * 31 + 3])
+    check_workload(w)
 
 
-def test_verify_b2_q256_128k_config_sampled(dev):
-    """The multi-query verify chunk: 2 sequences x 256 new tokens on 128K."""
+def test_verify_b2_q256_128k_config(dev):
+    """The multi-query verify chunk: 2 sequences x 256 new tokens on 128K,
+    all 512 rows."""
     w = synth.make_config("verify_b2_q256_128k", device=dev)
-    check_workload(w, rows=[0, 1, 2, 130, 255, 256, 300, 511])
+    check_workload(w)
 
 
-def test_verify_b2_q256_128k_nvfp4_index_sampled(dev):
-    """The multi-query verify chunk with the index cache in NVFP4, sampled rows."""
+def test_verify_b2_q256_128k_nvfp4_index(dev):
+    """The multi-query verify chunk with the index cache in NVFP4, all 512 rows."""
     w = synth.make_config("verify_b2_q256_128k_nvfp4_idx", device=dev)
-    check_workload(w, rows=[0, 2, 255, 256, 383, 511])
+    check_workload(w)
 
 
 def test_multi_query_nvfp4_extreme_index_queries_long_chunk(dev):
@@ -366,9 +363,7 @@ def test_workspace_reuse_across_calls_and_shapes(dev):
         msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
         torch.cuda.synchronize()
         P = oracle.Problem.from_workload(w)
-        o, s_ = out.cpu().numpy(), sel.cpu().numpy()
-        for row in range(w.rows):
-            check_row(P, row, o[row], s_[row])
+        check_rows(P, out.cpu().numpy(), sel.cpu().numpy())
 
 
 @pytest.mark.parametrize("q_len", [1, 64])
@@ -389,9 +384,7 @@ def test_decode_without_selected_ids_output(dev, q_len):
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
     P = oracle.Problem.from_workload(w)
-    o, s_ = out2.cpu().numpy(), sel.cpu().numpy()
-    for row in range(0, w.rows, max(1, w.rows // 24)):
-        check_row(P, row, o[row], s_[row])
+    check_rows(P, out2.cpu().numpy(), sel.cpu().numpy())
 
 
 @pytest.mark.parametrize("idx,share", [("fp8", None), ("fp8", (8, 12)), ("nvfp4", (5, 9))])
@@ -414,9 +407,7 @@ def test_large_decode_batch_three_launches(dev, idx, share):
         msa.msa_decode_shared(shape, cache, msa.MsaPrefixShare.from_workload(w), w.q, w.iq, out, sel, ws)
     torch.cuda.synchronize()
     P = oracle.Problem.from_workload(w)
-    o, s_ = out.cpu().numpy(), sel.cpu().numpy()
-    for row in range(w.rows):
-        check_row(P, row, o[row], s_[row])
+    check_rows(P, out.cpu().numpy(), sel.cpu().numpy())
 
 
 @pytest.mark.parametrize("group,shared", [(8, 20), (3, 7), (2, 0)])
@@ -424,7 +415,7 @@ def test_prefix_sharing_matches_unshared(dev, group, shared):
     """Prefix sharing (groups whose first blocks map to the leader's pages):
     the shared scan's block scores, the selection and the outputs equal the
     unshared calls' bit for bit (each MFMA column is computed alone), and
-    sampled rows match the oracle.  Ragged lengths, a last group shorter than
+    every row matches the oracle.  Ragged lengths, a last group shorter than
     the others, and shared = 0 (groups that share nothing)."""
     msa = _msa()
     lens = [2600, 9000, 4000, 2561, 7000, 3333, 5000, 2700, 6000, 2900, 4400]
@@ -445,9 +436,7 @@ def test_prefix_sharing_matches_unshared(dev, group, shared):
     assert torch.equal(bs1, bs2)
     assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
     P = oracle.Problem.from_workload(w)
-    o, s_, b_ = out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy()
-    for row in (0, 1, 7, 8, 10):
-        check_row(P, row, o[row], s_[row], b_[row])
+    check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy())
 
 
 @pytest.mark.parametrize("group,shared", [(8, 20), (3, 7)])
@@ -476,15 +465,13 @@ def test_prefix_sharing_nvfp4_index_keys(dev, group, shared):
     for b, own in enumerate(w.seq_shared_blocks.cpu().tolist()):
         assert torch.equal(bs1[b, :, own:], bs2[b, :, own:]), b
     P = oracle.Problem.from_workload(w)
-    o, s_, b_ = out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy()
-    for row in range(len(lens)):
-        check_row(P, row, o[row], s_[row], b_[row])
+    check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy())
 
 
-def test_shared_b32_128k_nvfp4_index_sampled(dev):
+def test_shared_b32_128k_nvfp4_index(dev):
     """Batch 32 x 128K in groups of 8 sharing a 96K prefix with NVFP4 index
-    keys, through the shared path in the bench's launch configuration; sampled
-    rows checked against the oracle."""
+    keys, through the shared path in the bench's launch configuration; every
+    row checked against the oracle."""
     msa = _msa()
     w = synth.make_config("shared_b32_128k_nvfp4_idx", device=dev)
     shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
@@ -496,9 +483,7 @@ def test_shared_b32_128k_nvfp4_index_sampled(dev):
     msa.msa_indexer_score_shared(shape, cache, share, w.iq, bs)
     torch.cuda.synchronize()
     P = oracle.Problem.from_workload(w)
-    o, s_, b_ = out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy()
-    for row in (0, 7, 8, 31):
-        check_row(P, row, o[row], s_[row], b_[row])
+    check_rows(P, out.cpu().numpy(), sel.cpu().numpy(), bs.cpu().numpy())
 
 
 def test_prefix_sharing_general_descriptors(dev):
@@ -507,7 +492,7 @@ def test_prefix_sharing_general_descriptors(dev):
     context is the shared prefix (seq_len = shared_blocks x 128), sequences in
     no group, a padded row.  The members' block-table rows are pointed at the
     leader's pages for the shared blocks, then the shared and the unshared
-    calls must agree bit for bit, and sampled rows match the oracle."""
+    calls must agree bit for bit, and every row matches the oracle."""
     msa = _msa()
     lens = [3000, 5000, 0, 4200, 12 * 128, 6100, 2300]
     w = synth.make_workload(seq_lens=lens, zipf=1.1, layout="paged", seed=88, device=dev)
@@ -540,15 +525,13 @@ def test_prefix_sharing_general_descriptors(dev):
     assert torch.equal(bs1, bs2)
     assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
     P = oracle.Problem.from_workload(w)
-    o, s_, b_ = out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy()
-    for row in range(len(lens)):
-        check_row(P, row, o[row], s_[row], b_[row])
+    check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy())
 
 
-def test_shared_b32_128k_config_sampled(dev):
+def test_shared_b32_128k_config(dev):
     """Batch 32 x 128K in groups of 8 sharing a 96K prefix, through the shared
     path in the bench's launch configuration: bit-equal to the unshared path
-    and sampled rows checked against the oracle."""
+    and every row checked against the oracle."""
     msa = _msa()
     w = synth.make_config("shared_b32_128k", device=dev)
     shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
@@ -561,9 +544,7 @@ def test_shared_b32_128k_config_sampled(dev):
     torch.cuda.synchronize()
     assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
     P = oracle.Problem.from_workload(w)
-    o, s_ = out2.cpu().numpy(), sel2.cpu().numpy()
-    for row in (0, 7, 8, 31):
-        check_row(P, row, o[row], s_[row])
+    check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy())
 
 
 def test_graph_capture_replays(dev):
@@ -608,20 +589,27 @@ def _bits(t):
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("kv,idx,q_len", [("nvfp4", "fp8", 1), ("nvfp4", "nvfp4", 1), ("bf16", "bf16", 1),
-                                          ("nvfp4", "bf16", 3), ("nvfp4", "fp8", 3), ("bf16", "fp8", 3),
-                                          ("nvfp4", "nvfp4", 12)])
-def test_kv_insert_matches_oracle(dev, kv, idx, q_len):
+@pytest.mark.parametrize("kv,idx,q_len,scales", [("nvfp4", "fp8", 1, None), ("nvfp4", "nvfp4", 1, None),
+                                                 ("bf16", "bf16", 1, None), ("nvfp4", "bf16", 3, None),
+                                                 ("nvfp4", "fp8", 3, None), ("bf16", "fp8", 3, None),
+                                                 ("nvfp4", "nvfp4", 12, None),
+                                                 ("bf16", "bf16", 1, (0.37, 1.7, 0.61)),
+                                                 ("bf16", "bf16", 3, (3.0, 0.1, 1.3))])
+def test_kv_insert_matches_oracle(dev, kv, idx, q_len, scales):
     """msa_kv_insert writes exactly the oracle's bytes (every pool, bit for
     bit: the quantiser's integer decisions are taken in the same fp32 steps),
     touches nothing else, and the decode over the updated cache matches the
     oracle.  New tokens mix magnitudes from 1e-3 to 30, an all-zero group, a
     group of tiny values, E4M3 ties (x = midpoints) in the index keys and
-    negative values that round to zero; a padded sequence writes nothing."""
+    negative values that round to zero; a padded sequence writes nothing.
+    With `scales` (k, v, idx tensor scales that are neither 1 nor powers of
+    two) the bf16 pools store x / scale, which must round (to nearest even)."""
     msa = _msa()
     lens = [300, 0, 128 * 3, 5000 + q_len]
     w = synth.make_workload(seq_lens=lens, q_len=q_len, kv_dtype=kv, idx_dtype=idx, plant=2, layout="paged",
                             seed=50 + q_len, spare_pages=3, device=dev)
+    if scales is not None:
+        w.k_scale, w.v_scale, w.idx_scale = scales
     P = oracle.Problem.from_workload(w)
     g = torch.Generator(device="cpu").manual_seed(7)
     rows = w.rows
@@ -635,6 +623,10 @@ def test_kv_insert_matches_oracle(dev, kv, idx, q_len):
     x_new[0, :8] = torch.tensor([1.0625, -1.0625, 0.5625, 3.25, -0.0001, 2.0 ** -10, 1.5 * 2 ** -8, 448.0])
     if x_new.shape[0] > 1:
         x_new[-1, :4] = torch.tensor([1000.0, -1000.0, 0.0, -0.0])   # clamped to +-448 in FP8
+    if scales is not None:  # the quotients x / scale (fp32) are not all bf16 values: the stores round
+        for x, sc in ((k_new, scales[0]), (v_new, scales[1]), (x_new, scales[2])):
+            y = x.float() / torch.tensor(sc, dtype=torch.float32)
+            assert (y.to(torch.bfloat16).float() != y).sum() > 100
     before = {k: getattr(w, k).clone() for k in ("k", "v", "k_sf", "v_sf", "idx_k", "idx_sf") if getattr(w, k) is not None}
     shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
     msa.msa_kv_insert(shape, cache, k_new.to(dev), v_new.to(dev), x_new.to(dev))

@@ -437,6 +437,32 @@ def test_e4m3_rne_matches_torch_cast():
     assert np.array_equal(got, ref)
 
 
+def test_bf16_rne_matches_torch_cast():
+    """bf16 rounding of the insert (bf16 pools: x / scale stored as bf16)
+    against torch's float32 -> bfloat16 cast (a library round-to-nearest-even):
+    random floats over the whole exponent range, every pattern whose low 16
+    bits are exactly halfway (ties, both parities of the kept bit) and one
+    ulp either side of it, subnormals, signed zeros, the largest finite
+    values (which round to infinity past half a bf16 unit), and quotients
+    x / s with non-unit, non-power-of-two scales s as the insert forms them."""
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 0x7F800000, size=20000, dtype=np.uint32)
+    half = (bits & 0xFFFF0000) | 0x8000
+    pts = np.concatenate([bits, half, half + 1, half - 1,
+                          rng.integers(0, 0x00800000, size=2000, dtype=np.uint32),          # subnormals
+                          np.uint32([0, 0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF, 0x00008000, 0x00018000])])
+    pts = np.concatenate([pts, pts | 0x80000000]).view(np.float32)
+    x = (rng.standard_normal(4000) * np.exp(rng.uniform(-8, 8, 4000))).astype(np.float32)
+    for s in (np.float32(0.37), np.float32(1.7), np.float32(3.0), np.float32(0.1)):
+        pts = np.concatenate([pts, x / s])
+    ref = torch.from_numpy(pts).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_rne(float(y)) for y in pts], dtype=np.uint16)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, [(float(pts[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+    assert np.count_nonzero(ref == 0x7F80) > 0          # overflow to infinity was exercised
+    assert len(set(((half >> 16) & 1).tolist())) == 2     # ties with both parities of the kept bit
+
+
 def test_e2m1_rne_brute_force_and_generator():
     """E2M1 rounding: nearest magnitude by brute force (ties to the even code),
     saturating at 6; and equal to the generator's torch quantiser."""
