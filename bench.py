@@ -281,6 +281,114 @@ def run_counter_pass(args, w, copies, shape, caches):
         f"{args.steps} copies of {COPY_BYTES} B")
 
 
+OTHER_CONFIGS = ("tiny_b1_4k_bf16", "decode_b8_32k", "paged_b4_512k", "verify_b2_q256_128k")
+
+
+def time_steps(step, steps: int, warmup: int, stream):
+    """(mean us over `steps` back-to-back steps between one event pair, sorted
+    us of single steps each between its own event pair, host wall us per step)."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) / steps * 1e6
+    mean_us = e0.elapsed_time(e1) / steps * 1e3
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return mean_us, sorted(a.elapsed_time(b) * 1e3 for a, b in pairs), wall
+
+
+def pct(xs, p):
+    return round(xs[min(len(xs) - 1, int(p / 100.0 * len(xs)))], 2)
+
+
+def median(xs):
+    n = len(xs)
+    return round(xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2]), 2)
+
+
+def setup(name: str, dev, ncopies: int = 0):
+    """The workload, its input copies (see auto_copies), shape and caches."""
+    import torch
+    from block_sparse_attention_msa_amd import msa, synth
+    t0 = time.perf_counter()
+    w = synth.make_config(name, device=dev)
+    ncopies = ncopies or auto_copies(w)
+    copies = [w] + [clone_workload(w) for _ in range(max(0, ncopies - 1))]
+    torch.cuda.synchronize()
+    log(f"[bench] generated {name} x{len(copies)} in {time.perf_counter() - t0:.1f} s")
+    return w, copies, msa.MsaShape.from_workload(w), [msa.MsaCache.from_workload(c) for c in copies]
+
+
+def measure_step_and_scan(w, copies, shape, caches, steps: int, warmup: int, stream):
+    """Times the fused step and the index scan alone (same rotation of input
+    copies); returns a dict of the figures and the step's selected ids."""
+    import torch
+    from block_sparse_attention_msa_amd import msa
+    dev = w.q.device
+    ws = msa.alloc_workspace(shape, dev)
+    out, sel = msa.alloc_outputs(w)
+
+    def step(i):
+        decode_call(msa, shape, caches[i % len(copies)], copies[i % len(copies)], out, sel, ws, stream)
+
+    us_step, per_step, wall = time_steps(step, steps, warmup, stream)
+    bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+
+    def scan(i):
+        scan_call(msa, shape, caches[i % len(copies)], copies[i % len(copies)], bs, stream)
+
+    scan_us, _, _ = time_steps(scan, steps, warmup, stream)
+    return dict(us_step=us_step, per_step=per_step, wall=wall, scan_us=scan_us), sel
+
+
+def scan_roofline(w, scan_us: float):
+    """(bound, achieved, peak, unit, frac, algorithmic amount) of the index scan:
+    the bound with the longer ideal time at the published peaks."""
+    sb = scan_bytes(w)
+    fl = scan_flops(w) if w.q_len > 1 else 0.0
+    if fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > sb / (HBM_PEAK_GBPS * 1e9):
+        tf = fl / (scan_us * 1e-6) / 1e12
+        return "mfma", tf, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", tf / MFMA_BF16_PEAK_TFLOPS, fl
+    gb = sb / (scan_us * 1e-6) / 1e9
+    return "hbm", gb, HBM_PEAK_GBPS, "GB/s", gb / HBM_PEAK_GBPS, sb
+
+
+def config_summary(name: str, dev, steps: int, warmup: int, stream) -> dict:
+    """The compact record of one more workload: us per step (K-step mean and
+    single-step median), algorithmic GB/s and % of HBM peak, the index scan's
+    us and roofline fraction (MFMA for the long multi-query chunk)."""
+    import torch
+    w, copies, shape, caches = setup(name, dev)
+    m, sel = measure_step_and_scan(w, copies, shape, caches, steps, warmup, stream)
+    nb = w.nbytes_algorithmic(sel if w.q_len > 1 else None)
+    bound, ach, peak, unit, frac, amount = scan_roofline(w, m["scan_us"])
+    rec = {"us": round(m["us_step"], 2), "us_p50": median(m["per_step"]),
+           "us_p10_p90": [pct(m["per_step"], 10), pct(m["per_step"], 90)],
+           "bytes": int(nb["total"]), "GBps": round(nb["total"] / (m["us_step"] * 1e-6) / 1e9, 1),
+           "pct_hbm_peak": round(100.0 * nb["total"] / (m["us_step"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+           "scan_us": round(m["scan_us"], 2), "scan_bound": bound, "scan_achieved": round(ach, 1),
+           "scan_unit": unit, "scan_frac": round(frac, 4), "scan_share_of_step": round(m["scan_us"] / m["us_step"], 3),
+           "input_copies": len(copies)}
+    log(f"[bench] {name}: step {rec['us']} us (p50 {rec['us_p50']}), {rec['GBps']} GB/s algorithmic "
+        f"({rec['pct_hbm_peak']} %), scan {rec['scan_us']} us = {rec['scan_achieved']} {unit} ({100 * frac:.1f} % of "
+        f"{bound} peak)")
+    del w, copies, caches, sel
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +400,9 @@ def main():
                          "Infinity Cache of other inputs is read between two uses of one copy)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the compact records of the other workloads (tiny, batch-8 32K, batch-4 512K, "
+                         "2 x 256-token chunk)")
     ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
                     help="counters: only the scan kernel and a plain 512 MiB copy of known size, for rocprofv3 --pmc")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -308,71 +419,19 @@ def main():
         sys.exit(2)
 
     import torch
-    from block_sparse_attention_msa_amd import msa, synth
+    from block_sparse_attention_msa_amd import msa
 
     dev = torch.device("cuda:0")
-    t0 = time.perf_counter()
-    w = synth.make_config(args.config, device=dev)
-    ncopies = args.copies or auto_copies(w)
-    copies = [w] + [clone_workload(w) for _ in range(max(0, ncopies - 1))]
-    torch.cuda.synchronize()
-    log(f"[bench] generated {args.config} x{len(copies)} in {time.perf_counter() - t0:.1f} s "
-        f"({torch.cuda.get_device_name(0)})")
-
-    shape = msa.MsaShape.from_workload(w)
-    caches = [msa.MsaCache.from_workload(c) for c in copies]
+    log(f"[bench] device {torch.cuda.get_device_name(0)}")
+    w, copies, shape, caches = setup(args.config, dev, args.copies)
+    ncopies = len(copies)
     if args.mode == "counters":
         run_counter_pass(args, w, copies, shape, caches)
         return
-    ws = msa.alloc_workspace(shape, dev)
-    out, sel = msa.alloc_outputs(w)
     stream = torch.cuda.current_stream()
-
-    def step(i):
-        c = copies[i % len(copies)]
-        decode_call(msa, shape, caches[i % len(copies)], c, out, sel, ws, stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    us_step = ms_per_step * 1e3
-
-    # spread of single steps (a second pass with an event pair per step; the
-    # reported value is the one above, over the K steps as a whole)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i, (a, b) in enumerate(pairs):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_step = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
-
-    def pct(p):
-        return round(per_step[min(len(per_step) - 1, int(p / 100.0 * len(per_step)))], 2)
-
-    # dominant kernel: the index scan alone, same launch configuration, same rotation
-    bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
-    for i in range(args.warmup):
-        c = copies[i % len(copies)]
-        scan_call(msa, shape, caches[i % len(copies)], c, bs, stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        c = copies[i % len(copies)]
-        scan_call(msa, shape, caches[i % len(copies)], c, bs, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    scan_us = e0.elapsed_time(e1) / args.steps * 1e3
+    m, sel = measure_step_and_scan(w, copies, shape, caches, args.steps, args.warmup, stream)
+    us_step, per_step, scan_us = m["us_step"], m["per_step"], m["scan_us"]
+    ms_per_step = us_step / 1e3
 
     ceiling = read_ceiling(w, copies, stream, args.steps, args.warmup)
 
@@ -382,31 +441,18 @@ def main():
     k_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
     v_new = torch.randn(w.rows, w.num_kv_heads, 128, generator=gi, device=dev).to(torch.bfloat16)
     x_new = torch.randn(w.rows, 128, generator=gi, device=dev).to(torch.bfloat16)
-    for i in range(args.warmup):
-        msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    insert_us = e0.elapsed_time(e1) / args.steps * 1e3
+    insert_us, _, _ = time_steps(lambda i: msa.msa_kv_insert(shape, caches[i % len(copies)], k_new, v_new, x_new,
+                                                             stream), args.steps, args.warmup, stream)
 
     nb = w.nbytes_algorithmic(sel if w.q_len > 1 else None)
     step_gbps = nb["total"] / (us_step * 1e-6) / 1e9
     sb = scan_bytes(w)
-    scan_gbps = sb / (scan_us * 1e-6) / 1e9
     ctx_tokens = int(w.seq_lens.sum())
     per_tok = nb["total"] / ctx_tokens
-    log(f"[bench] step {us_step:.1f} us ({step_gbps:.0f} GB/s algorithmic, {nb['total'] / 1e6:.1f} MB), "
-        f"scan {scan_us:.1f} us ({scan_gbps:.0f} GB/s, {sb / 1e6:.1f} MB), host wall {wall / args.steps * 1e6:.1f} us"
-        + ("" if insert_us is None else f", kv insert {insert_us:.1f} us"))
+    log(f"[bench] step {us_step:.1f} us, single-step median {median(per_step)} us ({step_gbps:.0f} GB/s "
+        f"algorithmic, {nb['total'] / 1e6:.1f} MB), scan {scan_us:.1f} us ({sb / 1e6:.1f} MB), "
+        f"host wall {m['wall']:.1f} us, kv insert {insert_us:.1f} us")
 
-    # The bound is the one that gives the longer ideal time: the decode scan and
-    # short multi-query batches (a few rows per sequence) stream the keys with
-    # little arithmetic per byte; long ones are a dense contraction.
-    fl = scan_flops(w) if w.q_len > 1 else 0.0
-    mfma_bound = fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > sb / (HBM_PEAK_GBPS * 1e9)
     if w.share_members is not None:
         kname = (f"index scan + block max-pool, each shared-prefix page read once per group "
                  f"({w.idx_dtype.upper()} keys, bf16 MFMA)")
@@ -419,17 +465,11 @@ def main():
                  f"columns per sequence (bf16 MFMA)")
     else:
         kname = "multi-query index scan + causal block max-pool (bf16 MFMA)"
-    if not mfma_bound:
-        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(scan_gbps, 1),
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
-                    "traffic": scan_traffic(args.config),
-                    "launch_us": round(scan_us, 2), "algorithmic_bytes": int(sb)}
-    else:
-        tflops = fl / (scan_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": kname,
-                    "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "launch_us": round(scan_us, 2), "algorithmic_flops": int(fl)}
+    bound, ach, peak, unit, frac, amount = scan_roofline(w, scan_us)
+    roofline = {"bound": bound, "kernel": kname, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(frac, 4), "traffic": scan_traffic(args.config) if bound == "hbm" else None,
+                "launch_us": round(scan_us, 2)}
+    roofline["algorithmic_bytes" if bound == "hbm" else "algorithmic_flops"] = int(amount)
     read_ceil = None
     if ceiling is not None:
         c_us, c_bytes = ceiling
@@ -438,15 +478,20 @@ def main():
                      "scan_us_over_ceiling_us": round(scan_us / c_us, 4)}
         log(f"[bench] read ceiling {c_us:.1f} us ({read_ceil['GBps']:.0f} GB/s, {c_bytes / 1e6:.1f} MB): "
             f"the scan takes {scan_us / c_us:.3f}x the pure read of its pages")
-    if fl:
-        log(f"[bench] multi-query scan {fl / 1e9:.1f} GFLOP, {fl / (scan_us * 1e-6) / 1e12:.0f} TFLOP/s, "
-            f"{'mfma' if mfma_bound else 'hbm'}-bound")
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
         cpu = cpu_baseline(w, args.cpu_sample_seqs, us_step)
         log(f"[bench] cpu baseline {cpu['value'] / 1e6:.2f} s/step on {cpu['cores']} cores "
             f"({time.perf_counter() - t0:.1f} s)")
+    del copies, caches
+    torch.cuda.empty_cache()
+
+    others = None
+    if not args.no_other_configs and args.config == "paged_b32_128k":
+        # the other workloads, compactly (fewer steps: each is a short run)
+        n, wu = max(5, min(args.steps, 30)), max(2, min(args.warmup, 10))
+        others = {name: config_summary(name, dev, n, wu, stream) for name in OTHER_CONFIGS}
 
     rec = {
         "metric": METRIC,
@@ -463,17 +508,22 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "num_seqs": w.num_seqs, "context_tokens": int(w.seq_lens[0]),
                    "q_len": w.q_len, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": 128,
-                   "block": 128, "top_blocks": 16, "layout": w.meta.get("layout"), "input_copies": len(copies)},
+                   "block": 128, "top_blocks": 16, "layout": w.meta.get("layout"), "input_copies": ncopies},
         "achieved_GBps": round(step_gbps, 1),
         "pct_hbm_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_step": int(nb["total"]),
         "bytes_per_ctx_token": round(per_tok, 1),
         "vs_dense_fp8_kv_per_token": round(per_tok / 1024.0, 4),
-        "step_us_p10_p50_p90": [pct(10), pct(50), pct(90)],
+        "step_us_median": median(per_step),
+        "pct_hbm_peak_at_median": round(100.0 * nb["total"] / (median(per_step) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+        "step_us_p10_p50_p90": [pct(per_step, 10), median(per_step), pct(per_step, 90)],
+        "timing": "value: mean over the K back-to-back steps between one event pair; step_us_median: median of "
+                  "K single steps, each between its own event pair (includes the event overhead)",
         "roofline": roofline,
         "read_ceiling": read_ceil,
         "cpu_baseline": cpu,
-        "kv_insert_us": None if insert_us is None else round(insert_us, 2),
+        "kv_insert_us": round(insert_us, 2),
+        "other_configs": others,
     }
     print(json.dumps(rec), flush=True)
 
