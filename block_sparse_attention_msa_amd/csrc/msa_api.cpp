@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "msa.h"
 #include "msa_kernels.hpp"
 
@@ -175,6 +177,37 @@ msa_status check_scale_alignment(const msa_shape* s, const msa_cache* c, bool ne
   return MSA_OK;
 }
 
+// ---- static scratch of the allocation-free entry point --------------------
+// The workspace of msa_decode_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in symbol):
+// each device's own address is looked up once with hipGetSymbolAddress, with
+// that device current, and that pointer is what the kernels receive.
+constexpr size_t kScratchBytes = (size_t)MSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (looked up on the first call per device).
+msa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,6 +323,24 @@ static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, co
 msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
                       int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_impl(shape, cache, nullptr, q, idx_q, out, sel_blocks, workspace, workspace_bytes, stream);
+}
+
+msa_status msa_decode_noalloc(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q,
+                              float* out, int32_t* sel_blocks, hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  const size_t need = msa_workspace_size(shape);
+  if (need > kScratchBytes)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_decode_noalloc: this shape needs %zu B of scratch, the static scratch holds %zu B "
+                "(use msa_decode with a caller workspace)", need, kScratchBytes);
+  if (shape->num_seqs == 0) return decode_impl(shape, cache, nullptr, q, idx_q, out, sel_blocks, nullptr, 0, stream);
+  // the arguments are validated before the scratch lookup (the first HIP call)
+  if ((st = check_cache(shape, cache, true, true)) != MSA_OK) return st;
+  if (!q || !idx_q || !out) return fail(MSA_ERR_INVALID_ARGUMENT, "q / idx_q / out is NULL");
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != MSA_OK) return st;
+  return decode_impl(shape, cache, nullptr, q, idx_q, out, sel_blocks, ws, kScratchBytes, stream);
 }
 
 msa_status msa_decode_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,

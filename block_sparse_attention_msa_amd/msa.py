@@ -24,7 +24,8 @@ MSA_SHARE_MAX = 8  # members per prefix-sharing group
 _IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
             "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_indexer_score_shared", "msa_decode_shared",
-            "msa_status_string", "msa_last_error")
+            "msa_status_string", "msa_last_error", "msa_decode_noalloc")
+MSA_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of msa_decode_noalloc
 
 
 class MsaError(RuntimeError):
@@ -124,11 +125,12 @@ def lib():
         L.msa_sparse_attn_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_kv_insert.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp]
+        L.msa_decode_noalloc.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp]
         L.msa_indexer_score_shared.argtypes = [P(MsaShape), P(MsaCache), P(MsaPrefixShare), vp, vp, vp]
         L.msa_decode_shared.argtypes = [P(MsaShape), P(MsaCache), P(MsaPrefixShare), vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
         for f in ("msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert",
-                  "msa_indexer_score_shared", "msa_decode_shared"):
+                  "msa_indexer_score_shared", "msa_decode_shared", "msa_decode_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -188,6 +190,12 @@ def msa_decode(shape, cache, q, idx_q, out, sel_blocks, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().msa_decode(ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(idx_q), _ptr(out),
                             _ptr(sel_blocks), _ptr(workspace), nbytes, _stream(stream)), "msa_decode")
+
+
+def msa_decode_noalloc(shape, cache, q, idx_q, out, sel_blocks, stream=None):
+    """msa_decode with the library's static scratch as its workspace."""
+    _check(lib().msa_decode_noalloc(ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(idx_q), _ptr(out),
+                                    _ptr(sel_blocks), _stream(stream)), "msa_decode_noalloc")
 
 
 def msa_indexer_score_shared(shape, cache, share, idx_q, block_scores, stream=None):

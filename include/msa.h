@@ -164,6 +164,25 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
 msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
                       int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* msa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same launches, with the workspace taken from a
+ * static device array of MSA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library
+ * holds on each GPU it runs on until the process ends.  Nothing is allocated
+ * and nothing in the scratch needs clearing (every byte a step reads is
+ * written earlier in that step).  Shapes whose msa_workspace_size() exceeds
+ * the scratch return MSA_ERR_WORKSPACE_TOO_SMALL before any launch (the
+ * block scores take 16 B per (row, block of the table row), so 32 MiB holds
+ * rows x max_blocks_per_seq up to about 2M: e.g. batch 64 at 2M tokens per
+ * sequence, or 256 query rows at 512K).  Every call on one GPU shares its scratch:
+ * calls that may overlap on that GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  The first call on a device looks
+ * up its copy of the scratch (hipGetSymbolAddress); other arguments as in
+ * msa_decode. */
+#define MSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+msa_status msa_decode_noalloc(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q,
+                              float* out, int32_t* sel_blocks, hipStream_t stream);
+
 /* The write side of a decode step ("Decode execution" of the M3 post: the
  * step updates the cache before scoring; "What is new in M3.1": NVFP4 K/V,
  * E2M1 values with one E4M3 scale per 16 elements and a tensor scale): the
