@@ -66,6 +66,8 @@ struct MergeSmem {
   float o[NT / kWave][kHeadsPerGroup][kDim];
   float m[NT / kWave][kHeadsPerGroup];
   float l[NT / kWave][kHeadsPerGroup];
+  float f[NT / kWave][kHeadsPerGroup];  // exp2(m_w - M_h): the wave's rescale factor per head
+  float inv[kHeadsPerGroup];             // v_scale / sum_w f l_w per head (0 without keys)
 };
 
 template <int NT>
@@ -444,25 +446,32 @@ __device__ __forceinline__ void attn_workgroup(
   }
   __syncthreads();
 
-  // ---- merge the waves: thread -> (head, dim)
+  // ---- merge the waves: first the per (wave, head) factors f = exp2(m_w - M_h)
+  //      (0 for a wave without keys) and per head v_scale / sum_w f l_w, by one
+  //      wave (lane = 4 w + h); then each thread (head, dim) sums f o_w
+  if (wave == 0) {
+    const int w = lane >> 2, h = lane & 3;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm.u.merge.m[k][h]);
+    const float mw = w < kWaves ? sm.u.merge.m[w][h] : -INFINITY;
+    const float f = mw == -INFINITY ? 0.f : exp2_nonpos(mw - M);
+    float fl = w < kWaves ? f * sm.u.merge.l[w][h] : 0.f;
+    fl += __shfl_xor(fl, 4);
+    fl += __shfl_xor(fl, 8);
+    fl += __shfl_xor(fl, 16);
+    fl += __shfl_xor(fl, 32);
+    if (w < kWaves) sm.u.merge.f[w][h] = f;
+    if (w == 0) sm.u.merge.inv[h] = fl > 0.f ? v_scale / fl : 0.f;
+  }
+  __syncthreads();
   if (tid < kHeadsPerGroup * kDims) {
     const int h = tid / kDims;
     const int d = dbase + tid % kDims;
-    float M = -INFINITY;
+    float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][h]);
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.u.merge.m[w][h];
-        if (mw == -INFINITY) continue;
-        const float f = exp2_nonpos(mw - M);
-        o = fmaf(f, sm.u.merge.o[w][h][d], o);
-        l = fmaf(f, sm.u.merge.l[w][h], l);
-      }
-    }
-    out_row[h * kDim + d] = l > 0.f ? o * (v_scale / l) : 0.f;
+    for (int w = 0; w < kWaves; ++w) o = fmaf(sm.u.merge.f[w][h], sm.u.merge.o[w][h][d], o);
+    out_row[h * kDim + d] = o * sm.u.merge.inv[h];
   }
 }
 
