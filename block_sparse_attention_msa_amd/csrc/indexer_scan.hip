@@ -83,77 +83,99 @@ __global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_kernel(const
   scan_wave_fp8_mfma<NT>(idx_pool, block_table + (size_t)b * mbps, cm, jbeg, jend, idx_scale, lds_t[wave], lane);
 }
 
-// Prefix sharing (FP8 index keys, q_len 1) in one launch: grid rows y <
-// num_groups are the shared pass, one wave per (sharing group, shared block):
-// the group leader's page is read once and scored against the index queries
-// of all the group's members (up to 8: 32 MFMA columns); rows y >= num_groups
-// are the sequences' own blocks (the column scan, the shared blocks skipped).
-// The shared rows come first in dispatch order, so the two parts overlap.
-__global__ __launch_bounds__(kColsScanWaves * kWave, 4) void scan_shared_kernel(
-    const uint8_t* __restrict__ idx_pool, const int32_t* __restrict__ block_table,
+// Prefix sharing in one launch (FP8 or NVFP4 index keys, 1 <= q_len <= 8).
+// The first workgroups are the shared pass: workgroup (x, group) takes the
+// group's shared blocks 8x .. 8x + 7, each page read once from HBM and scored
+// against the index queries of all the group's members:
+//  * WIDE = false (at most 32 (member, query, group) columns: max_members x
+//    q_len <= 8): one wave per page, two 16-column tiles in registers (FP8: the
+//    column scan's body; NVFP4: the page dequantised exactly to bf16 in
+//    registers);
+//  * WIDE = true (up to 256 columns: 64 decode requests, or 64 / q_len
+//    requests of q_len tokens): the workgroup converts each page once into
+//    LDS and its 8 waves score it against 2 column tiles each.
+// The rest are the sequences' own blocks from block min_shared on (a lower
+// bound of every sequence's shared count, so no workgroup is spent on blocks
+// known to be shared), with the unshared scans' bodies, the shared blocks
+// skipped.  The shared pass comes first in dispatch order, so the two parts
+// overlap.  With FP8 keys every block score equals
+// the unshared scan's bit for bit (the same products and fp32 sums in the
+// same order); with NVFP4 keys the shared pages are dequantised exactly to
+// bf16 and their scores agree with the unshared scan's to fp32 rounding.
+// NT_OWN: 16-column tiles of a sequence's own (query, group) columns (0: NVFP4
+// keys at q_len 1, the decode scan's body); Q1: q_len is 1 (a compile-time
+// column count keeps the q_len 1 forms within their registers).
+template <bool NVFP4, int NT_OWN, int MINW, bool WIDE, bool Q1>
+__global__ __launch_bounds__(kColsScanWaves * kWave, MINW) void scan_shared_kernel(
+    const uint8_t* __restrict__ pool, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores,
     const int32_t* __restrict__ members, const int32_t* __restrict__ shared_blocks,
-    const int32_t* __restrict__ seq_shared_blocks, int num_groups, int mbps, float idx_scale) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_t[kColsScanWaves][2 * 2048];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int j = blockIdx.x * kColsScanWaves + wave;
-  if ((int)blockIdx.y >= num_groups) {  // a sequence's own blocks
-    const int b = blockIdx.y - num_groups;
+    const int32_t* __restrict__ seq_shared_blocks, int num_groups, int max_members, int q_len_arg, int mbps,
+    int min_shared, float idx_scale) {
+  const int q_len = Q1 ? 1 : q_len_arg;
+  // one flat grid: num_groups x xs workgroups of the shared pass, then
+  // num_seqs x xo of the own blocks (which start at block min_shared)
+  const int xs = (mbps + kColsScanWaves - 1) / kColsScanWaves;
+  const int xo = (mbps - min_shared + kColsScanWaves - 1) / kColsScanWaves;
+  const int id = blockIdx.x;
+  const bool own_row = id >= num_groups * xs;
+  const int row = own_row ? (id - num_groups * xs) / xo : id / xs;
+  const int wx = own_row ? (id - num_groups * xs) % xo : id % xs;
+  // wide: two 32 KB page buffers; otherwise 4 KB (FP8) or 1 KB (NVFP4) per wave
+  __shared__ __attribute__((aligned(16))) uint8_t lds[WIDE ? 2 * kBlock * kDim * 2 : kColsScanWaves * 2 * 2048];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int ncols_seq = q_len * kGroups;
+  if (own_row) {  // a sequence's own blocks
+    const int b = row;
+    const int j = min_shared + wx * kColsScanWaves + wave;
     if (j >= mbps || j < seq_shared_blocks[b]) return;
     const int L = seq_lens[b];
-    const SeqCols cm{iq + (size_t)b * kGroups * kDim, block_scores + (size_t)b * kGroups * mbps, mbps, kGroups, L - 1,
-                     L > 0 ? (L - 1) / kBlock + 1 : 0};
-    scan_wave_fp8_mfma<1>(idx_pool, block_table + (size_t)b * mbps, cm, j, j + 1, idx_scale, lds_t[wave], lane);
+    const uint16_t* iq_seq = iq + (size_t)b * ncols_seq * kDim;
+    float* bs_seq = block_scores + (size_t)b * ncols_seq * mbps;
+    if constexpr (NVFP4) {
+      uint8_t* lds_sc = lds + wave * (kBlock * 8);
+      if constexpr (NT_OWN == 0)  // q_len 1
+        scan_wave_nvfp4(pool, scales, block_table + (size_t)b * mbps, L, iq_seq, bs_seq, mbps, j, j + 1, idx_scale,
+                        lds_sc, lane);
+      else
+        scan_wave_nvfp4_cols<NT_OWN>(pool, scales, block_table + (size_t)b * mbps, L, q_len, iq_seq, bs_seq, mbps, j,
+                                     j + 1, idx_scale, lds_sc, lane);
+    } else {
+      const SeqCols cm{iq_seq, bs_seq, mbps, ncols_seq, L - q_len, L > 0 ? (L - 1) / kBlock + 1 : 0};
+      scan_wave_fp8_mfma<NT_OWN>(pool, block_table + (size_t)b * mbps, cm, j, j + 1, idx_scale,
+                                 lds + wave * (2 * 2048), lane);
+    }
     return;
   }
-  const int gi = blockIdx.y;
-  if (j >= min(shared_blocks[gi], mbps)) return;
-  const int32_t* mem = members + (size_t)gi * kShareMax;
-  int nmem = 0, pos0 = 0x7fffffff;
-  for (int k = 0; k < kShareMax; ++k) {  // wave-uniform
-    if (mem[k] < 0) break;
-    ++nmem;
-    pos0 = min(pos0, seq_lens[mem[k]] - 1);
-  }
+  const int gi = row;
+  const int jbeg = wx * kColsScanWaves;
+  const int jend = min(min(shared_blocks[gi], mbps), jbeg + kColsScanWaves);
+  if (jbeg >= jend) return;  // workgroup-uniform
+  // the group's members in one lane each (two loads in flight, not a chain):
+  // the member count runs to the first -1, pos0 is their least first-query position
+  const int32_t* mem = members + (size_t)gi * max_members;
+  const int mk = lane < max_members ? mem[lane] : -1;
+  const uint64_t stop = __ballot(mk < 0);
+  const int nmem = stop ? __builtin_ctzll(stop) : kWave;  // workgroup-uniform
   if (nmem == 0) return;
-  const ShareCols cm{mem, seq_lens, iq, block_scores, mbps, nmem * kGroups, pos0, 0x7fffffff};
-  scan_wave_fp8_mfma<2>(idx_pool, block_table + (size_t)mem[0] * mbps, cm, j, j + 1, idx_scale, lds_t[wave], lane);
-}
-
-// The same with NVFP4 index keys: the shared rows dequantise each shared page
-// exactly to bf16 once for the group's members (up to 32 (member, group)
-// columns); the own rows are the NVFP4 decode scan's, so those scores equal
-// the unshared call's.
-__global__ __launch_bounds__(kColsScanWaves * kWave, 4) void scan_shared_nvfp4_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores,
-    const int32_t* __restrict__ members, const int32_t* __restrict__ shared_blocks,
-    const int32_t* __restrict__ seq_shared_blocks, int num_groups, int mbps, float idx_scale) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kColsScanWaves][kBlock * 8];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int j = blockIdx.x * kColsScanWaves + wave;
-  if ((int)blockIdx.y >= num_groups) {  // a sequence's own blocks
-    const int b = blockIdx.y - num_groups;
-    if (j >= mbps || j < seq_shared_blocks[b]) return;
-    scan_wave_nvfp4(codes, scales, block_table + (size_t)b * mbps, seq_lens[b], iq + (size_t)b * kGroups * kDim,
-                    block_scores + (size_t)b * kGroups * mbps, mbps, j, j + 1, idx_scale, lds_sc[wave], lane);
-    return;
+  int p = lane < nmem ? seq_lens[mk] - q_len : 0x7fffffff;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) p = min(p, __shfl_xor(p, off));
+  const int pos0 = p;
+  const ShareCols cm{mem, seq_lens, iq, block_scores, mbps, nmem * ncols_seq, pos0, 0x7fffffff, q_len};
+  const int32_t* bt_lead = block_table + (size_t)mem[0] * mbps;
+  if constexpr (WIDE) {
+    scan_shared_wide<NVFP4>(pool, scales, bt_lead, cm, jbeg, jend, idx_scale, lds, tid);
+  } else {
+    const int j = jbeg + wave;
+    if (j >= jend) return;
+    if constexpr (NVFP4)
+      scan_wave_nvfp4_exact_cols<2>(pool, scales, bt_lead, cm, j, j + 1, idx_scale, lds + wave * (kBlock * 8), lane);
+    else
+      scan_wave_fp8_mfma<2>(pool, bt_lead, cm, j, j + 1, idx_scale, lds + wave * (2 * 2048), lane);
   }
-  const int gi = blockIdx.y;
-  if (j >= min(shared_blocks[gi], mbps)) return;
-  const int32_t* mem = members + (size_t)gi * kShareMax;
-  int nmem = 0, pos0 = 0x7fffffff;
-  for (int k = 0; k < kShareMax; ++k) {  // wave-uniform
-    if (mem[k] < 0) break;
-    ++nmem;
-    pos0 = min(pos0, seq_lens[mem[k]] - 1);
-  }
-  if (nmem == 0) return;
-  const ShareCols cm{mem, seq_lens, iq, block_scores, mbps, nmem * kGroups, pos0, 0x7fffffff};
-  scan_wave_nvfp4_exact_cols<2>(codes, scales, block_table + (size_t)mem[0] * mbps, cm, j, j + 1, idx_scale,
-                                lds_sc[wave], lane);
 }
 
 // NVFP4 index keys, 2 <= q_len <= 8: the same columns, keys dequantised
@@ -208,18 +230,57 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
 }
 
 hipError_t launch_scan_shared(const ScanArgs& a, const int32_t* members, const int32_t* shared_blocks,
-                              const int32_t* seq_shared_blocks, int num_groups, hipStream_t stream) {
-  if (a.idx_fmt == kIdxBf16 || num_groups + a.num_seqs > 65535) return hipErrorInvalidValue;
-  dim3 grid((a.mbps + kColsScanWaves - 1) / kColsScanWaves, num_groups + a.num_seqs);
+                              const int32_t* seq_shared_blocks, int num_groups, int max_members, int min_shared,
+                              int q_len, hipStream_t stream) {
+  if (a.idx_fmt == kIdxBf16 || q_len < 1 || q_len > 8 || max_members < 1 || max_members * q_len > kShareMax ||
+      min_shared < 0 || min_shared >= a.mbps)
+    return hipErrorInvalidValue;
+  const long long xs = (a.mbps + kColsScanWaves - 1) / kColsScanWaves;
+  const long long xo = (a.mbps - min_shared + kColsScanWaves - 1) / kColsScanWaves;
+  const long long wgs = num_groups * xs + (long long)a.num_seqs * xo;
+  if (wgs <= 0 || wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
+  dim3 block(kColsScanWaves * kWave);
+  const uint8_t* pool = static_cast<const uint8_t*>(a.idx_pool);
+#define MSA_SHARED_ARGS                                                                                      \
+  pool, a.idx_sf, a.block_table, a.seq_lens, a.iq, a.block_scores, members, shared_blocks, seq_shared_blocks, \
+      num_groups, max_members, q_len, a.mbps, min_shared, a.idx_scale
+  // at most 32 (member, query, group) columns: one wave per shared page
+  const bool wide = max_members * q_len * kGroups > 32;
   if (a.idx_fmt == kIdxNvfp4) {
-    scan_shared_nvfp4_kernel<<<grid, dim3(kColsScanWaves * kWave), 0, stream>>>(
-        static_cast<const uint8_t*>(a.idx_pool), a.idx_sf, a.block_table, a.seq_lens, a.iq, a.block_scores, members,
-        shared_blocks, seq_shared_blocks, num_groups, a.mbps, a.idx_scale);
-    return hipGetLastError();
+    if (!wide) {
+      if (q_len == 1)
+        scan_shared_kernel<true, 0, 4, false, true><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+      else if (q_len <= 4)
+        scan_shared_kernel<true, 1, 4, false, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+      else
+        scan_shared_kernel<true, 2, 4, false, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    } else if (q_len == 1) {
+      // 5 waves per SIMD (at most 102 VGPRs: the wide shared body takes 96, the
+      // own rows' NVFP4 decode body 80; 6 per SIMD spilled 38)
+      scan_shared_kernel<true, 0, 5, true, true><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    } else if (q_len <= 4) {
+      scan_shared_kernel<true, 1, 4, true, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    } else {
+      scan_shared_kernel<true, 2, 4, true, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    }
+  } else {
+    if (!wide) {
+      if (q_len == 1)
+        scan_shared_kernel<false, 1, 4, false, true><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+      else if (q_len <= 4)
+        scan_shared_kernel<false, 1, 4, false, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+      else
+        scan_shared_kernel<false, 2, 4, false, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    } else if (q_len == 1) {
+      scan_shared_kernel<false, 1, 4, true, true><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    } else if (q_len <= 4) {
+      scan_shared_kernel<false, 1, 4, true, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    } else {
+      scan_shared_kernel<false, 2, 4, true, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+    }
   }
-  scan_shared_kernel<<<grid, dim3(kColsScanWaves * kWave), 0, stream>>>(
-      static_cast<const uint8_t*>(a.idx_pool), a.block_table, a.seq_lens, a.iq, a.block_scores, members,
-      shared_blocks, seq_shared_blocks, num_groups, a.mbps, a.idx_scale);
+#undef MSA_SHARED_ARGS
   return hipGetLastError();
 }
 

@@ -143,11 +143,22 @@ msa_status check_share(const msa_shape* s, const msa_prefix_share* sh) {
   if (sh->num_groups == 0) return MSA_OK;
   if (!sh->members || !sh->shared_blocks || !sh->seq_shared_blocks)
     return fail(MSA_ERR_INVALID_ARGUMENT, "share members / shared_blocks / seq_shared_blocks is NULL");
-  if (s->q_len != 1) return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with q_len = %d (supported for q_len 1)", s->q_len);
+  if (s->q_len > 8)
+    return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with q_len = %d (supported for q_len 1 to 8)", s->q_len);
+  if (sh->max_members < 1 || sh->max_members > MSA_SHARE_MAX)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "share max_members = %d outside [1, %d]", sh->max_members, MSA_SHARE_MAX);
+  if ((long long)sh->max_members * s->q_len > MSA_SHARE_MAX)
+    return fail(MSA_ERR_UNSUPPORTED, "share max_members x q_len = %lld > %d (query columns per shared page)",
+                (long long)sh->max_members * s->q_len, MSA_SHARE_MAX);
   if (s->idx_dtype == MSA_IDX_BF16)
     return fail(MSA_ERR_UNSUPPORTED, "prefix sharing with bf16 index keys (supported for FP8 and NVFP4)");
-  if ((long long)sh->num_groups + s->num_seqs > 65535)
-    return fail(MSA_ERR_UNSUPPORTED, "share num_groups + num_seqs = %lld > 65535", (long long)sh->num_groups + s->num_seqs);
+  if (sh->min_shared_blocks < 0 || sh->min_shared_blocks >= s->max_blocks_per_seq)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "share min_shared_blocks = %d outside [0, %d)", sh->min_shared_blocks,
+                s->max_blocks_per_seq);
+  const long long xs = (s->max_blocks_per_seq + 7) / 8, xo = (s->max_blocks_per_seq - sh->min_shared_blocks + 7) / 8;
+  if (sh->num_groups * xs + (long long)s->num_seqs * xo > 0x7fffffffLL)
+    return fail(MSA_ERR_UNSUPPORTED, "share: %d groups and %d sequences need too many workgroups", sh->num_groups,
+                s->num_seqs);
   return MSA_OK;
 }
 
@@ -157,7 +168,7 @@ hipError_t launch_scan_any(const msa_shape* s, const msa::ScanArgs& a, const msa
                            hipStream_t stream) {
   if (!share || share->num_groups == 0) return launch_scan(s, a, stream);
   return msa::launch_scan_shared(a, share->members, share->shared_blocks, share->seq_shared_blocks,
-                                 share->num_groups, stream);
+                                 share->num_groups, share->max_members, share->min_shared_blocks, s->q_len, stream);
 }
 
 msa_status check_aligned(const void* p, size_t a, const char* what) {

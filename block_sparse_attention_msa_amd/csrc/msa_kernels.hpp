@@ -35,12 +35,14 @@ hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream);
 // FP8 index keys with 1 <= q_len <= 8, NVFP4 with 2 <= q_len <= 8: the (query, group) columns on
 // MFMA, pages streamed by waves.
 hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream);
-// Index scan with prefix sharing (FP8 or NVFP4 index keys, q_len 1), one launch: each
-// sharing group's shared pages read once for all its members (at most
-// kShareMax), the sequences' own blocks as in the column scan.
-constexpr int kShareMax = 8;
+// Index scan with prefix sharing (FP8 or NVFP4 index keys, 1 <= q_len <= 8), one
+// launch: each sharing group's shared pages read once for all its members
+// (members rows of max_members entries, max_members x q_len <= kShareMax),
+// the sequences' own blocks as in the unshared scans.
+constexpr int kShareMax = 64;
 hipError_t launch_scan_shared(const ScanArgs& a, const int32_t* members, const int32_t* shared_blocks,
-                              const int32_t* seq_shared_blocks, int num_groups, hipStream_t stream);
+                              const int32_t* seq_shared_blocks, int num_groups, int max_members, int min_shared,
+                              int q_len, hipStream_t stream);
 
 struct TopkArgs {
   const int32_t* seq_lens;

@@ -249,18 +249,29 @@ struct SeqCols {  // one sequence's q_len x 4 (query, group) columns: col = 4 i 
   int mbps, ncols, pos0, nbv;
   __device__ const uint16_t* iq(int col) const { return iq_seq + (size_t)col * kDim; }
   __device__ float* bs(int col) const { return bs_seq + (size_t)col * mbps; }
+  __device__ int brow(int col) const { return col; }  // the column's block-score row, relative to at()
+  __device__ float* at(int brow, int j) const { return bs_seq + (size_t)brow * mbps + j; }
   __device__ int last_pos(int col) const { return pos0 + col / kGroups; }
 };
-struct ShareCols {  // a sharing group's members x 4 (member, group) columns, q_len 1: col = 4 k + g
-  const int32_t* members;  // [8] sequence ids of the group (-1 padded)
+struct ShareCols {  // a sharing group's members x q_len x 4 columns: col = (k q_len + i) 4 + g
+  const int32_t* members;  // the group's sequence ids (-1 padded)
   const int32_t* seq_lens;
-  const uint16_t* iq_all;  // [num_seqs][4][128]
-  float* bs_all;           // [num_seqs][4][mbps]
-  int mbps, ncols, pos0, nbv;
-  __device__ size_t row(int col) const { return (size_t)members[col / kGroups] * kGroups + col % kGroups; }
+  const uint16_t* iq_all;  // [num_seqs * q_len][4][128]
+  float* bs_all;           // [num_seqs * q_len][4][mbps]
+  int mbps, ncols, pos0, nbv, q_len;
+  // (query row, group) of column col: member k, query i, group g
+  __device__ size_t row(int col) const {
+    const int per = kGroups * q_len;
+    return (size_t)members[col / per] * per + col % per;
+  }
   __device__ const uint16_t* iq(int col) const { return iq_all + row(col) * kDim; }
   __device__ float* bs(int col) const { return bs_all + row(col) * mbps; }
-  __device__ int last_pos(int col) const { return seq_lens[members[col / kGroups]] - 1; }
+  __device__ int brow(int col) const { return (int)row(col); }
+  __device__ float* at(int brow, int j) const { return bs_all + (size_t)brow * mbps + j; }
+  __device__ int last_pos(int col) const {
+    const int per = kGroups * q_len;
+    return seq_lens[members[col / per]] - q_len + (col % per) / kGroups;
+  }
 };
 
 template <int NT, class Cols>
@@ -273,12 +284,12 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
   const int ncols = cm.ncols;
   const int pos0 = cm.pos0;  // smallest query position of the columns
   // this lane's columns 16t + n: block-score rows and query positions
-  float* bsp[NT];
+  int brow[NT];
   int lastp[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int col = 16 * t + n;
-    bsp[t] = col < ncols ? cm.bs(col) : nullptr;
+    brow[t] = col < ncols ? cm.brow(col) : 0;
     lastp[t] = col < ncols ? cm.last_pos(col) : 0;
   }
   // LDS offsets of this lane's tile writes (token 8hh + lane/8, chunk lane%8)
@@ -304,7 +315,7 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
     if (j >= nbv) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        if (c == 0 && 16 * t + n < ncols) bsp[t][j] = -INFINITY;
+        if (c == 0 && 16 * t + n < ncols) *cm.at(brow[t], j) = -INFINITY;
       continue;
     }
     const int64_t page = bt_row[j];
@@ -359,7 +370,7 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
     for (int t = 0; t < NT; ++t) {
       float x = fmaxf(m[t], __shfl_xor(m[t], 16));
       x = fmaxf(x, __shfl_xor(x, 32));
-      if (c == 0 && 16 * t + n < ncols) bsp[t][j] = x * idx_scale;
+      if (c == 0 && 16 * t + n < ncols) *cm.at(brow[t], j) = x * idx_scale;
     }
     __builtin_amdgcn_wave_barrier();  // the next block rewrites this wave's tiles
   }
@@ -507,8 +518,12 @@ __device__ __forceinline__ void scan_wave_nvfp4_cols(const uint8_t* __restrict__
   }
 }
 
+}  // namespace msa
+
+namespace msa {
+
 // NVFP4 index keys with the columns of a column map (the members of a
-// prefix-sharing group, q_len 1): the page's codes arrive as in
+// prefix-sharing group, at most 32 columns): the page's codes arrive as in
 // scan_wave_nvfp4_cols, but each code x E4M3 group scale is converted exactly
 // to bf16 (E2M1 -> f32, times the scale in f32, -> bf16: at most 6
 // significant bits, so every step is exact) and the scores run on bf16 MFMAs
@@ -526,12 +541,12 @@ __device__ __forceinline__ void scan_wave_nvfp4_exact_cols(const uint8_t* __rest
   const int n = lane & 15;
   const int ncols = cm.ncols;
   const int pos0 = cm.pos0;  // smallest query position of the columns
-  float* bsp[NT];
+  int brow[NT];
   int lastp[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int col = 16 * t + n;
-    bsp[t] = col < ncols ? cm.bs(col) : nullptr;
+    brow[t] = col < ncols ? cm.brow(col) : 0;
     lastp[t] = col < ncols ? cm.last_pos(col) : 0;
   }
   // B operands: column 16t + n, dims 32c + 8s .. + 7 for step s (the A side's
@@ -551,7 +566,7 @@ __device__ __forceinline__ void scan_wave_nvfp4_exact_cols(const uint8_t* __rest
     if (j >= nbv) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        if (c == 0 && 16 * t + n < ncols) bsp[t][j] = -INFINITY;
+        if (c == 0 && 16 * t + n < ncols) *cm.at(brow[t], j) = -INFINITY;
       continue;
     }
     const int64_t page = bt_row[j];
@@ -606,9 +621,172 @@ __device__ __forceinline__ void scan_wave_nvfp4_exact_cols(const uint8_t* __rest
     for (int t = 0; t < NT; ++t) {
       float x = fmaxf(m[t], __shfl_xor(m[t], 16));
       x = fmaxf(x, __shfl_xor(x, 32));
-      if (c == 0 && 16 * t + n < ncols) bsp[t][j] = x * idx_scale;
+      if (c == 0 && 16 * t + n < ncols) *cm.at(brow[t], j) = x * idx_scale;
     }
     __builtin_amdgcn_wave_barrier();  // the next page rewrites this wave's scales
+  }
+}
+
+}  // namespace msa
+
+namespace msa {
+
+// Shared-prefix pages with more columns than one wave's registers hold: up to
+// 256 (member, query, group) columns of one sharing group (64 decode
+// requests, or 64 / q_len requests of q_len query tokens).  The 8 waves of a
+// workgroup take the group's pages [jbeg, jend) one at a time:
+//  * the page is loaded once (FP8: 32 contiguous bytes per thread; NVFP4: 16 B
+//    of codes and the 2 scale bytes of those 32 dims) and converted once,
+//    exactly, to bf16 (FP8: E4M3 -> bf16; NVFP4: E2M1 -> f32, times the E4M3
+//    group scale, -> bf16, at most 6 significant bits) into a 32 KB LDS copy
+//    in the MFMA operand order: 16-B chunk k (dims 8k .. 8k + 7) of token t at
+//    t * 256 + 16 (k ^ (t % 16)), so each 8 lanes of a column read touch 8
+//    distinct 16-B slots;
+//  * wave w scores it against its column tiles w and w + 8 (B operands in
+//    registers, loaded once): MFMA step s = 2h + u takes dims 64h + 16c + 8u +
+//    e at K index 8c + e, as in the FP8 column scan, so with FP8 keys every
+//    column's products and fp32 sums are those of the unshared scan, operation
+//    for operation;
+//  * the next page's raw bytes are loaded while the current one is scored.
+// The page is read from HBM and converted once for all the group's requests,
+// whatever their number.
+constexpr int kWideWaves = 8;
+constexpr int kWideTiles = 2;   // column tiles per wave: 16 x 2 x 8 = 256 columns
+
+template <bool NVFP4>
+struct WideRaw {  // one thread's share of a page: 32 dims of one token
+  u32x4 a, b;     // FP8: 32 bytes; NVFP4: a = 16 B of codes, b.x = the 2 scale bytes
+};
+
+template <bool NVFP4>
+__device__ __forceinline__ WideRaw<NVFP4> wide_load(const uint8_t* __restrict__ pool, const uint8_t* __restrict__ scales,
+                                                    int64_t page, int tid) {
+  WideRaw<NVFP4> r;
+  if constexpr (NVFP4) {
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + page * (kBlock * kDim / 2) + 16 * tid));
+    const uint32_t sw = *reinterpret_cast<const uint16_t*>(scales + page * (kBlock * 8) + 2 * tid);
+    r.b = u32x4{sw, 0u, 0u, 0u};
+  } else {
+    const uint8_t* src = pool + page * (kBlock * kDim) + 32 * tid;
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16));
+  }
+  return r;
+}
+
+// Thread tid holds token tid / 4, dims 32 (tid % 4) .. + 31: converts them to
+// bf16 and stores chunks 4 (tid % 4) .. + 3 of that token's LDS row.
+template <bool NVFP4>
+__device__ __forceinline__ void wide_store(const WideRaw<NVFP4>& r, uint8_t* lds, int tid) {
+  const int t = tid >> 2, qd = tid & 3;
+  uint32_t w[16];  // 32 bf16
+  if constexpr (NVFP4) {
+    const f32x2 sf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.b.x, 1.0f, false);  // groups 2 qd, 2 qd + 1
+    const uint32_t c4[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float g = s < 2 ? sf.x : sf.y;
+      const f32x2 e0 = e2m1x2_to_f32x2<0>(c4[s]), e1 = e2m1x2_to_f32x2<1>(c4[s]);
+      const f32x2 e2 = e2m1x2_to_f32x2<2>(c4[s]), e3 = e2m1x2_to_f32x2<3>(c4[s]);
+      const bf16x2 p0 = {(__bf16)(e0.x * g), (__bf16)(e0.y * g)}, p1 = {(__bf16)(e1.x * g), (__bf16)(e1.y * g)};
+      const bf16x2 p2 = {(__bf16)(e2.x * g), (__bf16)(e2.y * g)}, p3 = {(__bf16)(e3.x * g), (__bf16)(e3.y * g)};
+      w[4 * s + 0] = __builtin_bit_cast(uint32_t, p0);
+      w[4 * s + 1] = __builtin_bit_cast(uint32_t, p1);
+      w[4 * s + 2] = __builtin_bit_cast(uint32_t, p2);
+      w[4 * s + 3] = __builtin_bit_cast(uint32_t, p3);
+    }
+  } else {
+    const uint32_t b8[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      w[2 * d] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(b8[d]));
+      w[2 * d + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(b8[d]));
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int k = 4 * qd + m;
+    *reinterpret_cast<u32x4*>(lds + t * 256 + 16 * (k ^ (t & 15))) = u32x4{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
+  }
+}
+
+// Block scores of the shared pages [jbeg, jend) of one sharing group for all
+// of the column map's columns; every thread of the 512-thread workgroup calls
+// it (it synchronises the workgroup).  lds: 2 x 32 KB (page j in buffer j % 2,
+// so one barrier per page orders both the stores and the reuse); the raw bytes
+// of the next two pages are in flight while a page is scored.
+template <bool NVFP4>
+__device__ __forceinline__ void scan_shared_wide(const uint8_t* __restrict__ pool, const uint8_t* __restrict__ scales,
+                                                 const int32_t* __restrict__ bt_row, const ShareCols& cm, int jbeg,
+                                                 int jend, float idx_scale, uint8_t* lds, int tid) {
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int ncols = cm.ncols;
+  bool has[kWideTiles];
+  int brow[kWideTiles];
+  int lastp[kWideTiles];
+  bf16x8 qb[kWideTiles][4];
+#pragma unroll
+  for (int q = 0; q < kWideTiles; ++q) {
+    const int col = 16 * (wave + kWideWaves * q) + n;
+    has[q] = 16 * (wave + kWideWaves * q) < ncols;  // wave-uniform
+    brow[q] = col < ncols ? cm.brow(col) : -1;
+    lastp[q] = col < ncols ? cm.last_pos(col) : 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int d = 64 * (s >> 1) + 16 * c + 8 * (s & 1);
+      const uint4 w = col < ncols ? *reinterpret_cast<const uint4*>(cm.iq(col) + d) : make_uint4(0, 0, 0, 0);
+      qb[q][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  // A operand chunks of this lane: token 16T + n, chunk 8h + 2c + u for step s = 2h + u
+  int rd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) rd[s] = n * 256 + 16 * ((8 * (s >> 1) + 2 * c + (s & 1)) ^ n);
+
+  WideRaw<NVFP4> raw0 = wide_load<NVFP4>(pool, scales, bt_row[jbeg], tid);
+  WideRaw<NVFP4> raw1 = raw0;
+  if (jbeg + 1 < jend) raw1 = wide_load<NVFP4>(pool, scales, bt_row[jbeg + 1], tid);
+  for (int j = jbeg; j < jend; ++j) {
+    uint8_t* buf = lds + (j & 1) * (kBlock * kDim * 2);
+    wide_store<NVFP4>(raw0, buf, tid);
+    raw0 = raw1;
+    if (j + 2 < jend) raw1 = wide_load<NVFP4>(pool, scales, bt_row[j + 2], tid);
+    __syncthreads();  // page j stored; every wave is done with page j - 2's buffer
+    if (!has[0]) continue;  // wave-uniform: this wave only converts
+    const bool full = (j + 1) * kBlock - 1 <= cm.pos0;  // every column sees the whole block
+    float m[kWideTiles];
+#pragma unroll
+    for (int q = 0; q < kWideTiles; ++q) m[q] = -INFINITY;
+#pragma unroll 2
+    for (int T = 0; T < 8; ++T) {
+      bf16x8 ka[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + T * 4096 + rd[s]));
+#pragma unroll
+      for (int q = 0; q < kWideTiles; ++q) {
+        if (!has[q]) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[q][s], acc, 0, 0, 0);
+        if (full) {
+          m[q] = fmaxf(m[q], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        } else {
+          const int vis = lastp[q] + 1 - j * kBlock;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[q] = fmaxf(m[q], 16 * T + 4 * c + i < vis ? acc[i] : -INFINITY);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kWideTiles; ++q) {
+      if (!has[q]) continue;
+      float x = fmaxf(m[q], __shfl_xor(m[q], 16));
+      x = fmaxf(x, __shfl_xor(x, 32));
+      if (c == 0 && brow[q] >= 0) *cm.at(brow[q], j) = x * idx_scale;
+    }
   }
 }
 

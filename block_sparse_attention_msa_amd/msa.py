@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("MSA_LIB_PATH") or os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARGUMENT, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_HIP = range(5)
 MSA_KV_BF16, MSA_KV_NVFP4 = 0, 1
 MSA_IDX_BF16, MSA_IDX_FP8_E4M3, MSA_IDX_NVFP4 = 0, 1, 2
-MSA_SHARE_MAX = 8  # members per prefix-sharing group
+MSA_SHARE_MAX = 64  # most (member x query token) per prefix-sharing group
 _IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
             "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_indexer_score_shared", "msa_decode_shared",
@@ -71,26 +71,34 @@ class MsaCache(ctypes.Structure):
 
 
 class MsaPrefixShare(ctypes.Structure):
-    """Prefix-sharing groups (msa_prefix_share): device int32 arrays."""
-    _fields_ = [("num_groups", ctypes.c_int32), ("members", ctypes.c_void_p), ("shared_blocks", ctypes.c_void_p),
-                ("seq_shared_blocks", ctypes.c_void_p)]
+    """Prefix-sharing groups (msa_prefix_share): device int32 arrays; members
+    [groups][max_members], its row length is max_members."""
+    _fields_ = [("num_groups", ctypes.c_int32), ("max_members", ctypes.c_int32),
+                ("min_shared_blocks", ctypes.c_int32), ("members", ctypes.c_void_p),
+                ("shared_blocks", ctypes.c_void_p), ("seq_shared_blocks", ctypes.c_void_p)]
 
     @classmethod
-    def from_tensors(cls, *, members, shared_blocks, seq_shared_blocks) -> "MsaPrefixShare":
+    def from_tensors(cls, *, members, shared_blocks, seq_shared_blocks, min_shared_blocks=0) -> "MsaPrefixShare":
+        """min_shared_blocks: a lower bound of seq_shared_blocks over all
+        sequences (host-side; 0 is always valid)."""
         for name, t in (("members", members), ("shared_blocks", shared_blocks),
                         ("seq_shared_blocks", seq_shared_blocks)):
             if t.dtype != torch.int32:
                 raise TypeError(f"{name} must be int32")
-        c = cls(int(shared_blocks.numel()), _ptr(members), _ptr(shared_blocks), _ptr(seq_shared_blocks))
+        if members.dim() != 2 or members.shape[0] != shared_blocks.numel():
+            raise ValueError("members must be [num_groups][max_members]")
+        c = cls(int(shared_blocks.numel()), int(members.shape[1]), int(min_shared_blocks), _ptr(members),
+                _ptr(shared_blocks), _ptr(seq_shared_blocks))
         c._keep = (members, shared_blocks, seq_shared_blocks)
         return c
 
     @classmethod
     def from_workload(cls, w) -> "MsaPrefixShare":
         if w.share_members is None:
-            return cls(0, None, None, None)
+            return cls(0, 1, 0, None, None, None)
         return cls.from_tensors(members=w.share_members, shared_blocks=w.share_blocks,
-                                seq_shared_blocks=w.seq_shared_blocks)
+                                seq_shared_blocks=w.seq_shared_blocks,
+                                min_shared_blocks=w.meta.get("min_shared_blocks", 0))
 
 
 def _ptr(t):

@@ -198,7 +198,7 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     shared_bias_iq: (q_len > 1) index queries are u_{b,g} + N(0,1), with u the
     bias direction shared by the chunk.
     share (group_size, shared_blocks): consecutive sequences form groups of
-    group_size (at most 8) whose first shared_blocks logical blocks map to the
+    group_size (at most 64 / q_len) whose first shared_blocks logical blocks map to the
     leader's (the group's first sequence's) pages: a shared prefix, keys and
     K/V included.  Every member must see all shared tokens.
     Index-key rows past a sequence's end are filled with a poison value that
@@ -217,7 +217,7 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     groups = []
     if share is not None:
         gsize, sblocks = int(share[0]), int(share[1])
-        assert 1 <= gsize <= 8 and sblocks >= 0
+        assert 1 <= gsize and gsize * q_len <= 64 and sblocks >= 0
         for g0 in range(0, S, gsize):
             members = list(range(g0, min(S, g0 + gsize)))
             if len(members) < 2:  # a group of one shares nothing
@@ -362,7 +362,10 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
                     q=q, iq=iq, idx_k=idx_pool, k=k, v=v, k_sf=k_sf, v_sf=v_sf,
                     block_table=bt.to(dev), seq_lens=torch.tensor(seq_lens, dtype=torch.int32, device=dev),
                     meta=dict(seed=seed, layout=layout, plant=plant, zipf=zipf, idx_dist=idx_dist,
-                              planted=planted, share=share),
+                              planted=planted, share=share,
+                              # lower bound of every sequence's shared blocks (0 unless all share)
+                              min_shared_blocks=(int(share[1]) if share is not None and
+                                                 sum(len(m) for m in groups) == S else 0)),
                     idx_sf=idx_sf, **_share_tensors(groups, share, S, dev))
 
 
@@ -370,7 +373,7 @@ def _share_tensors(groups, share, S, dev) -> dict:
     """The prefix-sharing descriptors of make_workload(share=...)."""
     if share is None:
         return {}
-    members = torch.full((len(groups), 8), -1, dtype=torch.int32)   # MSA_SHARE_MAX slots
+    members = torch.full((len(groups), int(share[0])), -1, dtype=torch.int32)   # rows of group_size slots
     for gi, mem in enumerate(groups):
         members[gi, :len(mem)] = torch.tensor(mem, dtype=torch.int32)
     sblocks = int(share[1])
@@ -408,6 +411,12 @@ CONFIGS = {
     # the five above
     "shared_b32_128k": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", share=(8, 768), seed=6),
     # the same with the index cache in NVFP4
+    # 64 requests sharing one 96K-token prompt prefix in a single group: each
+    # shared page read and converted once for all 64 (256 (request, group)
+    # index queries)
+    "shared_b64_128k": dict(seq_lens=[131072] * 64, zipf=1.1, layout="paged", share=(64, 768), seed=7),
+    "shared_b64_128k_nvfp4_idx": dict(seq_lens=[131072] * 64, zipf=1.1, layout="paged", share=(64, 768),
+                                      idx_dtype="nvfp4", seed=7),
     "shared_b32_128k_nvfp4_idx": dict(seq_lens=[131072] * 32, zipf=1.1, layout="paged", share=(8, 768),
                                       idx_dtype="nvfp4", seed=6),
     # the same with the index cache in NVFP4: the AMD serving setting of the

@@ -208,25 +208,39 @@ msa_status msa_kv_insert(const msa_shape* shape, const msa_cache* cache, const v
 
 /* Prefix sharing ("NVFP4 MSA kernel" of the vLLM MiniMax-M3.1-Flash post: a
  * shared-prefix page is dequantised once for up to 64 requests that share
- * it; here the index scan reads such a page once for the group's members and
- * scores it against all their index queries).  Sequences form sharing groups
- * of at most MSA_SHARE_MAX; in a group, the first shared_blocks[g] logical
- * blocks of every member map to the same physical pages as the first
- * member's (its leader's) block_table row.  Device arrays, read by the
- * kernels, unchecked like seq_lens (preconditions):
- *   members           int32 [num_groups][MSA_SHARE_MAX] sequence ids, -1 padded
+ * it; here the index scan reads such a page once for the group's members,
+ * converts it once and scores it against all their index queries).
+ * Sequences form sharing groups; in a group, the first shared_blocks[g]
+ * logical blocks of every member map to the same physical pages as the first
+ * member's (its leader's) block_table row.  Host fields:
+ *   num_groups        number of groups; 0 means no sharing (the arrays may
+ *                     then be NULL)
+ *   max_members       row stride of `members` and the most members a group
+ *                     may hold: 1 .. MSA_SHARE_MAX, with max_members x q_len
+ *                     <= MSA_SHARE_MAX (a shared page is scored against at
+ *                     most 64 query tokens x 4 groups = 256 index queries)
+ *   min_shared_blocks a lower bound of seq_shared_blocks[b] over ALL
+ *                     sequences, 0 .. max_blocks_per_seq - 1 (0 is always
+ *                     valid, and is the value when some sequence is in no
+ *                     group): the scan of the sequences' own blocks starts at
+ *                     this block, so the workgroups of blocks known to be
+ *                     shared are never launched.  A value above the true
+ *                     minimum leaves blocks unscored (precondition).
+ * Device arrays, read by the kernels, unchecked like seq_lens (preconditions):
+ *   members           int32 [num_groups][max_members] sequence ids, -1 padded
  *                     after the last member; a sequence is in at most one group
  *   shared_blocks     int32 [num_groups], each 0 ..
  *                     (seq_lens[b] - q_len + 1) / 128 for every member b: every
- *                     shared token is visible to the member's query
+ *                     shared token is visible to all the member's queries
  *   seq_shared_blocks int32 [num_seqs]: shared_blocks of the sequence's group,
  *                     0 for a sequence in no group
- * num_groups 0 means no sharing (the arrays may then be NULL).  Block scores,
- * selection and outputs equal those of the unshared calls bit for bit (FP8
- * index keys; NVFP4 keys: see below). */
-#define MSA_SHARE_MAX 8
+ * With FP8 index keys block scores, selection and outputs equal those of the
+ * unshared calls bit for bit; with NVFP4 keys see below. */
+#define MSA_SHARE_MAX 64
 typedef struct {
   int32_t num_groups;
+  int32_t max_members;
+  int32_t min_shared_blocks;
   const int32_t* members;
   const int32_t* shared_blocks;
   const int32_t* seq_shared_blocks;
@@ -234,11 +248,11 @@ typedef struct {
 
 /* msa_indexer_score and msa_decode with prefix sharing (one scan launch that
  * scores each group's shared blocks once and every sequence's own blocks).
- * Supported for q_len 1 with FP8 or NVFP4 index keys (MSA_ERR_UNSUPPORTED
+ * Supported for q_len 1 to 8 with FP8 or NVFP4 index keys (MSA_ERR_UNSUPPORTED
  * otherwise).  With NVFP4 keys the shared pages are dequantised exactly to
- * bf16 for the group's members (exact products, fp32 sums), a summation order
- * other than the unshared scan's: those block scores agree with the unshared
- * call's to fp32 rounding, the sequences' own blocks bit for bit;
+ * bf16 once for the group's members (exact products, fp32 sums), a summation
+ * order other than the unshared scan's: those block scores agree with the
+ * unshared call's to fp32 rounding, the sequences' own blocks bit for bit;
  * other arguments as in the unshared calls. */
 msa_status msa_indexer_score_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
                                     const void* idx_q, float* block_scores, hipStream_t stream);

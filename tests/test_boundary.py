@@ -129,27 +129,42 @@ def test_nvfp4_index_keys_validation():
 
 
 def test_prefix_share_validation():
-    """The shared entry points: a NULL descriptor, a negative group count or a
-    missing array is INVALID_ARGUMENT; sharing beyond q_len 1 or with bf16
-    index keys is UNSUPPORTED; FP8 and NVFP4 keys pass on to the next check
-    (here the short workspace), and so do zero groups (the unshared call)."""
+    """The shared entry points: a NULL descriptor, a negative group count, a
+    missing array or a member row length outside 1..64 is INVALID_ARGUMENT;
+    sharing beyond q_len 8, with bf16 index keys, or with more than 64 (member
+    x query token) columns per group is UNSUPPORTED; FP8 and NVFP4 keys at
+    q_len 1..8 within the limit pass on to the next check (here the short
+    workspace), and so do zero groups (the unshared call)."""
     L = msa.lib()
     s = _shape()
-    sh = msa.MsaPrefixShare(2, FAKE, FAKE, FAKE)
+    sh = msa.MsaPrefixShare(2, 8, 0, FAKE, FAKE, FAKE)
 
     def dec(shape, share, nbytes=1 << 30):
         return L.msa_decode_shared(ctypes.byref(shape), ctypes.byref(_cache()), share, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    nbytes, None)
 
     assert dec(s, None) == msa.MSA_ERR_INVALID_ARGUMENT
-    assert dec(s, ctypes.byref(msa.MsaPrefixShare(-1, FAKE, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
-    assert dec(s, ctypes.byref(msa.MsaPrefixShare(2, None, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert dec(s, ctypes.byref(msa.MsaPrefixShare(-1, 8, 0, FAKE, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert dec(s, ctypes.byref(msa.MsaPrefixShare(2, 8, 0, None, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
     assert "members" in msa.last_error()
-    assert dec(_shape(q_len=2), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
+    for bad in (0, -3, 65):
+        assert dec(s, ctypes.byref(msa.MsaPrefixShare(2, bad, 0, FAKE, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
+        assert "max_members" in msa.last_error()
+    assert dec(_shape(q_len=9, max_blocks_per_seq=8), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
+    assert dec(_shape(q_len=9), ctypes.byref(msa.MsaPrefixShare(2, 1, 0, FAKE, FAKE, FAKE))) == msa.MSA_ERR_UNSUPPORTED
+    assert dec(_shape(q_len=4), ctypes.byref(msa.MsaPrefixShare(2, 17, 0, FAKE, FAKE, FAKE))) == msa.MSA_ERR_UNSUPPORTED
     assert dec(_shape(idx_dtype=msa.MSA_IDX_BF16), ctypes.byref(sh)) == msa.MSA_ERR_UNSUPPORTED
     for idx in (msa.MSA_IDX_FP8_E4M3, msa.MSA_IDX_NVFP4):
         assert dec(_shape(idx_dtype=idx), ctypes.byref(sh), nbytes=16) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
-    assert dec(s, ctypes.byref(msa.MsaPrefixShare(0, None, None, None)), nbytes=16) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+        for q_len, mm in ((1, 64), (2, 32), (4, 16), (8, 8)):
+            share = msa.MsaPrefixShare(2, mm, 0, FAKE, FAKE, FAKE)
+            assert dec(_shape(idx_dtype=idx, q_len=q_len), ctypes.byref(share), nbytes=16) == \
+                msa.MSA_ERR_WORKSPACE_TOO_SMALL, (idx, q_len, mm, msa.last_error())
+    for bad in (-1, 8):  # min_shared_blocks outside [0, max_blocks_per_seq)
+        assert dec(s, ctypes.byref(msa.MsaPrefixShare(2, 8, bad, FAKE, FAKE, FAKE))) == msa.MSA_ERR_INVALID_ARGUMENT
+        assert "min_shared_blocks" in msa.last_error()
+    assert dec(s, ctypes.byref(msa.MsaPrefixShare(0, 1, 0, None, None, None)), nbytes=16) == \
+        msa.MSA_ERR_WORKSPACE_TOO_SMALL
     assert L.msa_indexer_score_shared(ctypes.byref(s), ctypes.byref(_cache()), None, FAKE, FAKE, None) == \
         msa.MSA_ERR_INVALID_ARGUMENT
 

@@ -439,6 +439,73 @@ def test_prefix_sharing_matches_unshared(dev, group, shared):
     check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy())
 
 
+def _shared_vs_unshared(msa, w, dev, bit_equal):
+    """Runs the shared and the unshared index scan and decode on w; with
+    bit_equal (FP8 keys) every block score, id and output must be identical,
+    otherwise (NVFP4 keys) the sequences' own blocks must be; every row is
+    checked against the oracle (block scores, ids, outputs)."""
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_workload(w)
+    bs1 = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
+    bs2 = torch.full_like(bs1, float("nan"))
+    msa.msa_indexer_score(shape, cache, w.iq, bs1)
+    msa.msa_indexer_score_shared(shape, cache, share, w.iq, bs2)
+    out1, sel1 = msa.alloc_outputs(w)
+    out2, sel2 = msa.alloc_outputs(w)
+    ws = msa.alloc_workspace(shape, dev)
+    msa.msa_decode(shape, cache, w.q, w.iq, out1, sel1, ws)
+    msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out2, sel2, ws)
+    torch.cuda.synchronize()
+    if bit_equal:
+        assert torch.equal(bs1, bs2)
+        assert torch.equal(sel1, sel2) and torch.equal(out1, out2)
+    else:
+        for b, own in enumerate(w.seq_shared_blocks.cpu().tolist()):
+            rows = slice(b * w.q_len, (b + 1) * w.q_len)
+            assert torch.equal(bs1[rows, :, own:], bs2[rows, :, own:]), b
+    P = oracle.Problem.from_workload(w)
+    ties, worst = check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy(), bs2.cpu().numpy())
+    _say(f"[parity] shared vs unshared: rows={w.rows} near_ties={ties} max_abs_err={worst:.3g}")
+
+
+@pytest.mark.parametrize("idx", ["fp8", "nvfp4"])
+def test_prefix_sharing_64_members(dev, idx):
+    """A sharing group of 64 decode requests (256 (member, group) columns: 16
+    MFMA column tiles over the 8 waves that score each converted page) plus a
+    group of 4 in the same launch: FP8 keys bit-equal to the
+    unshared calls, NVFP4 keys their own blocks bit-equal; every row against
+    the oracle.  Ragged lengths, all longer than the 20-block shared prefix."""
+    msa = _msa()
+    lens = [2600 + (397 * i) % 5000 for i in range(64)] + [3000, 2700, 4100, 2561]
+    w = synth.make_workload(seq_lens=lens[:64], share=(64, 20), zipf=1.1, layout="paged", idx_dtype=idx,
+                            seed=130, device=dev)
+    assert w.share_members.shape == (1, 64) and (w.share_members >= 0).all()
+    _say(f"[parity] 64-member sharing group, {idx} index keys")
+    _shared_vs_unshared(msa, w, dev, bit_equal=idx == "fp8")
+    # groups of 64 and 4 in one launch
+    w2 = synth.make_workload(seq_lens=lens, share=(64, 20), zipf=1.1, layout="paged", idx_dtype=idx, seed=131,
+                             device=dev)
+    _say(f"[parity] groups of 64 and 4, {idx} index keys")
+    _shared_vs_unshared(msa, w2, dev, bit_equal=idx == "fp8")
+
+
+@pytest.mark.parametrize("idx", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("q_len,group", [(2, 32), (4, 16), (4, 3), (8, 8), (5, 2)])
+def test_prefix_sharing_multi_query(dev, idx, q_len, group):
+    """Prefix sharing with q_len 2..8 query tokens per request (speculative
+    verify): groups of up to 64 / q_len members, (member, query, group)
+    columns 4 x q_len per member; each query row keeps its own causal
+    position.  FP8 keys bit-equal to the unshared calls; NVFP4 keys their own
+    blocks bit-equal; every row against the oracle."""
+    msa = _msa()
+    n = group + 3
+    lens = [q_len + 2600 + (331 * i) % 4000 for i in range(n)]
+    w = synth.make_workload(seq_lens=lens, q_len=q_len, share=(group, 18), zipf=1.1, layout="paged",
+                            idx_dtype=idx, seed=140 + q_len + group, device=dev)
+    _say(f"[parity] sharing q_len={q_len} groups of {group}, {idx} index keys")
+    _shared_vs_unshared(msa, w, dev, bit_equal=idx == "fp8")
+
+
 @pytest.mark.parametrize("group,shared", [(8, 20), (3, 7)])
 def test_prefix_sharing_nvfp4_index_keys(dev, group, shared):
     """Prefix sharing with NVFP4 index keys: the shared pages are dequantised
