@@ -188,6 +188,16 @@ msa_status check_scale_alignment(const msa_shape* s, const msa_cache* c, bool ne
   return MSA_OK;
 }
 
+msa_status check_block_major(const msa_shape* s) {
+  if (s->kv_dtype != MSA_KV_NVFP4) return fail(MSA_ERR_UNSUPPORTED, "block-major attention needs NVFP4 K/V");
+  if (s->q_len > msa::kBmMaxQ)
+    return fail(MSA_ERR_UNSUPPORTED, "block-major attention with q_len = %d (at most %d)", s->q_len, msa::kBmMaxQ);
+  if (s->max_blocks_per_seq > msa::kBmMaxBlocks)
+    return fail(MSA_ERR_UNSUPPORTED, "block-major attention with max_blocks_per_seq = %d (at most %d)",
+                s->max_blocks_per_seq, msa::kBmMaxBlocks);
+  return MSA_OK;
+}
+
 // ---- static scratch of the allocation-free entry point --------------------
 // The workspace of msa_decode_noalloc: a file-scope device array, one copy per
 // GPU the library runs on, held until the process ends.  Host code never uses
@@ -352,6 +362,46 @@ msa_status msa_decode_noalloc(const msa_shape* shape, const msa_cache* cache, co
   void* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != MSA_OK) return st;
   return decode_impl(shape, cache, nullptr, q, idx_q, out, sel_blocks, ws, kScratchBytes, stream);
+}
+
+size_t msa_block_major_workspace_size(const msa_shape* shape) {
+  if (check_shape(shape) != MSA_OK || check_block_major(shape) != MSA_OK) return 0;
+  return align256(scores_bytes(shape)) + align256(sel_bytes(shape)) +
+         msa::block_major_scratch_bytes(shape->num_seqs, shape->q_len);
+}
+
+msa_status msa_decode_block_major(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q,
+                                  float* out, int32_t* sel_blocks, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if ((st = check_block_major(shape)) != MSA_OK) return st;
+  if ((st = check_cache(shape, cache, true, true)) != MSA_OK) return st;
+  if (!q || !idx_q || !out) return fail(MSA_ERR_INVALID_ARGUMENT, "q / idx_q / out is NULL");
+  const void* aligned16[] = {q, idx_q, cache->idx_k, cache->k, cache->v, out};
+  const char* names[] = {"q", "idx_q", "idx_k", "k", "v", "out"};
+  for (int i = 0; i < 6; ++i)
+    if ((st = check_aligned(aligned16[i], 16, names[i])) != MSA_OK) return st;
+  if ((st = check_scale_alignment(shape, cache, true, true)) != MSA_OK) return st;
+  if (shape->num_seqs == 0) return ok();
+  const size_t need = msa_block_major_workspace_size(shape);
+  if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if ((st = check_aligned(workspace, 256, "workspace")) != MSA_OK) return st;
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  // index scan + block max-pool, the stand-alone selection, then the
+  // block-major attention (inversion, partials, merge)
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  int32_t* sel = sel_blocks ? sel_blocks : reinterpret_cast<int32_t*>(ws + align256(scores_bytes(shape)));
+  void* scratch = ws + align256(scores_bytes(shape)) + align256(sel_bytes(shape));
+  hipError_t e = launch_scan(shape, scan_args(shape, cache, idx_q, scores), stream);
+  if (e != hipSuccess) return hip_status(e, "index scan");
+  msa::TopkArgs ta{cache->seq_lens, scores, sel, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};
+  if ((e = msa::launch_block_topk(ta, stream)) != hipSuccess) return hip_status(e, "block top-k");
+  return hip_status(msa::launch_block_major_attn(attn_args(shape, cache, q, nullptr, sel, nullptr, out),
+                                                 shape->num_seqs, scratch, stream),
+                    "block-major attention");
 }
 
 msa_status msa_decode_shared(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,

@@ -76,6 +76,14 @@ struct AttnArgs {
 // Selection (fused path) + attention: one launch.
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
+// KV-block-major attention over given ids (a.sel), NVFP4 K/V: inversion of
+// the selections into per-block row lists, block-major partials, merge (three
+// launches).  scratch: block_major_scratch_bytes(num_seqs, q_len) bytes.
+constexpr int kBmMaxQ = 256;         // query rows per sequence (16 x 256 selections per (sequence, group))
+constexpr int kBmMaxBlocks = 8192;   // block-table row length (1M tokens)
+size_t block_major_scratch_bytes(int num_seqs, int q_len);
+hipError_t launch_block_major_attn(const AttnArgs& a, int num_seqs, void* scratch, hipStream_t stream);
+
 // Write side: new tokens quantised into the paged pools (one launch).
 struct InsertArgs {
   uint8_t* k;                  // NVFP4 [P][4][128][64] or bf16 [P][4][128][128]

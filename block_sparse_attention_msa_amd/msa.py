@@ -24,7 +24,8 @@ MSA_SHARE_MAX = 64  # most (member x query token) per prefix-sharing group
 _IDX = {"bf16": MSA_IDX_BF16, "fp8": MSA_IDX_FP8_E4M3, "nvfp4": MSA_IDX_NVFP4}
 EXPORTED = ("msa_workspace_size", "msa_attn_workspace_size", "msa_indexer_score", "msa_block_topk",
             "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert", "msa_indexer_score_shared", "msa_decode_shared",
-            "msa_status_string", "msa_last_error", "msa_decode_noalloc")
+            "msa_status_string", "msa_last_error", "msa_decode_noalloc", "msa_block_major_workspace_size",
+            "msa_decode_block_major")
 MSA_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of msa_decode_noalloc
 
 
@@ -134,11 +135,14 @@ def lib():
         L.msa_decode.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_kv_insert.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp]
         L.msa_decode_noalloc.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp]
+        L.msa_block_major_workspace_size.argtypes = [P(MsaShape)]
+        L.msa_block_major_workspace_size.restype = ctypes.c_size_t
+        L.msa_decode_block_major.argtypes = [P(MsaShape), P(MsaCache), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.msa_indexer_score_shared.argtypes = [P(MsaShape), P(MsaCache), P(MsaPrefixShare), vp, vp, vp]
         L.msa_decode_shared.argtypes = [P(MsaShape), P(MsaCache), P(MsaPrefixShare), vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
         for f in ("msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode", "msa_decode", "msa_kv_insert",
-                  "msa_indexer_score_shared", "msa_decode_shared", "msa_decode_noalloc"):
+                  "msa_indexer_score_shared", "msa_decode_shared", "msa_decode_noalloc", "msa_decode_block_major"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -198,6 +202,17 @@ def msa_decode(shape, cache, q, idx_q, out, sel_blocks, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().msa_decode(ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(idx_q), _ptr(out),
                             _ptr(sel_blocks), _ptr(workspace), nbytes, _stream(stream)), "msa_decode")
+
+
+def msa_block_major_workspace_size(shape: MsaShape) -> int:
+    return int(lib().msa_block_major_workspace_size(ctypes.byref(shape)))
+
+
+def msa_decode_block_major(shape, cache, q, idx_q, out, sel_blocks, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().msa_decode_block_major(ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(idx_q), _ptr(out),
+                                        _ptr(sel_blocks), _ptr(workspace), nbytes, _stream(stream)),
+           "msa_decode_block_major")
 
 
 def msa_decode_noalloc(shape, cache, q, idx_q, out, sel_blocks, stream=None):

@@ -180,7 +180,7 @@ class Workload:
 def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: str = "nvfp4",
                   idx_dtype: str = "fp8", max_blocks_per_seq: Optional[int] = None, layout: str = "identity",
                   spare_pages: int = 0, plant: int = 0, zipf: Optional[float] = None, zipf_amp: float = 4.0,
-                  idx_dist: str = "normal", shared_bias_iq: bool = False, seed: int = 0,
+                  idx_dist: str = "normal", shared_bias_iq: bool = False, iq_noise: float = 1.0, seed: int = 0,
                   device="cpu", num_q_heads: int = 16, num_kv_heads: int = 4,
                   sm_scale: Optional[float] = None, idx_scale: float = 1.0,
                   kv_chunk_pages: int = 1024, share: Optional[tuple] = None) -> Workload:
@@ -195,8 +195,9 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     zipf s: for each (sequence, group) a random permutation ranks the
     non-recent blocks 1..nb-1 and block of rank k gets zipf_amp * k^-s times the
     unit direction added.  idx_dist: "normal" N(0,1) or "uniform" U(-1,1).
-    shared_bias_iq: (q_len > 1) index queries are u_{b,g} + N(0,1), with u the
-    bias direction shared by the chunk.
+    shared_bias_iq: (q_len > 1) index queries are u_{b,g} + iq_noise N(0,1),
+    with u the bias direction shared by the chunk (a small iq_noise: queries
+    of a chunk that select mostly the same blocks).
     share (group_size, shared_blocks): consecutive sequences form groups of
     group_size (at most 64 / q_len) whose first shared_blocks logical blocks map to the
     leader's (the group's first sequence's) pages: a shared prefix, keys and
@@ -253,7 +254,7 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
     q = torch.randn(rows, Hq, DIM, generator=gq, device=dev).to(torch.bfloat16)
     if shared_bias_iq:
         u = torch.randn(S, 1, G, DIM, generator=gq, device=dev)
-        iqf = u + torch.randn(S, q_len, G, DIM, generator=gq, device=dev)
+        iqf = u + float(iq_noise) * torch.randn(S, q_len, G, DIM, generator=gq, device=dev)
         iq = iqf.reshape(rows, G, DIM).to(torch.bfloat16)
         direction = (u[:, 0] / u[:, 0].norm(dim=-1, keepdim=True))            # [S][G][D]
     else:
@@ -402,6 +403,11 @@ CONFIGS = {
     # batch 2 x 256 new query tokens appended causally to a 128K paged context
     "verify_b2_q256_128k": dict(seq_lens=[131072 + 256] * 2, q_len=256, zipf=1.1, layout="paged",
                                 shared_bias_iq=True, seed=4),
+    # the 2 x 256-token chunk with strongly correlated index queries
+    # (u + 0.25 N(0,1)): neighbouring queries select mostly the same blocks,
+    # the case the KV-block-major attention is built for; not one of the five
+    "verify_b2_q256_128k_corr": dict(seq_lens=[131072 + 256] * 2, q_len=256, zipf=1.1, layout="paged",
+                                     shared_bias_iq=True, iq_noise=0.25, seed=4),
     # speculative verify on the decode path: batch 32, each sequence a 128K
     # context plus 4 new query tokens (1 + 3 draft tokens, the draft length of
     # the AMD serving recipe); not one of the five above

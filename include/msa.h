@@ -164,6 +164,30 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
 msa_status msa_decode(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q, float* out,
                       int32_t* sel_blocks, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The fused path with KV-block-major attention for multi-query rows ("KV-
+ * block-major prefill" of the MiniMax M3 x vLLM post: the per-query block
+ * lists are inverted into per-block query lists, each selected block is
+ * loaded and dequantised once for all the queries of its (sequence, group)
+ * that chose it, and every query's per-block partials are merged by
+ * log-sum-exp).  Steps: the index scan, the stand-alone selection, the
+ * inversion, the block-major partials (each block's K and V dequantised once
+ * per work item of up to 16 rows), the merge: five launches.  Results: ids as
+ * msa_decode's (the same selection); outputs equal the same exact attention
+ * to fp32 rounding (another summation order than msa_decode's).  It pays off
+ * when many rows of a chunk select the same blocks; with rows that select
+ * mostly different blocks msa_decode's per-row attention is faster.
+ * Supported: NVFP4 K/V, q_len <= 256, max_blocks_per_seq <= 8192
+ * (MSA_ERR_UNSUPPORTED otherwise).
+ *   out       as in msa_decode, 16-B aligned (the merge stores float4s).
+ *   workspace >= msa_block_major_workspace_size(shape) bytes, 256-B aligned
+ *             (block scores, ids, inverted lists, per-(row, slot) partials:
+ *             about 133 KB per query row); no initialisation needed.
+ * Other arguments as in msa_decode. */
+size_t msa_block_major_workspace_size(const msa_shape* shape);
+msa_status msa_decode_block_major(const msa_shape* shape, const msa_cache* cache, const void* q, const void* idx_q,
+                                  float* out, int32_t* sel_blocks, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* msa_decode without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same launches, with the workspace taken from a

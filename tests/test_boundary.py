@@ -219,6 +219,30 @@ def test_other_entry_points_validate():
         assert msa.status_string(st).startswith("MSA_")
 
 
+def test_block_major_validation():
+    """msa_decode_block_major: NVFP4 K/V, q_len <= 256 and tables of at most
+    8,192 blocks only; 16-B aligned out; a workspace of
+    msa_block_major_workspace_size() bytes (0 for an unsupported shape)."""
+    L = msa.lib()
+
+    def dec(shape, out=FAKE, ws=FAKE, nbytes=1 << 30):
+        return L.msa_decode_block_major(ctypes.byref(shape), ctypes.byref(_cache()), FAKE, FAKE, out, FAKE, ws,
+                                        nbytes, None)
+
+    for kw in (dict(kv_dtype=msa.MSA_KV_BF16), dict(q_len=257), dict(max_blocks_per_seq=8193)):
+        s = _shape(**kw)
+        assert dec(s) == msa.MSA_ERR_UNSUPPORTED, kw
+        assert L.msa_block_major_workspace_size(ctypes.byref(s)) == 0
+    s = _shape(q_len=256, max_blocks_per_seq=1024)
+    need = L.msa_block_major_workspace_size(ctypes.byref(s))
+    assert need > L.msa_workspace_size(ctypes.byref(s)) and need % 256 == 0
+    assert dec(s, out=FAKE + 8) == msa.MSA_ERR_INVALID_ARGUMENT and "out" in msa.last_error()
+    assert dec(s, ws=None) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert dec(s, ws=FAKE + 16) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert dec(s, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert dec(_shape(num_seqs=0), ws=None, nbytes=0) == msa.MSA_OK
+
+
 def test_read_ceiling_library_exports_and_validates():
     """The benchmark's read-ceiling kernel library (not part of the MSA path)
     loads, exports its entry point and rejects bad arguments before any HIP

@@ -309,6 +309,68 @@ def test_multi_query_nvfp4_extreme_index_queries(dev):
     check_workload(w, label="multi-query nvfp4 index keys, extreme index queries")
 
 
+def _block_major(msa, w, dev):
+    """msa_decode_block_major on w (ids also written), plus msa_decode's ids
+    and outputs for comparison; host arrays."""
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    out, sel = msa.alloc_outputs(w)
+    ws = torch.full((msa.msa_block_major_workspace_size(shape),), 0x7F, dtype=torch.uint8, device=dev)
+    msa.msa_decode_block_major(shape, cache, w.q, w.iq, out, sel, ws)
+    out1, sel1 = msa.alloc_outputs(w)
+    msa.msa_decode(shape, cache, w.q, w.iq, out1, sel1, msa.alloc_workspace(shape, dev))
+    out_ns = torch.empty_like(out)
+    msa.msa_decode_block_major(shape, cache, w.q, w.iq, out_ns, None, ws)  # ids kept in the workspace
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ns)
+    return out.cpu().numpy(), sel.cpu().numpy(), out1.cpu().numpy(), sel1.cpu().numpy()
+
+
+@pytest.mark.parametrize("kv_idx", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("q_len", [1, 2, 5, 16, 64, 200])
+def test_block_major_attention(dev, q_len, kv_idx):
+    """The KV-block-major attention (msa_decode_block_major: selections
+    inverted into per-block row lists, each block's K/V dequantised once per
+    work item of up to 16 rows, per-(row, slot) partials merged): ids equal
+    msa_decode's, outputs within the tolerance of msa_decode's and of the
+    oracle on every row.  Ragged lengths: a sequence made only of the new
+    tokens, one shorter than 16 blocks (every block kept), a padded row, long
+    rows whose blocks are chosen by many rows (shared-bias queries)."""
+    msa = _msa()
+    lens = [q_len, 127 + q_len, 0, 16 * 128 + q_len, 5000, 9000 + q_len]
+    w = synth.make_workload(seq_lens=lens, q_len=q_len, plant=3, zipf=1.1, layout="paged", idx_dtype=kv_idx,
+                            shared_bias_iq=q_len > 1, iq_noise=0.5, seed=150 + q_len, device=dev,
+                            max_blocks_per_seq=80)
+    _say(f"[parity] block-major q_len={q_len} {kv_idx} index keys, rows={w.rows}")
+    out, sel, out1, sel1 = _block_major(msa, w, dev)
+    assert np.array_equal(sel, sel1)
+    P = oracle.Problem.from_workload(w)
+    ties, worst = check_rows(P, out, sel)
+    np.testing.assert_allclose(out, out1, rtol=1e-2, atol=2e-3)
+    pad = 2 * q_len
+    assert (out[pad:pad + q_len] == 0).all() and (sel[pad:pad + q_len] == -1).all()
+    _say(f"[parity] block-major q_len={q_len}: near_ties={ties} max_abs_err={worst:.3g}")
+
+
+@pytest.mark.parametrize("name", ["verify_b2_q256_128k", "verify_b2_q256_128k_corr"])
+def test_block_major_verify_chunk_configs(dev, name):
+    """The 2 x 256-token chunk on 128K (and its variant with strongly
+    correlated index queries) through the block-major attention, all 512 rows
+    against the oracle; ids equal msa_decode's."""
+    msa = _msa()
+    w = synth.make_config(name, device=dev)
+    out, sel, out1, sel1 = _block_major(msa, w, dev)
+    assert np.array_equal(sel, sel1)
+    P = oracle.Problem.from_workload(w)
+    ties, worst = check_rows(P, out, sel)
+    _say(f"[parity] block-major {name}: rows={w.rows} near_ties={ties} max_abs_err={worst:.3g}")
+
+
+def test_verify_b2_q256_128k_corr_config(dev):
+    """The correlated chunk through msa_decode (per-row attention), every row."""
+    w = synth.make_config("verify_b2_q256_128k_corr", device=dev)
+    check_workload(w)
+
+
 def test_spec_b32_q4_128k_config(dev):
     """Speculative verify on the decode path: batch 32 x (128K + 4) with 4 query
     tokens each, in the bench's launch configuration, all 128 rows."""
