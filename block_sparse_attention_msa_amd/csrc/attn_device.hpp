@@ -54,11 +54,14 @@ constexpr int kPvSteps = kBlock / 32;   // 32-token MFMA contraction steps per b
 // (8 waves, two kept blocks each, online softmax across the pair; rows of at
 // most 8,192 blocks).  The 512-thread form needs about half the LDS, so two
 // workgroups share a CU and hide each other's load and selection latency.
-template <int NT>
+// With the kept blocks split over SPLIT workgroups, each takes 16 / SPLIT
+// slots, one per wave (NT = 1024 / SPLIT).
+template <int NT, int SPLIT = 1>
 struct AttnShape {
   static constexpr int kWaves = NT / kWave;
-  static constexpr int kBlocksPerWave = kTopK / kWaves;
-  static_assert(kWaves * kBlocksPerWave == kTopK, "kept blocks split evenly over the waves");
+  static constexpr int kSlots = kTopK / SPLIT;  // kept-block slots of one workgroup
+  static constexpr int kBlocksPerWave = kSlots / kWaves;
+  static_assert(kWaves * kBlocksPerWave * SPLIT == kTopK, "kept blocks split evenly over the waves");
 };
 
 template <int NT>
@@ -137,18 +140,30 @@ struct PvType<false> {  // bf16 V
 // output dims [part * 128 / DSPLIT, (part + 1) * 128 / DSPLIT).  The DSPLIT
 // workgroups of one (row, g) repeat the selection and the softmax (identical,
 // deterministic) and split the PV work; part 0 writes the selected ids.
+// With SPLIT > 1 (DSPLIT = 1) the workgroups instead split the kept blocks:
+// part p takes slots [16 p / SPLIT, 16 (p + 1) / SPLIT) and writes, instead of
+// the output, its partial per head: po[pair][p][h][128] = sum over its keys of
+// 2^(z - M) v (K/V tensor scales aside) and pml[pair][p][h] = (M, sum 2^(z - M)),
+// M its largest logit (-inf, with zeros, for a part without keys); a merge
+// launch combines the parts.  Padded rows write nothing but -1 ids.
 // With SELECT, mbps must not exceed sel_max_blocks<NT>().  Every thread of the
 // workgroup must call it.
-template <bool FP4, bool SELECT, int DSPLIT, int NT>
+template <bool FP4, bool SELECT, int DSPLIT, int NT, int SPLIT = 1>
 __device__ __forceinline__ void attn_workgroup(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
     int32_t* __restrict__ sel_out, float* __restrict__ out, int q_len, int mbps, float qk_scale_log2, float v_scale,
-    int row, int g, int part, AttnSmem<NT>& sm) {
+    int row, int g, int part, AttnSmem<NT>& sm, float* __restrict__ po = nullptr, float2* __restrict__ pml = nullptr) {
   static_assert(DSPLIT == 1 || DSPLIT == 2 || DSPLIT == 4, "output split");
-  constexpr int kWaves = AttnShape<NT>::kWaves;
-  constexpr int kBpw = AttnShape<NT>::kBlocksPerWave;
+  static_assert(SPLIT == 1 || DSPLIT == 1, "split either the output dims or the kept blocks");
+  constexpr int kWaves = AttnShape<NT, SPLIT>::kWaves;
+  constexpr int kBpw = AttnShape<NT, SPLIT>::kBlocksPerWave;
+  constexpr int kSlot0Step = AttnShape<NT, SPLIT>::kSlots;  // first slot of part p: p * kSlots
+  // With the kept blocks split (one block per wave, at most 2 waves per SIMD)
+  // the V loads go out with the K loads: registers are plentiful and the
+  // wave's chain of round trips is what takes the time.
+  constexpr bool kVEarly = SPLIT > 1;
   using PV = PvType<FP4>;
   constexpr int kRowBytes = FP4 ? kDim / 2 : kDim * 2;  // bytes per (token, head) row
   constexpr int kDims = kDim / DSPLIT;                  // output dims of this workgroup
@@ -160,12 +175,13 @@ __device__ __forceinline__ void attn_workgroup(
   const int b = row / q_len;
   const int L = seq_lens[b];
   const int head0 = g * kHeadsPerGroup;
-  const int dbase = part * kDims;
+  const int dbase = SPLIT > 1 ? 0 : part * kDims;
   float* out_row = out + ((size_t)row * (kGroups * kHeadsPerGroup) + head0) * kDim;
   int32_t* sel_row = (sel_out && part == 0) ? sel_out + ((size_t)row * kGroups + g) * kTopK : nullptr;
 
   if (L <= 0) {  // padded row
-    if (tid < kHeadsPerGroup * kDims) out_row[(tid / kDims) * kDim + dbase + tid % kDims] = 0.f;
+    if (SPLIT == 1)
+      for (int i = tid; i < kHeadsPerGroup * kDims; i += NT) out_row[(i / kDims) * kDim + dbase + i % kDims] = 0.f;
     if (SELECT && sel_row && tid < kTopK) sel_row[tid] = -1;
     return;
   }
@@ -205,7 +221,7 @@ __device__ __forceinline__ void attn_workgroup(
   }
 
   for (int kb = 0; kb < kBpw; ++kb) {
-    const int slot = wave + kWaves * kb;
+    const int slot = (SPLIT > 1 ? part * kSlot0Step : 0) + wave + kWaves * kb;
     const int j = sm.sel[slot];
     // ids outside the row's visible blocks or the table contribute nothing
     if (j < 0 || j >= mbps || j * kBlock > pos) continue;  // wave-uniform
@@ -214,6 +230,39 @@ __device__ __forceinline__ void attn_workgroup(
     const int nvis = min(pos - j * kBlock + 1, kBlock);   // keys: tokens 0..nvis-1 (>= 1)
     const uint8_t* kbase = kpool + row0 * kRowBytes;
     const uint8_t* vbase = vpool + row0 * kRowBytes;
+
+    [[maybe_unused]] uint32_t vw[kPvSteps][8];
+    [[maybe_unused]] uint4 vb[FP4 ? 1 : 8];
+    [[maybe_unused]] uint4 vbe[(!FP4 && kVEarly) ? kPvSteps : 1][8];  // bf16 V, loaded early
+    auto load_v = [&]() {
+      if constexpr (!FP4 && kVEarly) {
+#pragma unroll
+        for (int s = 0; s < kPvSteps; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vbe[s][e] = *reinterpret_cast<const uint4*>(vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + 2 * d0);
+      } else if constexpr (!FP4 && kLaneDims == 2) {  // bf16 V, 2 dims per lane: all 4 steps' words fit 32 VGPRs
+#pragma unroll
+        for (int s = 0; s < kPvSteps; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vw[s][e] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + 2 * d0);
+      }
+      if constexpr (FP4) {
+#pragma unroll
+        for (int s = 0; s < kPvSteps; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint8_t* src = vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + d0 / 2;
+            if constexpr (kLaneDims == 8)
+              vw[s][e] = *reinterpret_cast<const uint32_t*>(src);
+            else if constexpr (kLaneDims == 4)
+              vw[s][e] = *reinterpret_cast<const uint16_t*>(src);
+            else
+              vw[s][e] = *src;
+          }
+      }
+    };
 
     // ---- issue the K loads (NVFP4: the whole block, 16 B per lane and tile)
     [[maybe_unused]] uint4 kv[kQkTiles];
@@ -227,6 +276,7 @@ __device__ __forceinline__ void attn_workgroup(
       ks16 = *reinterpret_cast<const uint4*>(k_sf + row0 * 8 + lane * 16);
       vs16 = *reinterpret_cast<const uint4*>(v_sf + row0 * 8 + lane * 16);
     }
+    if constexpr (kVEarly) load_v();
     if constexpr (FP4) {
       *reinterpret_cast<uint4*>(&sm.ksc[wave][lane * 16]) = ks16;
       *reinterpret_cast<uint4*>(&sm.vsc[wave][lane * 16]) = pair_scales(vs16, 2 * lane < nvis, 2 * lane + 1 < nvis);
@@ -287,31 +337,9 @@ __device__ __forceinline__ void attn_workgroup(
       z[T] = 16 * T + 4 * c + jj < nvis ? dot * qk_scale_log2 : -INFINITY;
     }
 
-    // ---- issue the V loads: lane (c, n) takes dims d0 .. d0 + kLaneDims - 1
-    //      of tokens 32s + 8c + e
-    [[maybe_unused]] uint32_t vw[kPvSteps][8];
-    [[maybe_unused]] uint4 vb[FP4 ? 1 : 8];
-    if constexpr (!FP4 && kLaneDims == 2) {  // bf16 V, 2 dims per lane: all 4 steps' words fit 32 VGPRs
-#pragma unroll
-      for (int s = 0; s < kPvSteps; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vw[s][e] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + 2 * d0);
-    }
-    if constexpr (FP4) {
-#pragma unroll
-      for (int s = 0; s < kPvSteps; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint8_t* src = vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + d0 / 2;
-          if constexpr (kLaneDims == 8)
-            vw[s][e] = *reinterpret_cast<const uint32_t*>(src);
-          else if constexpr (kLaneDims == 4)
-            vw[s][e] = *reinterpret_cast<const uint16_t*>(src);
-          else
-            vw[s][e] = *src;
-        }
-    }
+    // ---- issue the V loads (here, or with the K loads): lane (c, n) takes
+    //      dims d0 .. d0 + kLaneDims - 1 of tokens 32s + 8c + e
+    if constexpr (!kVEarly) load_v();
 
     // ---- softmax over the block; with two blocks per wave, online across them
     float mx = z[0];
@@ -397,8 +425,10 @@ __device__ __forceinline__ void attn_workgroup(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tok = 32 * s + 8 * c + e;
-          const uint8_t* src = vbase + (size_t)tok * kRowBytes + 2 * d0;
-          if constexpr (kLaneDims == 8) {
+          [[maybe_unused]] const uint8_t* src = vbase + (size_t)tok * kRowBytes + 2 * d0;
+          if constexpr (kVEarly) {
+            vb[e] = vbe[s][e];
+          } else if constexpr (kLaneDims == 8) {
             vb[e] = *reinterpret_cast<const uint4*>(src);
           } else if constexpr (kLaneDims == 4) {
             const uint2 t2 = *reinterpret_cast<const uint2*>(src);
@@ -428,6 +458,22 @@ __device__ __forceinline__ void attn_workgroup(
       }
     }
     wave_sync_lds();  // the next block rewrites this wave's LDS
+  }
+  if constexpr (SPLIT > 1 && kWaves == 1) {
+    // a one-wave part: its registers are the partial (lanes 0..15 hold heads
+    // 0..3 x dims d0 .. d0 + 7; lane 4 h holds head h's (m, l))
+    float* dst = po + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup * kDim;
+    if (c == 0) {
+#pragma unroll
+      for (int i = 0; i < kHeadsPerGroup; ++i) {
+        float4* d4 = reinterpret_cast<float4*>(dst + i * kDim + d0);
+        d4[0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+        d4[1] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+      }
+    }
+    if (c == 0 && jj == 0)
+      pml[((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + hq] = make_float2(m_w, l_w);
+    return;
   }
   __syncthreads();  // selection LDS is dead: the merge area reuses it
 
@@ -462,16 +508,18 @@ __device__ __forceinline__ void attn_workgroup(
     fl += __shfl_xor(fl, 16);
     fl += __shfl_xor(fl, 32);
     if (w < kWaves) sm.u.merge.f[w][h] = f;
-    if (w == 0) sm.u.merge.inv[h] = fl > 0.f ? v_scale / fl : 0.f;
+    if (w == 0) sm.u.merge.inv[h] = SPLIT > 1 ? 1.f : (fl > 0.f ? v_scale / fl : 0.f);
+    if (SPLIT > 1 && w == 0) pml[((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + h] = make_float2(M, fl);
   }
   __syncthreads();
-  if (tid < kHeadsPerGroup * kDims) {
-    const int h = tid / kDims;
-    const int d = dbase + tid % kDims;
+  float* dst = SPLIT > 1 ? po + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup * kDim : out_row;
+  for (int i = tid; i < kHeadsPerGroup * kDims; i += NT) {
+    const int h = i / kDims;
+    const int d = dbase + i % kDims;
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) o = fmaf(sm.u.merge.f[w][h], sm.u.merge.o[w][h][d], o);
-    out_row[h * kDim + d] = o * sm.u.merge.inv[h];
+    dst[h * kDim + d] = o * sm.u.merge.inv[h];
   }
 }
 

@@ -234,13 +234,16 @@ msa_status scratch_for_current_device(void** out) {
 extern "C" {
 
 size_t msa_attn_workspace_size(const msa_shape* shape) {
-  (void)check_shape(shape);
-  return 0;  // the attention kernel merges its split work on chip
+  if (check_shape(shape) != MSA_OK) return 0;
+  // the kept-block split's partials (few (row, group) pairs); otherwise the
+  // attention merges its split work on chip
+  return align256(msa::split_partials_bytes(rows_of(shape) * (long long)MSA_NUM_KV_HEADS));
 }
 
 size_t msa_workspace_size(const msa_shape* shape) {
   if (check_shape(shape) != MSA_OK) return 0;
-  return align256(scores_bytes(shape)) + align256(sel_bytes(shape));
+  return align256(scores_bytes(shape)) + align256(sel_bytes(shape)) +
+         align256(msa::split_partials_bytes(rows_of(shape) * (long long)MSA_NUM_KV_HEADS));
 }
 
 static msa_status indexer_impl(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
@@ -282,8 +285,6 @@ msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const
 msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache, const void* q,
                                   const int32_t* sel_blocks, float* out, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;  // no workspace is needed (msa_attn_workspace_size() == 0)
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;
   if ((st = check_cache(shape, cache, false, true)) != MSA_OK) return st;
@@ -291,10 +292,19 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
   if ((st = check_aligned(q, 16, "q")) != MSA_OK) return st;
   if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
+  if ((st = check_aligned(out, 16, "out")) != MSA_OK) return st;
   if ((st = check_scale_alignment(shape, cache, false, true)) != MSA_OK) return st;
   if (shape->num_seqs == 0) return ok();
-  return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, nullptr, sel_blocks, nullptr, out), stream),
-                    "sparse attention");
+  const size_t need = msa_attn_workspace_size(shape);
+  msa::AttnArgs a = attn_args(shape, cache, q, nullptr, sel_blocks, nullptr, out);
+  if (need > 0) {  // few pairs: the kept-block split, as in msa_decode
+    if (!workspace) return fail(MSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((st = check_aligned(workspace, 256, "workspace")) != MSA_OK) return st;
+    if (workspace_bytes < need)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+    a.partials = static_cast<float*>(workspace);
+  }
+  return hip_status(msa::launch_sparse_attn(a, stream), "sparse attention");
 }
 
 static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
@@ -310,6 +320,7 @@ static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, co
   if ((st = check_aligned(cache->idx_k, 16, "idx_k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->k, 16, "k")) != MSA_OK) return st;
   if ((st = check_aligned(cache->v, 16, "v")) != MSA_OK) return st;
+  if ((st = check_aligned(out, 16, "out")) != MSA_OK) return st;
   if ((st = check_scale_alignment(shape, cache, true, true)) != MSA_OK) return st;
   const size_t need = msa_workspace_size(shape);
   if (shape->num_seqs > 0) {
@@ -330,9 +341,13 @@ static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, co
   hipError_t e = launch_scan_any(shape, scan_args(shape, cache, idx_q, scores), share, stream);
   if (e != hipSuccess) return hip_status(e, "index scan");
   const long long pairs = (long long)rows_of(shape) * shape->num_kv_heads;
-  if (pairs <= 2LL * msa::device_cus())
-    return hip_status(msa::launch_sparse_attn(attn_args(shape, cache, q, scores, nullptr, sel_blocks, out), stream),
-                      "selection + sparse attention");
+  if (pairs <= 2LL * msa::device_cus()) {
+    msa::AttnArgs a = attn_args(shape, cache, q, scores, nullptr, sel_blocks, out);
+    if (msa::split_partials_bytes(pairs) > 0)  // few pairs: room for the kept-block split
+      a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)) +
+                                            align256(sel_bytes(shape)));
+    return hip_status(msa::launch_sparse_attn(a, stream), "selection + sparse attention");
+  }
   int32_t* sel = sel_blocks ? sel_blocks
                             : reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)));
   msa::TopkArgs ta{cache->seq_lens, scores, sel, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};

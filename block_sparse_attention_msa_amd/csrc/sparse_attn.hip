@@ -37,6 +37,112 @@ __global__ __launch_bounds__(NT, 4) void attn_kernel(
                                       pair % kGroups, part, sm);
 }
 
+// Kept blocks split over SPLIT workgroups of NT = 1024 / SPLIT threads, one
+// block per wave; each workgroup writes its partial (o, M, sum) per head.
+template <bool FP4, bool SELECT, int SPLIT>
+__global__ __launch_bounds__(1024 / SPLIT) void attn_split_kernel(
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
+    const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
+    int32_t* __restrict__ sel_out, float* __restrict__ po, float2* __restrict__ pml, int rows, int q_len, int mbps,
+    float qk_scale_log2) {
+  constexpr int NT = 1024 / SPLIT;
+  __shared__ AttnSmem<NT> sm;
+  int pair, part;
+  attn_decode_wg<SPLIT>(blockIdx.x, pair, part);
+  if (pair >= rows * kGroups) return;
+  attn_workgroup<FP4, SELECT, 1, NT, SPLIT>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores, sel_in,
+                                           sel_out, nullptr, q_len, mbps, qk_scale_log2, 1.f, pair / kGroups,
+                                           pair % kGroups, part, sm, po, pml);
+}
+
+// Log-sum-exp merge of the SPLIT partials of each (row, group): one wave per
+// pair.  For the factors lane l takes (part l / 4, head l % 4); for the sums
+// head l / 16, dims 8 (l % 16) .. + 7.  Every load is issued up front, none
+// waiting on another: each part of a non-padded row writes its partial (zeros
+// and (-inf, 0) without keys); a padded row's partials are never written,
+// are read anyway (inside the buffer) and discarded: its output is 0.
+template <int SPLIT>
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(const int32_t* __restrict__ seq_lens, int pairs,
+                                                               int q_len, const float* __restrict__ po,
+                                                               const float2* __restrict__ pml, float v_scale,
+                                                               float* __restrict__ out) {
+  static_assert(SPLIT * kHeadsPerGroup <= kWave, "one factor per lane");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int id = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (id >= pairs) return;
+  const int row = id / kGroups;
+  const int h = lane >> 4, d0 = 8 * (lane & 15);
+  const int L = seq_lens[row / q_len];
+  const float2 ml = lane < SPLIT * kHeadsPerGroup ? pml[(size_t)id * SPLIT * kHeadsPerGroup + lane]
+                                                  : make_float2(-INFINITY, 0.f);
+  const float4* src = reinterpret_cast<const float4*>(po + ((size_t)id * SPLIT * kHeadsPerGroup + h) * kDim + d0);
+  float4 v[SPLIT][2];
+#pragma unroll
+  for (int p = 0; p < SPLIT; ++p) {
+    v[p][0] = src[p * kHeadsPerGroup * kDim / 4];
+    v[p][1] = src[p * kHeadsPerGroup * kDim / 4 + 1];
+  }
+  float M = ml.x;
+#pragma unroll
+  for (int off = kHeadsPerGroup; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float f = ml.x == -INFINITY ? 0.f : exp2_nonpos(ml.x - M);
+  float fl = f * ml.y;
+#pragma unroll
+  for (int off = kHeadsPerGroup; off < kWave; off <<= 1) fl += __shfl_xor(fl, off);
+  float acc[8] = {};
+#pragma unroll
+  for (int p = 0; p < SPLIT; ++p) {
+    const float w = __shfl(f, kHeadsPerGroup * p + h);  // 0 for a part without keys (its partial is 0)
+    acc[0] = fmaf(w, v[p][0].x, acc[0]);
+    acc[1] = fmaf(w, v[p][0].y, acc[1]);
+    acc[2] = fmaf(w, v[p][0].z, acc[2]);
+    acc[3] = fmaf(w, v[p][0].w, acc[3]);
+    acc[4] = fmaf(w, v[p][1].x, acc[4]);
+    acc[5] = fmaf(w, v[p][1].y, acc[5]);
+    acc[6] = fmaf(w, v[p][1].z, acc[6]);
+    acc[7] = fmaf(w, v[p][1].w, acc[7]);
+  }
+  const float flh = __shfl(fl, h);  // lanes 0 .. 3 hold heads 0 .. 3
+  const float sc = L > 0 && flh > 0.f ? v_scale / flh : 0.f;
+  float4* dst = reinterpret_cast<float4*>(out + ((size_t)id * kHeadsPerGroup + h) * kDim + d0);
+  dst[0] = L > 0 ? make_float4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc) : make_float4(0.f, 0.f, 0.f, 0.f);
+  dst[1] = L > 0 ? make_float4(acc[4] * sc, acc[5] * sc, acc[6] * sc, acc[7] * sc) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <bool FP4, bool SELECT, int SPLIT>
+void launch_split(const AttnArgs& a, hipStream_t stream) {
+  const long long pairs = (long long)a.rows * kGroups;
+  float* po = a.partials;
+  float2* pml = reinterpret_cast<float2*>(a.partials + (size_t)pairs * kTopK * kHeadsPerGroup * kDim);
+  const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * SPLIT));
+  attn_split_kernel<FP4, SELECT, SPLIT><<<grid, 1024 / SPLIT, 0, stream>>>(
+      static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table, a.seq_lens,
+      a.q, a.block_scores, a.sel, a.sel_out, po, pml, a.rows, a.q_len, a.mbps, a.qk_scale_log2);
+  attn_split_merge_kernel<SPLIT><<<dim3((unsigned)((pairs + 3) / 4)), 256, 0, stream>>>(
+      a.seq_lens, (int)pairs, a.q_len, po, pml, a.v_scale, a.out);
+}
+
+// Kept blocks split over workgroups (few (row, group) pairs, a partials
+// buffer): SPLIT = 16 / w, w the waves the selection needs for the row
+// length (1,024 blocks per wave, rounded up to a power of two); the same
+// split with the selection fused or the ids given, so that both give the
+// same sums.  Returns false where it does not apply.
+template <bool FP4, bool SELECT>
+bool try_launch_split(const AttnArgs& a, hipStream_t stream) {
+  const long long pairs = (long long)a.rows * kGroups;
+  if (!a.partials || pairs > kSplitMaxPairs) return false;
+  int w = 1;
+  while (w * sel_max_blocks<kWave>() < a.mbps) w *= 2;
+  switch (w) {
+    case 1: launch_split<FP4, SELECT, 16>(a, stream); return true;
+    case 2: launch_split<FP4, SELECT, 8>(a, stream); return true;
+    case 4: launch_split<FP4, SELECT, 4>(a, stream); return true;
+    case 8: launch_split<FP4, SELECT, 2>(a, stream); return true;
+    default: return false;
+  }
+}
+
 template <bool FP4, bool SELECT, int DSPLIT, int NT>
 void launch3(const AttnArgs& a, hipStream_t stream) {
   const long long pairs = (long long)a.rows * kGroups;
@@ -89,15 +195,17 @@ int device_cus() {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.kv_nvfp4) {
-    if (a.block_scores)
-      launch2<true, true>(a, stream);
-    else
+    if (a.block_scores) {
+      if (!try_launch_split<true, true>(a, stream)) launch2<true, true>(a, stream);
+    } else if (!try_launch_split<true, false>(a, stream)) {
       launch2<true, false>(a, stream);
+    }
   } else {
-    if (a.block_scores)
-      launch2<false, true>(a, stream);
-    else
+    if (a.block_scores) {
+      if (!try_launch_split<false, true>(a, stream)) launch2<false, true>(a, stream);
+    } else if (!try_launch_split<false, false>(a, stream)) {
       launch2<false, false>(a, stream);
+    }
   }
   return hipGetLastError();
 }

@@ -249,8 +249,8 @@ def alloc_outputs(w):
 
 
 def alloc_workspace(shape: MsaShape, device, attn_only: bool = False):
-    """Workspace for msa_decode (the fp32 block scores); None for the
-    stand-alone attention, which needs none."""
+    """Workspace for msa_decode (the fp32 block scores, ...) or, with
+    attn_only, for the stand-alone attention (None where it needs none)."""
     n = msa_attn_workspace_size(shape) if attn_only else msa_workspace_size(shape)
     if n == 0:
         if shape.num_seqs > 0 and not attn_only:

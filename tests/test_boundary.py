@@ -219,6 +219,30 @@ def test_other_entry_points_validate():
         assert msa.status_string(st).startswith("MSA_")
 
 
+def test_kept_block_split_workspace():
+    """At most 64 (row, group) pairs: msa_decode's workspace adds the split's
+    partials (2,080 B per (pair, kept block)) after the scores and ids, and the
+    stand-alone attention then needs the same partials as its workspace."""
+    L = msa.lib()
+    s = _shape(num_seqs=2, max_blocks_per_seq=8)  # 8 pairs
+    parts = 8 * 16 * 2080
+    assert L.msa_attn_workspace_size(ctypes.byref(s)) == parts
+    assert L.msa_workspace_size(ctypes.byref(s)) == 256 + 512 + parts
+    s16 = _shape(num_seqs=16, max_blocks_per_seq=8)  # 64 pairs: the largest split batch
+    assert L.msa_attn_workspace_size(ctypes.byref(s16)) == 64 * 16 * 2080
+    s17 = _shape(num_seqs=17, max_blocks_per_seq=8)
+    assert L.msa_attn_workspace_size(ctypes.byref(s17)) == 0
+
+    def attn(ws, nbytes, out=FAKE):
+        return L.msa_sparse_attn_decode(ctypes.byref(s), ctypes.byref(_cache()), FAKE, FAKE, out, ws, nbytes, None)
+
+    assert attn(None, 0) == msa.MSA_ERR_INVALID_ARGUMENT and "workspace" in msa.last_error()
+    assert attn(FAKE, parts - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert attn(FAKE + 64, parts) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert attn(FAKE, parts, out=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT and "out" in msa.last_error()
+    assert _decode(s, out=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT and "out" in msa.last_error()
+
+
 def test_block_major_validation():
     """msa_decode_block_major: NVFP4 K/V, q_len <= 256 and tables of at most
     8,192 blocks only; 16-B aligned out; a workspace of

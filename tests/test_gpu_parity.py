@@ -224,6 +224,23 @@ def test_max_context_fused(dev, idx):
     check_workload(w, label=f"max context 16,384 blocks, {idx} index keys")
 
 
+@pytest.mark.parametrize("kv", ["nvfp4", "bf16"])
+@pytest.mark.parametrize("mbps", [40, 1024, 1025, 3000, 4096, 6000, 9000])
+def test_kept_block_split(dev, kv, mbps):
+    """At most 64 (row, group) pairs the kept blocks are split over 16, 8, 4
+    or 2 workgroups (by the selection's waves for the row length: 1,024
+    blocks each), and a second launch merges the partials; a table row past
+    8,192 blocks keeps the on-chip merge.  Ragged rows, one of them padded and
+    one shorter than 16 blocks (parts without keys); fused and stand-alone
+    attention identical, every row against the oracle."""
+    top = mbps * 128
+    lens = [top - 77, 0, 5 * 128 + 3, min(top, 20000)]
+    w = synth.make_workload(seq_lens=lens, kv_dtype=kv, idx_dtype="fp8", plant=4, layout="paged", seed=50 + mbps,
+                            max_blocks_per_seq=mbps, zipf=1.1, device=dev)
+    out, sel, _ = check_workload(w, label=f"kept-block split, {kv} K/V, {mbps} blocks per table row")
+    assert (out[1] == 0).all() and (sel[1] == -1).all()
+
+
 def test_long_table_batch_1024_thread_form(dev):
     """40 rows (160 (row, group) pairs: more than one per two compute units, at
     most two per unit) with block-table rows of 9,000 entries, more than the 512-thread
