@@ -389,6 +389,48 @@ def config_summary(name: str, dev, steps: int, warmup: int, stream) -> dict:
     return rec
 
 
+BLOCK_MAJOR_CONFIGS = ("verify_b2_q256_128k", "verify_b2_q256_128k_corr")
+
+
+def block_major_summary(name: str, dev, steps: int, warmup: int, stream) -> dict:
+    """us per step of msa_decode (per-row attention) and msa_decode_block_major
+    on one multi-query chunk, timed in alternation (4 rounds each, median of
+    the rounds' K-step means), with the distinct blocks its rows select per
+    (sequence, group)."""
+    import torch
+    from block_sparse_attention_msa_amd import msa
+    w, copies, shape, caches = setup(name, dev)
+    ws = msa.alloc_workspace(shape, dev)
+    wsb = torch.empty(msa.msa_block_major_workspace_size(shape), dtype=torch.uint8, device=dev)
+    out, sel = msa.alloc_outputs(w)
+
+    def per_row(i):
+        c = copies[i % len(copies)]
+        msa.msa_decode(shape, caches[i % len(copies)], c.q, c.iq, out, sel, ws, stream)
+
+    def block_major(i):
+        c = copies[i % len(copies)]
+        msa.msa_decode_block_major(shape, caches[i % len(copies)], c.q, c.iq, out, sel, wsb, stream)
+
+    runs = {"per_row": [], "block_major": []}
+    for _ in range(4):
+        for key, f in (("per_row", per_row), ("block_major", block_major)):
+            runs[key].append(time_steps(f, steps, warmup, stream)[0])
+    s4 = sel.view(w.num_seqs, w.q_len, 4, 16).cpu()
+    distinct = [len(set(x for x in s4[b, :, g].flatten().tolist() if x >= 0))
+                for b in range(w.num_seqs) for g in range(4)]
+    rec = {"per_row_us": median(sorted(runs["per_row"])),
+           "block_major_us": median(sorted(runs["block_major"])),
+           "distinct_blocks_per_seq_group_mean": round(sum(distinct) / len(distinct), 1),
+           "selections_per_seq_group": w.q_len * 16}
+    log(f"[bench] {name}: per-row attention step {rec['per_row_us']} us, block-major step {rec['block_major_us']} us "
+        f"({rec['distinct_blocks_per_seq_group_mean']} distinct blocks of {rec['selections_per_seq_group']} "
+        f"selections per (sequence, group))")
+    del w, copies, caches, sel, wsb
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,11 +529,12 @@ def main():
     del copies, caches
     torch.cuda.empty_cache()
 
-    others = None
+    others = bmaj = None
     if not args.no_other_configs and args.config == "paged_b32_128k":
         # the other workloads, compactly (fewer steps: each is a short run)
         n, wu = max(5, min(args.steps, 30)), max(2, min(args.warmup, 10))
         others = {name: config_summary(name, dev, n, wu, stream) for name in OTHER_CONFIGS}
+        bmaj = {name: block_major_summary(name, dev, n, wu, stream) for name in BLOCK_MAJOR_CONFIGS}
 
     rec = {
         "metric": METRIC,
@@ -524,6 +567,7 @@ def main():
         "cpu_baseline": cpu,
         "kv_insert_us": round(insert_us, 2),
         "other_configs": others,
+        "block_major_vs_per_row": bmaj,
     }
     print(json.dumps(rec), flush=True)
 

@@ -693,15 +693,31 @@ def test_shared_b32_128k_config(dev):
     check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy())
 
 
-def test_graph_capture_replays(dev):
-    """msa_decode captured in a HIP graph: every replay (with eager work and
-    synchronisation in between) equals the eager result bit for bit."""
+@pytest.mark.parametrize("case", ["plain", "shared_fp8", "shared_nvfp4_wide"])
+def test_graph_capture_replays(dev, case):
+    """msa_decode (or msa_decode_shared, whose shared pass is forked onto the
+    library's second stream and joined back with events) captured in a HIP
+    graph: every replay (with eager work and synchronisation in between)
+    equals the eager result bit for bit."""
     msa = _msa()
-    w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", seed=43, device=dev)
+    if case == "plain":
+        w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", seed=43, device=dev)
+    else:
+        n = 8 if case == "shared_fp8" else 16
+        w = synth.make_workload(seq_lens=[9000 + 97 * i for i in range(n)], plant=3, layout="paged", seed=44,
+                                idx_dtype="fp8" if case == "shared_fp8" else "nvfp4", share=(n, 40), device=dev)
     shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    share = msa.MsaPrefixShare.from_workload(w) if case != "plain" else None
     out, sel = msa.alloc_outputs(w)
     ws = msa.alloc_workspace(shape, dev)
-    msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+
+    def call(stream=None):
+        if share is None:
+            msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws, stream=stream)
+        else:
+            msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out, sel, ws, stream=stream)
+
+    call()
     torch.cuda.synchronize()
     ref_out, ref_sel = out.clone(), sel.clone()
     s = torch.cuda.Stream()
@@ -709,7 +725,7 @@ def test_graph_capture_replays(dev):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws, stream=s)
+            call(stream=s)
     torch.cuda.synchronize()
     for rep in range(4):
         out.fill_(float("nan"))
@@ -719,7 +735,7 @@ def test_graph_capture_replays(dev):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), rep
         assert torch.equal(sel, ref_sel), rep
-        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)  # eager call between replays
+        call()  # eager call between replays
         torch.cuda.synchronize()
 
 
