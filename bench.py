@@ -253,9 +253,12 @@ def scan_call(msa, shape, cache, c, bs, stream):
         msa.msa_indexer_score(shape, cache, c.iq, bs, stream)
 
 
-def decode_call(msa, shape, cache, c, out, sel, ws, stream):
-    """One msa_decode step of workload copy c (msa_decode_shared when it has groups)."""
-    if c.share_members is not None:
+def decode_call(msa, shape, cache, c, out, sel, ws, stream, block_major: bool = False):
+    """One msa_decode step of workload copy c (msa_decode_shared when it has
+    groups, msa_decode_block_major when asked for)."""
+    if block_major:
+        msa.msa_decode_block_major(shape, cache, c.q, c.iq, out, sel, ws, stream)
+    elif c.share_members is not None:
         msa.msa_decode_shared(shape, cache, msa.MsaPrefixShare.from_workload(c), c.q, c.iq, out, sel, ws, stream)
     else:
         msa.msa_decode(shape, cache, c.q, c.iq, out, sel, ws, stream)
@@ -331,17 +334,21 @@ def setup(name: str, dev, ncopies: int = 0):
     return w, copies, msa.MsaShape.from_workload(w), [msa.MsaCache.from_workload(c) for c in copies]
 
 
-def measure_step_and_scan(w, copies, shape, caches, steps: int, warmup: int, stream):
-    """Times the fused step and the index scan alone (same rotation of input
-    copies); returns a dict of the figures and the step's selected ids."""
+def measure_step_and_scan(w, copies, shape, caches, steps: int, warmup: int, stream, block_major: bool = False):
+    """Times the fused step (with the block-major attention when asked for)
+    and the index scan alone (same rotation of input copies); returns a dict
+    of the figures and the step's selected ids."""
     import torch
     from block_sparse_attention_msa_amd import msa
     dev = w.q.device
-    ws = msa.alloc_workspace(shape, dev)
+    if block_major:
+        ws = torch.empty(msa.msa_block_major_workspace_size(shape), dtype=torch.uint8, device=dev)
+    else:
+        ws = msa.alloc_workspace(shape, dev)
     out, sel = msa.alloc_outputs(w)
 
     def step(i):
-        decode_call(msa, shape, caches[i % len(copies)], copies[i % len(copies)], out, sel, ws, stream)
+        decode_call(msa, shape, caches[i % len(copies)], copies[i % len(copies)], out, sel, ws, stream, block_major)
 
     us_step, per_step, wall = time_steps(step, steps, warmup, stream)
     bs = torch.empty(w.rows, 4, w.max_blocks_per_seq, dtype=torch.float32, device=dev)
@@ -442,6 +449,8 @@ def main():
                          "Infinity Cache of other inputs is read between two uses of one copy)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attention", choices=["per-row", "block-major"], default="per-row",
+                    help="block-major: the step runs msa_decode_block_major (NVFP4 K/V, q_len <= 256)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the compact records of the other workloads (tiny, batch-8 32K, batch-4 512K, "
                          "2 x 256-token chunk)")
@@ -471,7 +480,8 @@ def main():
         run_counter_pass(args, w, copies, shape, caches)
         return
     stream = torch.cuda.current_stream()
-    m, sel = measure_step_and_scan(w, copies, shape, caches, args.steps, args.warmup, stream)
+    m, sel = measure_step_and_scan(w, copies, shape, caches, args.steps, args.warmup, stream,
+                                   args.attention == "block-major")
     us_step, per_step, scan_us = m["us_step"], m["per_step"], m["scan_us"]
     ms_per_step = us_step / 1e3
 
@@ -551,7 +561,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "num_seqs": w.num_seqs, "context_tokens": int(w.seq_lens[0]),
                    "q_len": w.q_len, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": 128,
-                   "block": 128, "top_blocks": 16, "layout": w.meta.get("layout"), "input_copies": ncopies},
+                   "block": 128, "top_blocks": 16, "layout": w.meta.get("layout"), "input_copies": ncopies,
+                   "attention": args.attention},
         "achieved_GBps": round(step_gbps, 1),
         "pct_hbm_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_step": int(nb["total"]),
