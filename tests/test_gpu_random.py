@@ -6,7 +6,11 @@ and, without sharing, the unfused trio; rows against the fp64 oracle (every
 row, or 66 sampled rows of a case with more than 96).  The second generator
 reaches the larger shapes: chunks of 17-300 query tokens, decode batches of
 100-200 short rows (more (row, group) pairs than two per compute unit) and
-contexts up to 300K tokens."""
+contexts up to 300K tokens.  A third generator draws prefix-sharing batches
+(1-8 query tokens, groups of up to 64 / q_len requests, so both the narrow and
+the wide shared pass).  Every case that the KV-block-major attention takes
+(NVFP4 K/V, at most 256 query tokens, no sharing) also runs through it: the
+same ids as the fused step, its rows against the oracle."""
 import random
 import sys
 
@@ -103,6 +107,29 @@ def _wide_case(i):
 WIDE_CASES = [0, 7, 8, 9, 2, 4, 5, 10, 21, 22, 28, 18, 38, 61, 67, 88, 1, 3, 35, 12, 37, 23, 13]
 
 
+def _share_case(i):
+    """The i-th prefix-sharing case (deterministic): consecutive sequences in
+    groups of gsize share their first blocks."""
+    rng = random.Random(90000 + i)
+    q_len = rng.choice([1, 1, 2, 3, 4, 5, 8])
+    gsize = rng.randint(2, 64 // q_len)
+    S = gsize * rng.randint(1, 2) + rng.randint(0, 1)   # maybe one sequence in no group
+    S = min(S, 64)
+    lens = [rng.randint(max(q_len, 1500), 8000) for _ in range(S)]
+    kw = dict(seq_lens=lens, q_len=q_len, kv_dtype=rng.choice(["nvfp4", "nvfp4", "bf16"]),
+              idx_dtype=rng.choice(["fp8", "nvfp4"]), layout="paged", seed=91000 + i,
+              share=(gsize, rng.randint(0, (min(lens) - q_len + 1) // 128)))
+    kw["max_blocks_per_seq"] = max((L + 127) // 128 for L in lens) + rng.randint(0, 5)
+    if rng.random() < 0.5:
+        kw["zipf"] = 1.1
+    if q_len > 1 and rng.random() < 0.5:
+        kw["shared_bias_iq"] = True
+    return kw
+
+
+SHARE_CASES = range(16)
+
+
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available()
@@ -139,6 +166,16 @@ def _run_case(dev, kw, label):
         rows = sorted(set(random.Random(w.rows).sample(rows, 64) + [0, w.rows - 1]))
     for row in rows:
         check_row(P, row, o[row], s_[row], b_[row])
+    if w.share_members is None and w.kv_dtype == "nvfp4" and w.q_len <= 256 and w.max_blocks_per_seq <= 8192:
+        wsb = torch.empty(msa.msa_block_major_workspace_size(shape), dtype=torch.uint8, device=dev)
+        out_b, sel_b = msa.alloc_outputs(w)
+        msa.msa_decode_block_major(shape, cache, w.q, w.iq, out_b, sel_b, wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(sel_b, sel)
+        ob = out_b.cpu().numpy()
+        assert np.isfinite(ob).all()
+        for row in rows:
+            check_row(P, row, ob[row], s_[row], b_[row])
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
@@ -149,3 +186,8 @@ def test_random_case(dev, i):
 @pytest.mark.parametrize("i", WIDE_CASES)
 def test_random_wide_case(dev, i):
     _run_case(dev, _wide_case(i), f"wide case {i}")
+
+
+@pytest.mark.parametrize("i", SHARE_CASES)
+def test_random_share_case(dev, i):
+    _run_case(dev, _share_case(i), f"share case {i}")
