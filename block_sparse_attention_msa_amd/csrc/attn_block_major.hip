@@ -12,8 +12,9 @@
 //     (query row, slot) pairs of its q_len x 16 selections by block id in LDS
 //     and cuts each block's list into work items of at most 16 rows;
 //  2. block-major attention: a persistent grid walks the work items; per item
-//     the block's K is dequantised once (exactly) to bf16 and its V to f16,
-//     transposed, into LDS; each wave then takes 4 of the item's rows x the 4
+//     the block's K is dequantised once (exactly) to bf16 and its V to f16
+//     into LDS (V is stored by dim, so each 4-byte word of a dim row is 8
+//     tokens of it, already in the PV operand order); each wave then takes 4 of the item's rows x the 4
 //     heads of the group (16 MFMA columns): QK on bf16 MFMAs, the causal mask
 //     of each row inside the block, softmax statistics, PV on f16 MFMAs, and
 //     writes the row's partial (m, l, o) for that slot;
@@ -143,6 +144,8 @@ struct BmSmem {
   uint8_t vt[kDim * kBlock * 2];
   // softmax weights per wave, f16 [16 (row, head) columns][128 tokens]: chunk
   // k (tokens 8k .. 8k + 7) of column n at n * 256 + 16 (k ^ n)
+  // (while an item's K and V are staged, before any wave writes its weights,
+  // p[0]'s first 1 KB holds the block's V scales by group, [8][128 tokens])
   uint8_t p[kBmWaves][16 * kBlock * 2];
 };
 
@@ -171,6 +174,13 @@ __global__ __launch_bounds__(kBmThreads, 2) void bm_attn_kernel(
     const int64_t row0 = (page * kGroups + g) * kBlock;  // first (token, head) row of the slab
     const int tvis = min(L - kBlock * blk, kBlock);      // tokens of the block the last row sees
     __syncthreads();  // every wave is done with the previous item's LDS
+    uint8_t* vs = sm.p[0];  // V scales by group [8][128 tokens]; 0 past the last token any row sees
+    {  // V scales, transposed to [group][token]: thread = (token t, 4 groups)
+      const int t = tid >> 1, g4 = 4 * (tid & 1);
+      const uint32_t w = t < tvis ? *reinterpret_cast<const uint32_t*>(v_sf + (row0 + t) * 8 + g4) : 0u;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) vs[(g4 + q4) * kBlock + t] = (uint8_t)(w >> (8 * q4));
+    }
     {  // K: thread = (token t, half): 64 dims -> bf16, 8 chunks
       const int t = tid >> 1, h2 = tid & 1;
       const uint4 c0 = *reinterpret_cast<const uint4*>(kpool + (row0 + t) * 64 + 32 * h2);
@@ -187,32 +197,27 @@ __global__ __launch_bounds__(kBmThreads, 2) void bm_attn_kernel(
         *reinterpret_cast<bf16x8*>(sm.k + swz(t, 8 * h2 + m)) = v8;
       }
     }
-    {  // V: thread = (token pair p, quarter): tokens 2p, 2p + 1, dims 32 qd .. + 31
-      const int p = tid >> 2, qd = tid & 3;
-      const int64_t ra = row0 + 2 * p, rb = ra + 1;
-      const uint4 xa = *reinterpret_cast<const uint4*>(vpool + ra * 64 + 16 * qd);
-      const uint4 xb = *reinterpret_cast<const uint4*>(vpool + rb * 64 + 16 * qd);
-      // scales of groups 2 qd, 2 qd + 1 for both tokens; tokens no row sees: 0
-      const uint32_t sa = 2 * p < tvis ? *reinterpret_cast<const uint16_t*>(v_sf + ra * 8 + 2 * qd) : 0u;
-      const uint32_t sb = 2 * p + 1 < tvis ? *reinterpret_cast<const uint16_t*>(v_sf + rb * 8 + 2 * qd) : 0u;
-      // (a, b) pairs per group: byte 0 = group 2qd of a, byte 1 = of b, bytes 2, 3 the next group
-      const uint32_t spair = __builtin_amdgcn_perm(sb, sa, 0x05010400u);
-      const f16x2 sg0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spair, 1.0f, false);
-      const f16x2 sg1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spair, 1.0f, true);
-      const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w}, wb[4] = {xb.x, xb.y, xb.z, xb.w};
+    __syncthreads();  // the V scales
+    {  // V (stored by dim): thread = (8-token chunk k, 8 dims of group G): each
+       // dim row's 4 bytes of tokens 8k .. 8k + 7 -> one 16-B chunk of vt
+      const int k = tid & 15, G = tid >> 5, d0 = 16 * G + 8 * ((tid >> 4) & 1);
+      uint32_t w[8];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {  // dims 32 qd + 8 s .. + 7
-        const uint32_t lo = (wa[s] & 0x0F0F0F0Fu) | ((wb[s] << 4) & 0xF0F0F0F0u);  // even dims: (a, b)
-        const uint32_t hi = ((wa[s] >> 4) & 0x0F0F0F0Fu) | (wb[s] & 0xF0F0F0F0u);  // odd dims
-        const f16x2 scl = s < 2 ? sg0 : sg1;
+      for (int i = 0; i < 8; ++i)
+        w[i] = *reinterpret_cast<const uint32_t*>(vpool + (row0 + d0 + i) * 64 + 4 * k);
+      // group G's scales of the 8 tokens, as (2p, 2p + 1) pairs
+      const uint2 s8 = *reinterpret_cast<const uint2*>(vs + G * kBlock + 8 * k);
+      const f16x2 sc[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8.x, 1.0f, false),
+                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8.x, 1.0f, true),
+                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8.y, 1.0f, false),
+                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8.y, 1.0f, true)};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int d = 32 * qd + 8 * s + 2 * k;
-          const f16x2 ve = e2m1x2_to_f16x2(lo, k) * scl;
-          const f16x2 vo = e2m1x2_to_f16x2(hi, k) * scl;
-          *reinterpret_cast<f16x2*>(sm.vt + swz(d, p >> 2) + 4 * (p & 3)) = ve;
-          *reinterpret_cast<f16x2*>(sm.vt + swz(d + 1, p >> 2) + 4 * (p & 3)) = vo;
-        }
+      for (int i = 0; i < 8; ++i) {
+        f16x2 v[4];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) v[pp] = e2m1x2_to_f16x2(w[i], pp) * sc[pp];
+        const f16x8 v8 = {v[0].x, v[0].y, v[1].x, v[1].y, v[2].x, v[2].y, v[3].x, v[3].y};
+        *reinterpret_cast<f16x8*>(sm.vt + swz(d0 + i, k)) = v8;
       }
     }
     __syncthreads();

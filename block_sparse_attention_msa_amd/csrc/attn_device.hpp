@@ -28,9 +28,10 @@
 //    bf16 hi + lo pair, two MFMAs: a single bf16 p would carry 2^-9 relative
 //    error into outputs that cancel);
 //  * PV on v_mfma_f32_16x16x32_f16: A = p (rows = the 4 heads), B = V with
-//    the tokens on the contraction axis.  Each lane loads the same 8 dims of 8
-//    tokens (4 bytes each), regroups nibbles into token pairs with two
-//    bit-field merges per pair, converts (E2M1 -> f16 exact) and applies both
+//    the tokens on the contraction axis.  NVFP4 V is stored by dim (row d of
+//    the page's head slab: dim d of its 128 tokens, token 2i in the low nibble
+//    of byte i), so one 4-byte load gives a lane 8 consecutive tokens of one
+//    dim; each byte converts to a token pair (E2M1 -> f16 exact) and takes both
 //    tokens' E4M3 scales with one packed f16 multiply (code x scale has <= 6
 //    significant bits: exact in f16).  K's and V's tensor scales and sm_scale
 //    are applied in fp32 outside the MFMAs.
@@ -232,6 +233,7 @@ __device__ __forceinline__ void attn_workgroup(
     const uint8_t* vbase = vpool + row0 * kRowBytes;
 
     [[maybe_unused]] uint32_t vw[kPvSteps][8];
+    [[maybe_unused]] uint4 vq[FP4 ? kLaneDims : 1];  // NVFP4 V: dim d0 + t, tokens 32c .. 32c + 31
     [[maybe_unused]] uint4 vb[FP4 ? 1 : 8];
     [[maybe_unused]] uint4 vbe[(!FP4 && kVEarly) ? kPvSteps : 1][8];  // bf16 V, loaded early
     auto load_v = [&]() {
@@ -249,18 +251,11 @@ __device__ __forceinline__ void attn_workgroup(
             vw[s][e] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + 2 * d0);
       }
       if constexpr (FP4) {
+        // V by dim: row d0 + t holds dim d0 + t of the 128 tokens; this lane's
+        // tokens 32c .. 32c + 31 (all four PV steps) are its 16 bytes at 16c
 #pragma unroll
-        for (int s = 0; s < kPvSteps; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint8_t* src = vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + d0 / 2;
-            if constexpr (kLaneDims == 8)
-              vw[s][e] = *reinterpret_cast<const uint32_t*>(src);
-            else if constexpr (kLaneDims == 4)
-              vw[s][e] = *reinterpret_cast<const uint16_t*>(src);
-            else
-              vw[s][e] = *src;
-          }
+        for (int t = 0; t < kLaneDims; ++t)
+          vq[t] = *reinterpret_cast<const uint4*>(vbase + (size_t)(d0 + t) * (kBlock / 2) + 16 * c);
       }
     };
 
@@ -381,44 +376,39 @@ __device__ __forceinline__ void attn_workgroup(
     // ---- PV
 #pragma unroll
     for (int s = 0; s < kPvSteps; ++s) {
-      // A: p of head n (rows 4..15 zero), tokens 32s + 8c + e
+      // A: p of head n (rows 4..15 zero); the contraction's K index 8c + e is
+      // token 32c + 8s + e with NVFP4 V (a lane's V bytes of one dim are then
+      // one 16-B run), token 32s + 8c + e with bf16 V
+      const int tok0 = FP4 ? 32 * c + 8 * s : 32 * s + 8 * c;
       [[maybe_unused]] typename PV::Vec8 pa, pl;
       {
         const bool head = n < kHeadsPerGroup;
-        const uint4 w = head ? *reinterpret_cast<const uint4*>(&sm.p[wave][n][32 * s + 8 * c]) : make_uint4(0, 0, 0, 0);
+        const uint4 w = head ? *reinterpret_cast<const uint4*>(&sm.p[wave][n][tok0]) : make_uint4(0, 0, 0, 0);
         pa = __builtin_bit_cast(typename PV::Vec8, w);
         if constexpr (!FP4) {
-          const uint4 wl =
-              head ? *reinterpret_cast<const uint4*>(&sm.plo[wave][n][32 * s + 8 * c]) : make_uint4(0, 0, 0, 0);
+          const uint4 wl = head ? *reinterpret_cast<const uint4*>(&sm.plo[wave][n][tok0]) : make_uint4(0, 0, 0, 0);
           pl = __builtin_bit_cast(typename PV::Vec8, wl);
         }
       }
       if constexpr (FP4) {
-        // token pairs (2p, 2p+1): nibble k of both tokens side by side in one byte
-        uint32_t lo[4], hi[4];
+        // the E4M3 scales of token pairs tok0 + 2p, + 1 of this lane's group
         f16x2 sc[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t x = vw[s][2 * p], y = vw[s][2 * p + 1];
-          lo[p] = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-          hi[p] = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-          const int pair = 16 * s + 4 * c + p;
+          const int pair = (tok0 >> 1) + p;
           const uint32_t sw = *reinterpret_cast<const uint16_t*>(&sm.vsc[wave][pair * 16 + 2 * (d0 >> 4)]);
           sc[p] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
         }
-        // output tile t holds dims d0 + t
+        // output tile t holds dim d0 + t; word s of its run = tokens tok0 .. + 7,
+        // byte p = tokens tok0 + 2p, + 1
 #pragma unroll
-        for (int k = 0; k < kLaneDims / 2; ++k) {
-          f16x2 bl[4], bh[4];
+        for (int t = 0; t < kLaneDims; ++t) {
+          const uint32_t w = s == 0 ? vq[t].x : s == 1 ? vq[t].y : s == 2 ? vq[t].z : vq[t].w;
+          f16x2 bt[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            bl[p] = e2m1x2_to_f16x2(lo[p], k) * sc[p];
-            bh[p] = e2m1x2_to_f16x2(hi[p], k) * sc[p];
-          }
-          const f16x8 b0 = {bl[0].x, bl[0].y, bl[1].x, bl[1].y, bl[2].x, bl[2].y, bl[3].x, bl[3].y};
-          const f16x8 b1 = {bh[0].x, bh[0].y, bh[1].x, bh[1].y, bh[2].x, bh[2].y, bh[3].x, bh[3].y};
-          acc[2 * k] = PV::mfma(pa, b0, acc[2 * k]);
-          acc[2 * k + 1] = PV::mfma(pa, b1, acc[2 * k + 1]);
+          for (int p = 0; p < 4; ++p) bt[p] = e2m1x2_to_f16x2(w, p) * sc[p];
+          const f16x8 b = {bt[0].x, bt[0].y, bt[1].x, bt[1].y, bt[2].x, bt[2].y, bt[3].x, bt[3].y};
+          acc[t] = PV::mfma(pa, b, acc[t]);
         }
       } else {
         // bf16 V: 8 tokens x kLaneDims dims; tokens past the end zeroed

@@ -20,7 +20,11 @@
 // One 128-thread workgroup per query row; a thread quantises one 16-element
 // group (4 K heads x 8, 4 V heads x 8, then the index key's 8 groups), so the
 // kernel reads 32 B and writes 9 B (NVFP4) per thread: a few hundred KB per
-// decode step, latency-bound, nothing to tile.
+// decode step, latency-bound, nothing to tile.  NVFP4 V is stored by dim (row
+// d of a page's head slab holds dim d of its 128 tokens, token 2i in the low
+// nibble of byte i), so a token's 16 codes of a group go to one nibble in each
+// of 16 rows; two tokens of one chunk share each byte, so each nibble is set
+// with an atomic AND (clear) and an atomic OR on its 32-bit word.
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -89,6 +93,22 @@ __device__ __forceinline__ void quant_nvfp4_group(const float (&x)[16], float gs
   *scale = (uint8_t)s;
 }
 
+// One NVFP4 V group of token tok: codes into nibble tok % 2 of byte tok / 2 of
+// the 16 dim rows starting at row0 (64 B each), scale as K's.
+__device__ __forceinline__ void quant_nvfp4_group_v(const float (&x)[16], float gs, uint8_t* row0, int tok,
+                                                    uint8_t* scale) {
+  uint8_t packed[8];
+  quant_nvfp4_group(x, gs, packed, scale);
+  const int byte = tok >> 1, sh = 8 * (byte & 3) + 4 * (tok & 1);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t code = (packed[i >> 1] >> (4 * (i & 1))) & 15u;
+    uint32_t* word = reinterpret_cast<uint32_t*>(row0 + (size_t)i * (kBlock / 2) + (byte & ~3));
+    atomicAnd(word, ~(15u << sh));
+    atomicOr(word, code << sh);
+  }
+}
+
 // 16 values -> 16 bf16 (x / scale, nearest-even).
 __device__ __forceinline__ void store_bf16_group(const float (&x)[16], float scale, uint16_t* dst) {
   uint32_t w[8];
@@ -117,8 +137,10 @@ __global__ __launch_bounds__(kInsThreads) void kv_insert_kernel(const InsertArgs
     load16((is_v ? a.v_new : a.k_new) + ((size_t)row * kGroups + h) * kDim + 16 * c, x);
     const int64_t r = (page * kGroups + h) * kBlock + tok;
     const float gs = is_v ? a.v_scale : a.k_scale;
-    if (a.kv_nvfp4)
-      quant_nvfp4_group(x, gs, (is_v ? a.v : a.k) + r * (kDim / 2) + 8 * c, (is_v ? a.v_sf : a.k_sf) + r * 8 + c);
+    if (a.kv_nvfp4 && is_v)
+      quant_nvfp4_group_v(x, gs, a.v + ((page * kGroups + h) * kDim + 16 * c) * (kBlock / 2), tok, a.v_sf + r * 8 + c);
+    else if (a.kv_nvfp4)
+      quant_nvfp4_group(x, gs, a.k + r * (kDim / 2) + 8 * c, a.k_sf + r * 8 + c);
     else
       store_bf16_group(x, gs, reinterpret_cast<uint16_t*>(is_v ? a.v : a.k) + r * kDim + 16 * c);
   } else if (u < 2 * kGroups * 8 + 8) {  // the index key: group c

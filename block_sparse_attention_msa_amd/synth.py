@@ -12,10 +12,14 @@ Stored formats (the layouts the library reads):
   idx_k  FP8 E4M3 (uint8) or bf16  [P][128 tokens][128], or NVFP4 uint8
          [P][128 tokens][64] + E4M3 scales idx_sf uint8 [P][128 tokens][8]
          (one shared index head; its fp32 tensor scale is idx_scale)
-  k, v   NVFP4: uint8 [P][Hkv][128 tokens][64]   (element 2i in the low nibble)
+  k      NVFP4: uint8 [P][Hkv][128 tokens][64]   (element 2i in the low nibble)
          + E4M3 scales uint8 [P][Hkv][128 tokens][8]  (one per 16 elements)
-         + one fp32 tensor scale each;
-         bf16: [P][Hkv][128 tokens][128]
+         + one fp32 tensor scale;
+  v      NVFP4: uint8 [P][Hkv][128 dims][64], each page's V transposed: row d
+         holds dim d of the page's 128 tokens, token 2i in the low nibble of
+         byte i; E4M3 scales as K's, [P][Hkv][128 tokens][8] (one per token and
+         16 dims), + one fp32 tensor scale;
+  k, v   bf16: [P][Hkv][128 tokens][128]
   block_table int32 [num_seqs][max_blocks_per_seq]; seq_lens int32 [num_seqs]
 
 NVFP4 quantiser (harness only; results do not depend on it because both sides
@@ -72,8 +76,8 @@ def nvfp4_tensor_scale(amax: float) -> float:
     return float(amax) / (6.0 * E4M3_MAX) if amax > 0 else 1.0
 
 
-def quant_nvfp4(x: torch.Tensor, gs: float):
-    """x [..., 128] float -> (packed uint8 [..., 64], scales uint8 [..., 8])."""
+def quant_nvfp4_codes(x: torch.Tensor, gs: float):
+    """x [..., 128] float -> (E2M1 codes uint8 [..., 128], scales uint8 [..., 8])."""
     shp = x.shape
     xg = x.float().reshape(*shp[:-1], DIM // 16, 16)
     amax16 = xg.abs().amax(dim=-1)
@@ -81,9 +85,26 @@ def quant_nvfp4(x: torch.Tensor, gs: float):
     sc_val = sc.view(torch.float8_e4m3fn).float()              # exact decode of the stored scale
     denom = (sc_val * gs).unsqueeze(-1)
     y = torch.where(denom > 0, xg / torch.where(denom > 0, denom, torch.ones_like(denom)), torch.zeros_like(xg))
-    codes = quant_e2m1_codes(y).reshape(*shp[:-1], DIM)
-    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
-    return packed.contiguous(), sc.contiguous()
+    return quant_e2m1_codes(y).reshape(*shp[:-1], DIM), sc.contiguous()
+
+
+def pack_nibbles(codes: torch.Tensor) -> torch.Tensor:
+    """[..., 2n] codes -> [..., n] bytes, element 2i in the low nibble of byte i."""
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).contiguous()
+
+
+def quant_nvfp4(x: torch.Tensor, gs: float):
+    """x [..., 128] float -> (packed uint8 [..., 64], scales uint8 [..., 8])."""
+    codes, sc = quant_nvfp4_codes(x, gs)
+    return pack_nibbles(codes), sc
+
+
+def quant_nvfp4_v(x: torch.Tensor, gs: float):
+    """V of whole pages, x [..., 128 tokens, 128 dims] float -> (packed uint8
+    [..., 128 dims, 64]: row d holds dim d of the tokens, token 2i in the low
+    nibble of byte i; scales uint8 [..., 128 tokens, 8])."""
+    codes, sc = quant_nvfp4_codes(x, gs)
+    return pack_nibbles(codes.transpose(-1, -2)), sc
 
 
 @dataclass
@@ -329,7 +350,7 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
         raise ValueError(idx_dtype)
 
     # ---- K / V pools (i.i.d. N(0,1), generated page-chunk by page-chunk)
-    def kv_pool(seed_k):
+    def kv_pool(seed_k, is_v):
         if kv_dtype == "bf16":
             gk = _gen(dev, seed_k)
             out = torch.empty(P, G, BLOCK, DIM, dtype=torch.bfloat16, device=dev)
@@ -350,11 +371,11 @@ def make_workload(*, name: str = "custom", seq_lens, q_len: int = 1, kv_dtype: s
         for c0 in range(0, P, kv_chunk_pages):
             c1 = min(P, c0 + kv_chunk_pages)
             x = torch.randn(c1 - c0, G, BLOCK, DIM, generator=gk, device=dev)
-            packed[c0:c1], scales[c0:c1] = quant_nvfp4(x, gs)
+            packed[c0:c1], scales[c0:c1] = quant_nvfp4_v(x, gs) if is_v else quant_nvfp4(x, gs)
         return packed, scales, gs
 
-    k, k_sf, k_scale = kv_pool(seed * 7919 + 5)
-    v, v_sf, v_scale = kv_pool(seed * 7919 + 6)
+    k, k_sf, k_scale = kv_pool(seed * 7919 + 5, False)
+    v, v_sf, v_scale = kv_pool(seed * 7919 + 6, True)
 
     return Workload(name=name, num_seqs=S, q_len=q_len, num_q_heads=Hq, num_kv_heads=G,
                     max_blocks_per_seq=mbps, num_pages=P, kv_dtype=kv_dtype, idx_dtype=idx_dtype,

@@ -41,11 +41,17 @@
  *           [num_pages][128 tokens][64] (element 2i in the low nibble of byte
  *           i, E2M1) plus idx_sf uint8 E4M3 [num_pages][128 tokens][8];
  *           value = e2m1 x scale x idx_scale.
- *  - k, v   NVFP4: uint8 [num_pages][num_kv_heads][128 tokens][64], element 2i
- *           in the low nibble of byte i (E2M1), plus k_sf / v_sf uint8 E4M3
+ *  - k      NVFP4: uint8 [num_pages][num_kv_heads][128 tokens][64], element 2i
+ *           in the low nibble of byte i (E2M1), plus k_sf uint8 E4M3
  *           [num_pages][num_kv_heads][128 tokens][8] (one scale per 16
- *           consecutive elements); value = e2m1 x scale x k_scale (v_scale).
- *           bf16: [num_pages][num_kv_heads][128][128], value = stored x k_scale.
+ *           consecutive elements); value = e2m1 x scale x k_scale.
+ *  - v      NVFP4, stored by dim: uint8 [num_pages][num_kv_heads][128 dims][64],
+ *           row d holding dim d of the page's 128 tokens, token 2i in the low
+ *           nibble of byte i (E2M1), plus v_sf as k_sf (one scale per token
+ *           and 16 consecutive dims); value = e2m1 x scale x v_scale.  (The
+ *           attention's PV contraction runs over tokens, so a dim's tokens are
+ *           contiguous here.)
+ *  - k, v   bf16: [num_pages][num_kv_heads][128][128], value = stored x scale.
  *  - block_table int32 [num_seqs][max_blocks_per_seq]; seq_lens int32 [num_seqs].
  */
 #ifndef MSA_H

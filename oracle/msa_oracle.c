@@ -51,7 +51,8 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
   int32_t num_pages;
-  int32_t kv_nvfp4;  /* 0: K/V bf16 [P][Hkv][128][128]; 1: NVFP4 values [P][Hkv][128][64] + E4M3 scales [P][Hkv][128][8] */
+  int32_t kv_nvfp4;  /* 0: K/V bf16 [P][Hkv][128 tok][128]; 1: NVFP4 K values [P][Hkv][128 tok][64], V values
+                        transposed [P][Hkv][128 dims][64 (128 tokens)], E4M3 scales [P][Hkv][128 tok][8] */
   int32_t idx_fmt;   /* index keys: 0 bf16 [P][128][128]; 1 FP8 E4M3 [P][128][128];
                         2 NVFP4 values [P][128][64] + E4M3 scales idx_sf [P][128][8] */
   double sm_scale;
@@ -106,18 +107,28 @@ double msa_oracle_e2m1(uint8_t nibble) {
 }
 
 /* One element d of token row `tok` (0..127) of KV head `h` in physical page
- * `page` of the K or V pool.  NVFP4: element 2k sits in the low nibble of
- * byte k, and elements 16c..16c+15 share scale byte c of the token. */
+ * `page` of the K or V pool.  NVFP4 K: element 2k of the token's row sits in
+ * the low nibble of byte k.  NVFP4 V (`transposed`): the page's (head) slab is
+ * stored by dim, 128 rows of 64 B, row d holding dim d of the 128 tokens,
+ * token 2k in the low nibble of byte k.  Both: elements 16c..16c+15 of a token
+ * share its scale byte c. */
 static double kv_elem(const oracle_problem* p, const void* pool, const uint8_t* sf, double tensor_scale,
-                      int64_t page, int h, int tok, int d) {
+                      int64_t page, int h, int tok, int d, int transposed) {
   int64_t row = (page * p->num_kv_heads + h) * OR_BLOCK + tok;
   if (!p->kv_nvfp4) {
     const uint16_t* x = (const uint16_t*)pool;
     return msa_oracle_bf16(x[row * OR_DIM + d]) * tensor_scale;
   }
   const uint8_t* x = (const uint8_t*)pool;
-  uint8_t byte = x[row * (OR_DIM / 2) + d / 2];
-  uint8_t nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  uint8_t nib;
+  if (transposed) {
+    int64_t drow = (page * p->num_kv_heads + h) * OR_DIM + d;
+    uint8_t byte = x[drow * (OR_BLOCK / 2) + tok / 2];
+    nib = (tok & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  } else {
+    uint8_t byte = x[row * (OR_DIM / 2) + d / 2];
+    nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  }
   double group_scale = msa_oracle_e4m3(sf[row * (OR_DIM / 16) + d / 16]);
   return msa_oracle_e2m1(nib) * group_scale * tensor_scale;
 }
@@ -252,7 +263,8 @@ int msa_oracle_attend(const oracle_problem* p, int row, int g, const int32_t* se
     double m = -INFINITY;
     for (int n = 0; n < nk; ++n) {
       double s = 0.0;
-      for (int d = 0; d < OR_DIM; ++d) s += q[d] * kv_elem(p, p->k, p->k_sf, p->k_scale, keys_page[n], g, keys_tok[n], d);
+      for (int d = 0; d < OR_DIM; ++d)
+        s += q[d] * kv_elem(p, p->k, p->k_sf, p->k_scale, keys_page[n], g, keys_tok[n], d, 0);
       z[n] = p->sm_scale * s;
       if (z[n] > m) m = z[n];
     }
@@ -261,7 +273,8 @@ int msa_oracle_attend(const oracle_problem* p, int row, int g, const int32_t* se
     for (int n = 0; n < nk; ++n) {
       double w = exp(z[n] - m);
       denom += w;
-      for (int d = 0; d < OR_DIM; ++d) vrow[d] = kv_elem(p, p->v, p->v_sf, p->v_scale, keys_page[n], g, keys_tok[n], d);
+      for (int d = 0; d < OR_DIM; ++d)
+        vrow[d] = kv_elem(p, p->v, p->v_sf, p->v_scale, keys_page[n], g, keys_tok[n], d, 1);
       for (int d = 0; d < OR_DIM; ++d) o[d] += w * vrow[d];
     }
     for (int d = 0; d < OR_DIM; ++d) o[d] /= denom;
@@ -409,7 +422,19 @@ int msa_oracle_kv_insert(const oracle_problem* p, const float* k_new, const floa
       for (int h = 0; h < G; ++h) {
         const float* x = src + ((int64_t)row * G + h) * OR_DIM;
         int64_t r = (page * G + h) * OR_BLOCK + tok;
-        if (p->kv_nvfp4) {
+        if (p->kv_nvfp4 && which) {
+          /* V: the group's 16 codes go to 16 dim rows of the transposed slab */
+          for (int c = 0; c < OR_DIM / 16; ++c) {
+            uint8_t packed[8];
+            msa_oracle_quant_nvfp4_group(x + 16 * c, gs, packed, sf + r * (OR_DIM / 16) + c);
+            for (int i = 0; i < 16; ++i) {
+              uint8_t code = (uint8_t)((packed[i / 2] >> (4 * (i & 1))) & 15);
+              int64_t drow = (page * G + h) * OR_DIM + 16 * c + i;
+              uint8_t* byte = (uint8_t*)pool + drow * (OR_BLOCK / 2) + tok / 2;
+              *byte = (tok & 1) ? (uint8_t)((*byte & 0x0F) | (code << 4)) : (uint8_t)((*byte & 0xF0) | code);
+            }
+          }
+        } else if (p->kv_nvfp4) {
           for (int c = 0; c < OR_DIM / 16; ++c)
             msa_oracle_quant_nvfp4_group(x + 16 * c, gs, (uint8_t*)pool + r * (OR_DIM / 2) + 8 * c, sf + r * (OR_DIM / 16) + c);
         } else {

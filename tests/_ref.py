@@ -32,6 +32,18 @@ def nvfp4_t(packed: np.ndarray, scales: np.ndarray, tensor_scale: float) -> torc
     return vals * sc * tensor_scale
 
 
+def nvfp4_v_t(packed_t: np.ndarray, scales: np.ndarray, tensor_scale: float) -> torch.Tensor:
+    """V pages as stored, [..., 128 dims, 64] (row d: the 128 tokens' dim d,
+    token 2i in the low nibble of byte i) + [..., 128 tokens, 8] E4M3 scales
+    -> fp64 [..., 128 tokens, 128 dims]."""
+    p = torch.from_numpy(np.ascontiguousarray(packed_t)).to(torch.int64)
+    lo, hi = p & 15, p >> 4
+    codes = torch.stack([lo, hi], dim=-1).reshape(*p.shape[:-1], 128).transpose(-1, -2)   # [..., tok, dim]
+    vals = E2M1_TABLE[codes]
+    sc = e4m3_t(scales).repeat_interleave(16, dim=-1)
+    return vals * sc * tensor_scale
+
+
 def dense_seq(P, b: int):
     """Logical-order fp64 tensors of sequence b: idx [L,128], K [G,L,128], V [G,L,128]."""
     a = P.arrays
@@ -47,7 +59,7 @@ def dense_seq(P, b: int):
     idx = idx.reshape(nb * 128, 128)[:L]
     if a["k_sf"] is not None:
         K = nvfp4_t(a["k"][pages], a["k_sf"][pages], P.k_scale)
-        V = nvfp4_t(a["v"][pages], a["v_sf"][pages], P.v_scale)
+        V = nvfp4_v_t(a["v"][pages], a["v_sf"][pages], P.v_scale)
     else:
         K = bf16_t(a["k"][pages]) * P.k_scale
         V = bf16_t(a["v"][pages]) * P.v_scale

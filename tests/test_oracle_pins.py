@@ -540,8 +540,10 @@ def test_kv_insert_writes_the_right_rows():
         bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
         P.kv_insert(bits(kf), bits(vf), bits(xf))
         a = P.arrays
-        touched = {k: np.zeros(v.shape[:3] if k in ("k", "v", "k_sf", "v_sf") else v.shape[:2], bool)
-                   for k, v in a.items() if k in ("k", "v", "k_sf", "v_sf", "idx_k", "idx_sf") and v is not None}
+        touched = {k: np.zeros(v.shape[:3] if k in ("k", "k_sf", "v_sf") else v.shape[:2], bool)
+                   for k, v in a.items() if k in ("k", "k_sf", "v_sf", "idx_k", "idx_sf") and v is not None}
+        # V is stored by dim: a written token changes one nibble of byte tok // 2 of each dim row
+        v_expect = before["v"].copy()
         for row in range(rows):
             b, i = divmod(row, w.q_len)
             L = int(a["seq_lens"][b])
@@ -549,11 +551,17 @@ def test_kv_insert_writes_the_right_rows():
                 continue
             pos = L - w.q_len + i
             page, tok = int(a["block_table"][b, pos // 128]), pos % 128
-            for name, src, gs in (("k", kf, w.k_scale), ("v", vf, w.v_scale)):
-                packed, sc = synth.quant_nvfp4(src[row].float(), gs)
-                assert np.array_equal(a[name][page, :, tok], packed.numpy())
-                assert np.array_equal(a[name + "_sf"][page, :, tok], sc.numpy())
-                touched[name][page, :, tok] = touched[name + "_sf"][page, :, tok] = True
+            packed, sc = synth.quant_nvfp4(kf[row].float(), w.k_scale)
+            assert np.array_equal(a["k"][page, :, tok], packed.numpy())
+            assert np.array_equal(a["k_sf"][page, :, tok], sc.numpy())
+            touched["k"][page, :, tok] = touched["k_sf"][page, :, tok] = True
+            # V: the token's codes sit in nibble tok % 2 of byte tok // 2 of every dim row
+            codes, sc = synth.quant_nvfp4_codes(vf[row].float(), w.v_scale)
+            sh = 4 * (tok % 2)
+            cell = v_expect[page, :, :, tok // 2]
+            v_expect[page, :, :, tok // 2] = (cell & (0xF0 >> sh)) | (codes.numpy().astype(np.uint8) << sh)
+            assert np.array_equal(a["v_sf"][page, :, tok], sc.numpy())
+            touched["v_sf"][page, :, tok] = True
             if idx_dtype == "nvfp4":
                 packed, sc = synth.quant_nvfp4(xf[row].float(), w.idx_scale)
                 assert np.array_equal(a["idx_k"][page, tok], packed.numpy())
@@ -566,3 +574,4 @@ def test_kv_insert_writes_the_right_rows():
             touched["idx_k"][page, tok] = True
         for name, t in touched.items():
             assert np.array_equal(a[name][~t], before[name][~t]), name
+        assert np.array_equal(a["v"], v_expect)
