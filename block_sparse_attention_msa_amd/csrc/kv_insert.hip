@@ -23,8 +23,12 @@
 // decode step, latency-bound, nothing to tile.  NVFP4 V is stored by dim (row
 // d of a page's head slab holds dim d of its 128 tokens, token 2i in the low
 // nibble of byte i), so a token's 16 codes of a group go to one nibble in each
-// of 16 rows; two tokens of one chunk share each byte, so each nibble is set
-// with an atomic AND (clear) and an atomic OR on its 32-bit word.
+// of 16 rows, and tokens 2i, 2i + 1 share each byte.  The thread of an even
+// token whose odd partner is written by the same call quantises the partner's
+// group too and stores whole bytes (the partner stores only its scale); a
+// token whose partner is not in the call sets its own nibble of each byte with
+// an atomic AND (clear) and an atomic OR on the byte's 32-bit word, leaving the
+// other nibble as it is (no other writer touches that nibble in the call).
 #include "msa_device.hpp"
 #include "msa_kernels.hpp"
 
@@ -70,8 +74,9 @@ __device__ __forceinline__ void load16(const uint16_t* src, float (&x)[16]) {
   }
 }
 
-// One NVFP4 group: 8 packed bytes (element 2k in the low nibble of byte k) + scale.
-__device__ __forceinline__ void quant_nvfp4_group(const float (&x)[16], float gs, uint8_t* packed, uint8_t* scale) {
+// One NVFP4 group in registers: the 16 codes packed (element 2k in the low
+// nibble of byte k: elements 0..7 in .x, 8..15 in .y) and the scale code.
+__device__ __forceinline__ uint2 nvfp4_group(const float (&x)[16], float gs, uint32_t& scale) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
@@ -89,23 +94,39 @@ __device__ __forceinline__ void quant_nvfp4_group(const float (&x)[16], float gs
 #pragma unroll
     for (int i = 0; i < 8; ++i) hi |= e2m1_rne(x[8 + i] / d) << (4 * i);
   }
-  *reinterpret_cast<uint2*>(packed) = make_uint2(lo, hi);
+  scale = s;
+  return make_uint2(lo, hi);
+}
+
+// One NVFP4 group: 8 packed bytes (element 2k in the low nibble of byte k) + scale.
+__device__ __forceinline__ void quant_nvfp4_group(const float (&x)[16], float gs, uint8_t* packed, uint8_t* scale) {
+  uint32_t s;
+  *reinterpret_cast<uint2*>(packed) = nvfp4_group(x, gs, s);
   *scale = (uint8_t)s;
 }
 
-// One NVFP4 V group of token tok: codes into nibble tok % 2 of byte tok / 2 of
-// the 16 dim rows starting at row0 (64 B each), scale as K's.
-__device__ __forceinline__ void quant_nvfp4_group_v(const float (&x)[16], float gs, uint8_t* row0, int tok,
-                                                    uint8_t* scale) {
-  uint8_t packed[8];
-  quant_nvfp4_group(x, gs, packed, scale);
+// One NVFP4 V group of token tok into byte tok / 2 of the 16 dim rows starting
+// at row0 (64 B each); its scale as K's.  With x_next (the group of token
+// tok + 1, tok even, written by the same call) both nibbles are stored whole;
+// otherwise only this token's nibble changes.
+__device__ __forceinline__ void quant_nvfp4_group_v(const float (&x)[16], const float (&x_next)[16], bool both,
+                                                    float gs, uint8_t* row0, int tok, uint8_t* scale) {
+  uint32_t s, s_next;
+  const uint2 own = nvfp4_group(x, gs, s);
+  *scale = (uint8_t)s;
+  const uint2 next = both ? nvfp4_group(x_next, gs, s_next) : make_uint2(0u, 0u);  // s_next: the partner stores it
   const int byte = tok >> 1, sh = 8 * (byte & 3) + 4 * (tok & 1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t code = (packed[i >> 1] >> (4 * (i & 1))) & 15u;
-    uint32_t* word = reinterpret_cast<uint32_t*>(row0 + (size_t)i * (kBlock / 2) + (byte & ~3));
-    atomicAnd(word, ~(15u << sh));
-    atomicOr(word, code << sh);
+    const uint32_t code = ((i < 8 ? own.x : own.y) >> (4 * (i & 7))) & 15u;
+    uint8_t* rowi = row0 + (size_t)i * (kBlock / 2);
+    if (both) {
+      rowi[byte] = (uint8_t)(code | ((((i < 8 ? next.x : next.y) >> (4 * (i & 7))) & 15u) << 4));
+    } else {
+      uint32_t* word = reinterpret_cast<uint32_t*>(rowi + (byte & ~3));
+      atomicAnd(word, ~(15u << sh));
+      atomicOr(word, code << sh);
+    }
   }
 }
 
@@ -137,9 +158,23 @@ __global__ __launch_bounds__(kInsThreads) void kv_insert_kernel(const InsertArgs
     load16((is_v ? a.v_new : a.k_new) + ((size_t)row * kGroups + h) * kDim + 16 * c, x);
     const int64_t r = (page * kGroups + h) * kBlock + tok;
     const float gs = is_v ? a.v_scale : a.k_scale;
-    if (a.kv_nvfp4 && is_v)
-      quant_nvfp4_group_v(x, gs, a.v + ((page * kGroups + h) * kDim + 16 * c) * (kBlock / 2), tok, a.v_sf + r * 8 + c);
-    else if (a.kv_nvfp4)
+    if (a.kv_nvfp4 && is_v) {
+      // the partner token tok ^ 1 (same page) is written by this call when it is
+      // the row after (tok even) or before (tok odd) in the same sequence's chunk
+      const int i_row = row % a.q_len;
+      const bool even = (tok & 1) == 0;
+      const bool partner = even ? i_row + 1 < a.q_len : i_row > 0;
+      uint8_t* row0 = a.v + ((page * kGroups + h) * kDim + 16 * c) * (kBlock / 2);
+      if (partner && !even) {
+        uint32_t s;
+        nvfp4_group(x, gs, s);  // the even partner stores the codes
+        a.v_sf[r * 8 + c] = (uint8_t)s;
+      } else {
+        float xn[16] = {};
+        if (partner) load16(a.v_new + ((size_t)(row + 1) * kGroups + h) * kDim + 16 * c, xn);
+        quant_nvfp4_group_v(x, xn, partner, gs, row0, tok, a.v_sf + r * 8 + c);
+      }
+    } else if (a.kv_nvfp4)
       quant_nvfp4_group(x, gs, a.k + r * (kDim / 2) + 8 * c, a.k_sf + r * 8 + c);
     else
       store_bf16_group(x, gs, reinterpret_cast<uint16_t*>(is_v ? a.v : a.k) + r * kDim + 16 * c);
