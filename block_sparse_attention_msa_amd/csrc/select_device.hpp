@@ -12,8 +12,9 @@
 //
 // Algorithm (one active wave per 1,024 candidate blocks, 16 keys per lane):
 //  1. wave w takes blocks j = 1024 w + lane + 64 e (e < 16; coalesced loads,
-//     all issued before use) as 64-bit keys (ordered score << 32 | ~j), and,
-//     for the attention, the blocks' page ids from the block table;
+//     all issued before use, and before the row length is known) as 64-bit
+//     keys (ordered score << 32 | ~j), and, for the attention, the blocks'
+//     page ids from the block table;
 //  2. each active wave sorts its 64 lane-best scores (32-bit bitonic, DPP lane
 //     moves where they exist); the wave's 15th best score T_w bounds the 15th
 //     best key overall from below (15 distinct blocks reach it), and so does
@@ -195,17 +196,44 @@ __device__ __forceinline__ int sel_ballots(const uint64_t (&keys)[E], uint64_t t
   return total;
 }
 
+// One wave's raw candidates: 16 block scores and block-table entries per lane.
+struct SelLoads {
+  float sv[kSelKeysPerLane];
+  int32_t pages[kSelKeysPerLane];
+};
+
+// Issues this wave's loads of blocks 1,024 w + lane + 64 e (e < 16), clamped
+// to the row's cap entries, so that they need not wait for the row length:
+// the scores s[] and, when PAGES, the block-table entries (read, never
+// followed).  Waves that start past the row load nothing.  Entries past the
+// candidates are discarded by select_blocks, so they may hold anything.
+template <bool PAGES>
+__device__ __forceinline__ void select_load(const float* __restrict__ s, const int32_t* __restrict__ bt_row, int cap,
+                                            SelLoads& ld) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  if (wave * kSelBlocksPerWave >= cap) return;  // wave-uniform
+  const int j0 = wave * kSelBlocksPerWave + lane;
+#pragma unroll
+  for (int e = 0; e < kSelKeysPerLane; ++e) {
+    const int idx = min(j0 + e * kWave, cap - 1);
+    ld.sv[e] = s[idx];
+    ld.pages[e] = PAGES ? bt_row[idx] : 0;
+  }
+}
+
 // Selection for one (row, group) by a workgroup of NT threads; r must be below
 // sel_max_blocks<NT>() so that every candidate fits the active waves'
 // registers (1,024 per wave).
-// s: block scores of the row/group; bt_row: its block table row (read only
-// when PAGES); r: the recent block (0 <= r < row length).  Writes 16 ids
-// (ascending, -1 padded) to out[] and, when PAGES, their page ids to
-// out_page[] (0 for padding), then synchronises the workgroup so LDS outputs
-// are readable by every thread.  Every thread of the workgroup must call it.
+// ld: the wave's select_load of the row/group's scores, with a cap above r;
+// bt_row: its block table row (read only when PAGES); r: the recent block
+// (0 <= r < row length).  Writes 16 ids (ascending, -1 padded) to out[] and,
+// when PAGES, their page ids to out_page[] (0 for padding), then synchronises
+// the workgroup so LDS outputs are readable by every thread.  Every thread of
+// the workgroup must call it.
 template <int NT, bool PAGES>
-__device__ void select_blocks(const float* __restrict__ s, const int32_t* __restrict__ bt_row, int r,
-                              SelectSmem<NT>& sm, int32_t* out, int32_t* out_page) {
+__device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r, SelectSmem<NT>& sm,
+                              int32_t* out, int32_t* out_page) {
   constexpr int kWaves = NT / kWave;
   static_assert(NT % kWave == 0 && kWaves >= 1, "whole waves");
   const int tid = threadIdx.x;
@@ -229,18 +257,12 @@ __device__ void select_blocks(const float* __restrict__ s, const int32_t* __rest
   uint64_t keys[kSelKeysPerLane];
   int32_t pages[kSelKeysPerLane];
   uint32_t best = 0;
-  if (wave < active) {
-    float sv[kSelKeysPerLane];
-#pragma unroll
-    for (int e = 0; e < kSelKeysPerLane; ++e) {
-      const int idx = min(j0 + e * kWave, n - 1);
-      sv[e] = s[idx];
-      pages[e] = PAGES ? bt_row[idx] : 0;
-    }
+  if (wave < active) {  // loaded: 1,024 w < n < cap
 #pragma unroll
     for (int e = 0; e < kSelKeysPerLane; ++e) {
       const int j = j0 + e * kWave;
-      keys[e] = j < n ? block_key(sv[e], j) : 0;
+      pages[e] = ld.pages[e];
+      keys[e] = j < n ? block_key(ld.sv[e], j) : 0;
       const uint32_t hi = (uint32_t)(keys[e] >> 32);
       best = hi > best ? hi : best;
     }
