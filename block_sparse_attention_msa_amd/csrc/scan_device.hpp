@@ -41,6 +41,10 @@ __device__ __forceinline__ void scan_wave(const uint8_t* __restrict__ idx_pool, 
                                           int L, const uint16_t* __restrict__ iq_row, float* __restrict__ bs_row,
                                           int mbps, int jbeg, int jend, float idx_scale, int lane) {
   using Geo = ScanGeom<FP8>;
+  // block-table entries are read one page ahead of their use, before the
+  // visibility test (entries of the row: jbeg < jend <= mbps); an invisible
+  // block's entry is never followed
+  int32_t pg = bt_row[jbeg];
   const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
   const int my_group = lane_group(lane);
 
@@ -57,11 +61,13 @@ __device__ __forceinline__ void scan_wave(const uint8_t* __restrict__ idx_pool, 
   }
 
   for (int j = jbeg; j < jend; ++j) {
+    const int32_t pg_j = pg;
+    if (j + 1 < jend) pg = bt_row[j + 1];
     if (j >= nbv) {
       if (lane < 4) bs_row[my_group * mbps + j] = -INFINITY;
       continue;
     }
-    const int64_t page = bt_row[j];
+    const int64_t page = pg_j;
     const uint8_t* base = idx_pool + page * Geo::kPageBytes + lane * 16;
     const int visible = L - j * kBlock;  // tokens of this block at or before the query
     float m = -INFINITY;
@@ -147,12 +153,18 @@ __device__ __forceinline__ void scan_wave_nvfp4(const uint8_t* __restrict__ code
     }
   }
 
+  // block-table entries are read one page ahead of their use, before the
+  // visibility test (entries of the row: jbeg < jend <= mbps); an invisible
+  // block's entry is never followed
+  int32_t pg = bt_row[jbeg];
   for (int j = jbeg; j < jend; ++j) {
+    const int32_t pg_j = pg;
+    if (j + 1 < jend) pg = bt_row[j + 1];
     if (j >= nbv) {
       if (lane < 4) bs_row[lane * mbps + j] = -INFINITY;
       continue;
     }
-    const int64_t page = bt_row[j];
+    const int64_t page = pg_j;
     const uint8_t* kbase = codes + page * (kBlock * kDim / 2);
     u32x4 kv[8];
 #pragma unroll
@@ -278,6 +290,10 @@ template <int NT, class Cols>
 __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ idx_pool,
                                                    const int32_t* __restrict__ bt_row, const Cols& cm, int jbeg,
                                                    int jend, float idx_scale, uint8_t* lds, int lane) {
+  // block-table entries are read one page ahead of their use, before the
+  // visibility test (entries of the row: jbeg < jend <= mbps); an invisible
+  // block's entry is never followed
+  int32_t pg = bt_row[jbeg];
   const int nbv = cm.nbv;
   const int c = lane >> 4;
   const int n = lane & 15;
@@ -312,13 +328,15 @@ __device__ __forceinline__ void scan_wave_fp8_mfma(const uint8_t* __restrict__ i
   }
 
   for (int j = jbeg; j < jend; ++j) {
+    const int32_t pg_j = pg;
+    if (j + 1 < jend) pg = bt_row[j + 1];
     if (j >= nbv) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (c == 0 && 16 * t + n < ncols) *cm.at(brow[t], j) = -INFINITY;
       continue;
     }
-    const int64_t page = bt_row[j];
+    const int64_t page = pg_j;
     const uint8_t* base = idx_pool + page * (kBlock * kDim) + lane * 16;
     u32x4 kv[16];
 #pragma unroll
@@ -411,6 +429,10 @@ __device__ __forceinline__ void scan_wave_nvfp4_cols(const uint8_t* __restrict__
                                                      const uint16_t* __restrict__ iq_seq, float* __restrict__ bs_seq,
                                                      int mbps, int jbeg, int jend, float idx_scale,
                                                      uint8_t* lds_sc, int lane) {
+  // block-table entries are read one page ahead of their use, before the
+  // visibility test (entries of the row: jbeg < jend <= mbps); an invisible
+  // block's entry is never followed
+  int32_t pg = bt_row[jbeg];
   const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
   const int c = lane >> 4;
   const int n = lane & 15;
@@ -451,13 +473,15 @@ __device__ __forceinline__ void scan_wave_nvfp4_cols(const uint8_t* __restrict__
   }
 
   for (int j = jbeg; j < jend; ++j) {
+    const int32_t pg_j = pg;
+    if (j + 1 < jend) pg = bt_row[j + 1];
     if (j >= nbv) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (c == 0 && 16 * t + n < ncols) bs_seq[(size_t)(16 * t + n) * mbps + j] = -INFINITY;
       continue;
     }
-    const int64_t page = bt_row[j];
+    const int64_t page = pg_j;
     const uint8_t* kbase = codes + page * (kBlock * kDim / 2) + n * (kDim / 2) + 16 * c;
     u32x4 kv[8];
 #pragma unroll
@@ -536,6 +560,10 @@ __device__ __forceinline__ void scan_wave_nvfp4_exact_cols(const uint8_t* __rest
                                                            const int32_t* __restrict__ bt_row, const Cols& cm,
                                                            int jbeg, int jend, float idx_scale, uint8_t* lds_sc,
                                                            int lane) {
+  // block-table entries are read one page ahead of their use, before the
+  // visibility test (entries of the row: jbeg < jend <= mbps); an invisible
+  // block's entry is never followed
+  int32_t pg = bt_row[jbeg];
   const int nbv = cm.nbv;
   const int c = lane >> 4;
   const int n = lane & 15;
@@ -563,13 +591,15 @@ __device__ __forceinline__ void scan_wave_nvfp4_exact_cols(const uint8_t* __rest
   }
 
   for (int j = jbeg; j < jend; ++j) {
+    const int32_t pg_j = pg;
+    if (j + 1 < jend) pg = bt_row[j + 1];
     if (j >= nbv) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (c == 0 && 16 * t + n < ncols) *cm.at(brow[t], j) = -INFINITY;
       continue;
     }
-    const int64_t page = bt_row[j];
+    const int64_t page = pg_j;
     const uint8_t* kbase = codes + page * (kBlock * kDim / 2) + n * (kDim / 2) + 16 * c;
     u32x4 kv[8];
 #pragma unroll
