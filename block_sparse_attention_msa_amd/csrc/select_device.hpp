@@ -222,44 +222,28 @@ __device__ __forceinline__ void select_load(const float* __restrict__ s, const i
   }
 }
 
-// Selection for one (row, group) by a workgroup of NT threads; r must be below
-// sel_max_blocks<NT>() so that every candidate fits the active waves'
-// registers (1,024 per wave).
-// ld: the wave's select_load of the row/group's scores, with a cap above r;
-// bt_row: its block table row (read only when PAGES); r: the recent block
-// (0 <= r < row length).  Writes 16 ids (ascending, -1 padded) to out[] and,
-// when PAGES, their page ids to out_page[] (0 for padding), then synchronises
-// the workgroup so LDS outputs are readable by every thread.  Every thread of
-// the workgroup must call it.
-template <int NT, bool PAGES>
-__device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r, SelectSmem<NT>& sm,
-                              int32_t* out, int32_t* out_page) {
-  constexpr int kWaves = NT / kWave;
-  static_assert(NT % kWave == 0 && kWaves >= 1, "whole waves");
+// The selection proper for n >= 16 candidates (blocks 0 .. n - 1, n = r), with
+// E of the 16 loaded keys per lane in use: 1 for n <= 64, 4 for n <= 256,
+// else 16 (the candidates beyond a lane's first E keys are past the row).
+template <int NT, bool PAGES, int E>
+__device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r,
+                                            SelectSmem<NT>& sm, int32_t* out, int32_t* out_page) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  if (r + 1 <= kTopK) {  // every visible block is kept
-    if (tid < kTopK) {
-      out[tid] = tid <= r ? tid : -1;
-      if constexpr (PAGES) out_page[tid] = tid <= r ? bt_row[tid] : 0;
-    }
-    __syncthreads();
-    return;
-  }
-  const int n = r;  // candidates: blocks 0 .. r-1 (n >= 16)
+  const int n = r;
   const int active = (n + kSelBlocksPerWave - 1) / kSelBlocksPerWave;
   const int j0 = wave * kSelBlocksPerWave + lane;
   int32_t recent_page = 0;
   if (PAGES && tid == kTopK - 1) recent_page = bt_row[r];
 
-  // 1. 16 keys (and pages) per lane of the active waves, each lane's best score
-  uint64_t keys[kSelKeysPerLane];
-  int32_t pages[kSelKeysPerLane];
+  // 1. E keys (and pages) per lane of the active waves, each lane's best score
+  uint64_t keys[E];
+  int32_t pages[E];
   uint32_t best = 0;
   if (wave < active) {  // loaded: 1,024 w < n < cap
 #pragma unroll
-    for (int e = 0; e < kSelKeysPerLane; ++e) {
+    for (int e = 0; e < E; ++e) {
       const int j = j0 + e * kWave;
       pages[e] = ld.pages[e];
       keys[e] = j < n ? block_key(ld.sv[e], j) : 0;
@@ -284,19 +268,19 @@ __device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt
   //    the wave's exact 15th-best lane key
   if (wave < active) {
     uint64_t thr = (uint64_t)t0 << 32;
-    uint64_t ballot[kSelKeysPerLane];
+    uint64_t ballot[E];
     int total = sel_ballots(keys, thr, ballot);
-    if (total > kSelWaveCap) {  // wave-uniform
+    if (total > (kTopK - 1) * E) {  // wave-uniform
       uint64_t best64 = 0;
 #pragma unroll
-      for (int e = 0; e < kSelKeysPerLane; ++e) best64 = keys[e] > best64 ? keys[e] : best64;
+      for (int e = 0; e < E; ++e) best64 = keys[e] > best64 ? keys[e] : best64;
       const uint64_t sorted = wave_sort_desc(best64, lane);
       const uint64_t tw = ((uint64_t)__shfl((uint32_t)(sorted >> 32), kTopK - 2) << 32) |
                           (uint32_t)__shfl((uint32_t)sorted, kTopK - 2);
       thr = tw > thr ? tw : thr;
       total = sel_ballots(keys, thr, ballot);
     }
-    sel_append<kSelKeysPerLane, PAGES>(keys, pages, thr, ballot, total, lane, sm.cand, sm.cand_page, &sm.count);
+    sel_append<E, PAGES>(keys, pages, thr, ballot, total, lane, sm.cand, sm.cand_page, &sm.count);
   }
   __syncthreads();
 
@@ -354,6 +338,41 @@ __device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt
     }
   }
   __syncthreads();
+}
+
+// Selection for one (row, group) by a workgroup of NT threads; r must be below
+// sel_max_blocks<NT>() so that every candidate fits the active waves'
+// registers (1,024 per wave).
+// ld: the wave's select_load of the row/group's scores, with a cap above r;
+// bt_row: its block table row (read only when PAGES); r: the recent block
+// (0 <= r < row length).  Writes 16 ids (ascending, -1 padded) to out[] and,
+// when PAGES, their page ids to out_page[] (0 for padding), then synchronises
+// the workgroup so LDS outputs are readable by every thread.  Every thread of
+// the workgroup must call it.
+template <int NT, bool PAGES>
+__device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r, SelectSmem<NT>& sm,
+                              int32_t* out, int32_t* out_page) {
+  constexpr int kWaves = NT / kWave;
+  static_assert(NT % kWave == 0 && kWaves >= 1, "whole waves");
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  if (r + 1 <= kTopK) {  // every visible block is kept
+    if (tid < kTopK) {
+      out[tid] = tid <= r ? tid : -1;
+      if constexpr (PAGES) out_page[tid] = tid <= r ? bt_row[tid] : 0;
+    }
+    __syncthreads();
+    return;
+  }
+  // candidates: blocks 0 .. r-1 (n = r >= 16); the keys per lane in use
+  // follow the row length (a workgroup-uniform choice)
+  if (r <= kWave)
+    select_core<NT, PAGES, 1>(ld, bt_row, r, sm, out, out_page);
+  else if (r <= 4 * kWave)
+    select_core<NT, PAGES, 4>(ld, bt_row, r, sm, out, out_page);
+  else
+    select_core<NT, PAGES, kSelKeysPerLane>(ld, bt_row, r, sm, out, out_page);
 }
 
 }  // namespace msa
