@@ -235,15 +235,17 @@ extern "C" {
 
 size_t msa_attn_workspace_size(const msa_shape* shape) {
   if (check_shape(shape) != MSA_OK) return 0;
-  // the kept-block split's partials (few (row, group) pairs); otherwise the
-  // attention merges its split work on chip
-  return align256(msa::split_partials_bytes(rows_of(shape) * (long long)MSA_NUM_KV_HEADS));
+  // the kept-block split's partials (bf16 K/V, few (row, group) pairs);
+  // otherwise the attention merges its split work on chip
+  return align256(msa::split_partials_bytes(rows_of(shape) * (long long)MSA_NUM_KV_HEADS,
+                                            shape->kv_dtype == MSA_KV_NVFP4));
 }
 
 size_t msa_workspace_size(const msa_shape* shape) {
   if (check_shape(shape) != MSA_OK) return 0;
   return align256(scores_bytes(shape)) + align256(sel_bytes(shape)) +
-         align256(msa::split_partials_bytes(rows_of(shape) * (long long)MSA_NUM_KV_HEADS));
+         align256(msa::split_partials_bytes(rows_of(shape) * (long long)MSA_NUM_KV_HEADS,
+                                            shape->kv_dtype == MSA_KV_NVFP4));
 }
 
 static msa_status indexer_impl(const msa_shape* shape, const msa_cache* cache, const msa_prefix_share* share,
@@ -343,7 +345,7 @@ static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, co
   const long long pairs = (long long)rows_of(shape) * shape->num_kv_heads;
   if (pairs <= 2LL * msa::device_cus()) {
     msa::AttnArgs a = attn_args(shape, cache, q, scores, nullptr, sel_blocks, out);
-    if (msa::split_partials_bytes(pairs) > 0)  // few pairs: room for the kept-block split
+    if (msa::split_partials_bytes(pairs, a.kv_nvfp4) > 0)  // few pairs, bf16 K/V: the kept-block split
       a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)) +
                                             align256(sel_bytes(shape)));
     return hip_status(msa::launch_sparse_attn(a, stream), "selection + sparse attention");

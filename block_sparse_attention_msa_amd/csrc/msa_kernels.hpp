@@ -72,15 +72,16 @@ struct AttnArgs {
   float qk_scale_log2;         // sm_scale * k_scale * log2(e)
   float v_scale;
   bool kv_nvfp4;
-  // fused path with at most kSplitMaxPairs (row, group) pairs: room for the
+  // bf16 K/V with at most kSplitMaxPairs (row, group) pairs: room for the
   // kept-block split's partials (split_partials_bytes), or nullptr
   float* partials = nullptr;
 };
-// Few (row, group) pairs: the kept blocks are split over workgroups and the
-// partials merged by a second launch.
+// Few (row, group) pairs with bf16 K/V: the kept blocks are split over
+// workgroups and the partials merged by a second launch (NVFP4 K/V merge on
+// chip: no partials).
 constexpr int kSplitMaxPairs = 64;
-inline size_t split_partials_bytes(long long pairs) {
-  return pairs <= kSplitMaxPairs ? (size_t)pairs * kTopK * kHeadsPerGroup * (kDim * 4 + 8) : 0;
+inline size_t split_partials_bytes(long long pairs, bool kv_nvfp4) {
+  return !kv_nvfp4 && pairs <= kSplitMaxPairs ? (size_t)pairs * kTopK * kHeadsPerGroup * (kDim * 4 + 8) : 0;
 }
 // Selection (fused path) + attention: one launch.
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);

@@ -115,13 +115,14 @@ typedef struct {
 /* Bytes of device workspace msa_decode needs for this shape: the fp32 block
  * scores [rows][num_kv_heads][max_blocks_per_seq], then the int32 selected
  * ids [rows][num_kv_heads][16] (used when sel_blocks is NULL and the
- * selection runs as a launch of its own), then, for at most 64 (row, group)
- * pairs (rows x num_kv_heads), the partial outputs of the kept-block split
- * (2,080 B per (pair, kept block)), each 256-B aligned.  Its contents
- * need no initialisation.  Returns 0 for an invalid shape (see
+ * selection runs as a launch of its own), then, with bf16 K/V and at most 64
+ * (row, group) pairs (rows x num_kv_heads), the partial outputs of the
+ * kept-block split (2,080 B per (pair, kept block)), each 256-B aligned.  Its
+ * contents need no initialisation.  Returns 0 for an invalid shape (see
  * msa_last_error()).  msa_attn_workspace_size(): the stand-alone attention's
- * workspace, the same partials for at most 64 pairs (it then splits the kept
- * blocks as msa_decode does), 0 otherwise (it merges its split work on chip). */
+ * workspace, the same partials for bf16 K/V and at most 64 pairs (it then
+ * splits the kept blocks as msa_decode does), 0 otherwise (it merges its split
+ * work on chip). */
 size_t msa_workspace_size(const msa_shape* shape);
 size_t msa_attn_workspace_size(const msa_shape* shape);
 
@@ -156,7 +157,8 @@ msa_status msa_block_topk(const msa_shape* shape, const int32_t* seq_lens, const
  *   sel_blocks int32 [rows][num_kv_heads][16] logical ids (-1 = none)
  *   out        fp32 [rows][num_q_heads][128], 16-B aligned
  *   workspace  >= msa_attn_workspace_size(shape) bytes, 256-B aligned; may be
- *              NULL when that is 0 (more than 64 (row, group) pairs)
+ *              NULL when that is 0 (NVFP4 K/V, or more than 64 (row, group)
+ *              pairs)
  * Keys: tokens t <= pos of the listed blocks; logits sm_scale * q.k.  Ids
  * outside [0, pos/128] contribute nothing; a row left with no keys outputs 0. */
 msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache, const void* q,
@@ -168,10 +170,11 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
  * attention (two launches), or, when there are more (row, group) pairs than
  * two per compute unit (the attention workgroups would run in several
  * rounds), the selection as a launch of its own before the attention (three
- * launches).  With at most 64 (row, group) pairs the kept blocks of each pair
- * are instead split over 2-16 workgroups ("Decode sparse GQA" of the MiniMax
- * M3 x vLLM post: split work, partial outputs merged), each repeating the
- * selection, and a third launch merges their partials by log-sum-exp.
+ * launches).  With bf16 K/V and at most 64 (row, group) pairs the kept blocks
+ * of each pair are instead split over 2-16 workgroups ("Decode sparse GQA" of
+ * the MiniMax M3 x vLLM post: split work, partial outputs merged), each
+ * repeating the selection, and a third launch merges their partials by
+ * log-sum-exp.
  * Results are the same in every form up to fp32 summation order (the ids are
  * identical).
  *   out        fp32 [rows][num_q_heads][128], 16-B aligned.

@@ -220,17 +220,21 @@ def test_other_entry_points_validate():
 
 
 def test_kept_block_split_workspace():
-    """At most 64 (row, group) pairs: msa_decode's workspace adds the split's
-    partials (2,080 B per (pair, kept block)) after the scores and ids, and the
-    stand-alone attention then needs the same partials as its workspace."""
+    """bf16 K/V and at most 64 (row, group) pairs: msa_decode's workspace adds
+    the split's partials (2,080 B per (pair, kept block)) after the scores and
+    ids, and the stand-alone attention then needs the same partials as its
+    workspace.  NVFP4 K/V merge on chip: no partials."""
     L = msa.lib()
-    s = _shape(num_seqs=2, max_blocks_per_seq=8)  # 8 pairs
+    nv = _shape(num_seqs=2, max_blocks_per_seq=8)  # NVFP4 K/V, 8 pairs
+    assert L.msa_attn_workspace_size(ctypes.byref(nv)) == 0
+    assert L.msa_workspace_size(ctypes.byref(nv)) == 256 + 512
+    s = _shape(num_seqs=2, max_blocks_per_seq=8, kv_dtype=msa.MSA_KV_BF16)  # 8 pairs
     parts = 8 * 16 * 2080
     assert L.msa_attn_workspace_size(ctypes.byref(s)) == parts
     assert L.msa_workspace_size(ctypes.byref(s)) == 256 + 512 + parts
-    s16 = _shape(num_seqs=16, max_blocks_per_seq=8)  # 64 pairs: the largest split batch
+    s16 = _shape(num_seqs=16, max_blocks_per_seq=8, kv_dtype=msa.MSA_KV_BF16)  # 64 pairs: the largest split batch
     assert L.msa_attn_workspace_size(ctypes.byref(s16)) == 64 * 16 * 2080
-    s17 = _shape(num_seqs=17, max_blocks_per_seq=8)
+    s17 = _shape(num_seqs=17, max_blocks_per_seq=8, kv_dtype=msa.MSA_KV_BF16)
     assert L.msa_attn_workspace_size(ctypes.byref(s17)) == 0
 
     def attn(ws, nbytes, out=FAKE):

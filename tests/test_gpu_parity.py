@@ -227,11 +227,12 @@ def test_max_context_fused(dev, idx):
 @pytest.mark.parametrize("kv", ["nvfp4", "bf16"])
 @pytest.mark.parametrize("mbps", [40, 1024, 1025, 3000, 4096, 6000, 9000])
 def test_kept_block_split(dev, kv, mbps):
-    """At most 64 (row, group) pairs the kept blocks are split over 16, 8, 4
-    or 2 workgroups (by the selection's waves for the row length: 1,024
-    blocks each), and a second launch merges the partials; a table row past
-    8,192 blocks keeps the on-chip merge.  Ragged rows, one of them padded and
-    one shorter than 16 blocks (parts without keys); fused and stand-alone
+    """At most 64 (row, group) pairs with bf16 K/V the kept blocks are split
+    over 16, 8, 4 or 2 workgroups (by the selection's waves for the row
+    length: 1,024 blocks each), and a second launch merges the partials; a
+    table row past 8,192 blocks, and NVFP4 K/V, keep the on-chip merge (output
+    dims split over 4 workgroups).  Ragged rows, one of them padded and one
+    shorter than 16 blocks (parts without keys); fused and stand-alone
     attention identical, every row against the oracle."""
     top = mbps * 128
     lens = [top - 77, 0, 5 * 128 + 3, min(top, 20000)]
