@@ -38,6 +38,51 @@ __global__ __launch_bounds__(kScanWaves * kWave, 5) void scan_decode_kernel(cons
                         block_scores + (size_t)b * kGroups * mbps, mbps, jbeg, jend, idx_scale, lane);
 }
 
+// bf16 index keys, few pages: each page's 32 wave-loads split over S waves of
+// a workgroup (kScanWaves / S pages per workgroup), whose per-wave block
+// maxima are combined through LDS.  A batch of a few short rows otherwise
+// runs one wave per page, a long serial chain on an almost empty GPU.  The
+// scores are the one-wave scan's (the same products and sums per token; the
+// maximum does not depend on the order).
+template <int S>
+__global__ __launch_bounds__(kScanWaves * kWave) void scan_decode_split_kernel(
+    const uint8_t* __restrict__ idx_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int mbps,
+    float idx_scale) {
+  using Geo = ScanGeom<false>;
+  static_assert(kScanWaves % S == 0 && Geo::kLoadsPerBlock % S == 0, "whole pages per workgroup");
+  constexpr int kN = Geo::kLoadsPerBlock / S;  // wave-loads per wave
+  __shared__ float part_max[kScanWaves][kGroups];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int j = blockIdx.x * (kScanWaves / S) + wave / S;
+  const int part = wave % S;
+  const bool in = j < mbps;  // wave-uniform; every wave reaches the barrier
+  const int32_t* bt_row = block_table + (size_t)b * mbps;
+  const int32_t pg = in ? bt_row[j] : 0;  // read before the visibility test, never followed unless visible
+  const int L = seq_lens[b];
+  const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
+  const bool vis = in && j < nbv;
+  float m = -INFINITY;
+  if (vis) {
+    uint32_t qr[4][Geo::kPairsPerLane];
+    scan_query_slice<false>(iq + (size_t)b * kGroups * kDim, lane, qr);
+    const uint8_t* base = idx_pool + (int64_t)pg * Geo::kPageBytes + lane * 16;
+    m = scan_loads<false, kN>(base, qr, L - j * kBlock, part * kN, lane, m);
+    m = wave_max_xor(m, Geo::kLanesPerToken);
+  }
+  if (lane < kGroups) part_max[wave][lane_group(lane)] = m;
+  __syncthreads();
+  if (part == 0 && in && lane < kGroups) {
+    const int g = lane_group(lane);
+    float x = part_max[wave][g];
+#pragma unroll
+    for (int p = 1; p < S; ++p) x = fmaxf(x, part_max[wave + p][g]);
+    block_scores[((size_t)b * kGroups + g) * mbps + j] = vis ? x * idx_scale : -INFINITY;
+  }
+}
+
 // NVFP4 index keys: one page per wave; 1 KB of LDS per wave for the scales.
 // 4-wave workgroups at 6 waves per SIMD (at most 85 VGPRs), from a sweep on
 // the batch-32 x 128K shape: 48.0-48.4 us, against 49.4-54.2 us for 8 waves
@@ -301,9 +346,16 @@ hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
     scan_decode_nvfp4_kernel<<<g2, dim3(kNvfp4ScanWaves * kWave), 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
                                                        a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
                                                        a.idx_scale);
-  } else
+  } else if ((long long)a.num_seqs * a.mbps <= 2LL * device_cus()) {
+    // few pages: 8 waves per page (4 wave-loads, 16 tokens each)
+    constexpr int S = kScanWaves;
+    dim3 g2((a.mbps + kScanWaves / S - 1) / (kScanWaves / S), a.num_seqs);
+    scan_decode_split_kernel<S><<<g2, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
+                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, a.idx_scale);
+  } else {
     scan_decode_kernel<false><<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
                                                            a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale);
+  }
   return hipGetLastError();
 }
 

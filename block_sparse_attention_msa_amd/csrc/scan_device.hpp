@@ -32,6 +32,64 @@ struct ScanGeom {
   static constexpr size_t kPageBytes = (size_t)kBlock * kDim * (FP8 ? 1 : 2);
 };
 
+// Wave-loads [i0, i0 + N) of one page (base: the page plus 16 B per lane): the
+// running per-lane maximum m of the scores of their visible tokens (tokens
+// before `visible`), each lane for group lane_group(lane) after the permuted
+// reduction; the caller reduces over the token slots (wave_max_xor).
+template <bool FP8, int N>
+__device__ __forceinline__ float scan_loads(const uint8_t* __restrict__ base,
+                                            const uint32_t (&qr)[4][ScanGeom<FP8>::kPairsPerLane], int visible,
+                                            int i0, int lane, float m) {
+  using Geo = ScanGeom<FP8>;
+  const int slot = lane / Geo::kLanesPerToken;
+  u32x4 buf[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    buf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)(i0 + i) * 1024));
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x2 lo = e4m3x2_to_bf16x2<false>(w[d]);
+        const bf16x2 hi = e4m3x2_to_bf16x2<true>(w[d]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[k] = dot2(lo, as_bf16x2(qr[k][2 * d]), a[k]);
+          a[k] = dot2(hi, as_bf16x2(qr[k][2 * d + 1]), a[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = dot2(as_bf16x2(w[d]), as_bf16x2(qr[k][d]), a[k]);
+    }
+    const float s = reduce4_permuted<Geo::kLog2Lpt>(a[0], a[1], a[2], a[3]);
+    const int tok = slot + (i0 + i) * Geo::kTokensPerLoad;
+    m = fmaxf(m, tok < visible ? s : -INFINITY);
+  }
+  return m;
+}
+
+// This lane's slice of the four index queries of one row, group order
+// permuted by lane (lane = (token slot, 16-byte dim chunk)).
+template <bool FP8>
+__device__ __forceinline__ void scan_query_slice(const uint16_t* __restrict__ iq_row, int lane,
+                                                 uint32_t (&qr)[4][ScanGeom<FP8>::kPairsPerLane]) {
+  using Geo = ScanGeom<FP8>;
+  const int chunk = lane & (Geo::kLanesPerToken - 1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(iq_row + permuted_group(lane, k) * kDim + chunk * (2 * Geo::kPairsPerLane));
+#pragma unroll
+    for (int p = 0; p < Geo::kPairsPerLane; ++p) qr[k][p] = src[p];
+  }
+}
+
 // Block scores of blocks [jbeg, jend) of one sequence (one query row):
 //   bs_row[g * mbps + j] = idx_scale * max over visible tokens of block j of
 //   sum_d iq_row[g][d] * ik[t][d]   (-inf for blocks past the last token).
@@ -48,17 +106,8 @@ __device__ __forceinline__ void scan_wave(const uint8_t* __restrict__ idx_pool, 
   const int nbv = L > 0 ? ((L - 1) / kBlock) + 1 : 0;
   const int my_group = lane_group(lane);
 
-  // This lane's slice of the four index queries, group order permuted by lane.
-  const int chunk = lane & (Geo::kLanesPerToken - 1);
-  const int slot = lane / Geo::kLanesPerToken;
   uint32_t qr[4][Geo::kPairsPerLane];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t* src =
-        reinterpret_cast<const uint32_t*>(iq_row + permuted_group(lane, k) * kDim + chunk * (2 * Geo::kPairsPerLane));
-#pragma unroll
-    for (int p = 0; p < Geo::kPairsPerLane; ++p) qr[k][p] = src[p];
-  }
+  scan_query_slice<FP8>(iq_row, lane, qr);
 
   for (int j = jbeg; j < jend; ++j) {
     const int32_t pg_j = pg;
@@ -72,37 +121,7 @@ __device__ __forceinline__ void scan_wave(const uint8_t* __restrict__ idx_pool, 
     const int visible = L - j * kBlock;  // tokens of this block at or before the query
     float m = -INFINITY;
 #pragma unroll
-    for (int i0 = 0; i0 < Geo::kLoadsPerBlock; i0 += CHUNK) {
-      u32x4 buf[CHUNK];
-#pragma unroll
-      for (int i = 0; i < CHUNK; ++i)
-        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)(i0 + i) * 1024));
-#pragma unroll
-      for (int i = 0; i < CHUNK; ++i) {
-        const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
-        float a[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const bf16x2 lo = e4m3x2_to_bf16x2<false>(w[d]);
-            const bf16x2 hi = e4m3x2_to_bf16x2<true>(w[d]);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              a[k] = dot2(lo, as_bf16x2(qr[k][2 * d]), a[k]);
-              a[k] = dot2(hi, as_bf16x2(qr[k][2 * d + 1]), a[k]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) a[k] = dot2(as_bf16x2(w[d]), as_bf16x2(qr[k][d]), a[k]);
-        }
-        const float s = reduce4_permuted<Geo::kLog2Lpt>(a[0], a[1], a[2], a[3]);
-        const int tok = slot + (i0 + i) * Geo::kTokensPerLoad;
-        m = fmaxf(m, tok < visible ? s : -INFINITY);
-      }
-    }
+    for (int i0 = 0; i0 < Geo::kLoadsPerBlock; i0 += CHUNK) m = scan_loads<FP8, CHUNK>(base, qr, visible, i0, lane, m);
     m = wave_max_xor(m, Geo::kLanesPerToken);
     if (lane < 4) bs_row[my_group * mbps + j] = m * idx_scale;
   }
