@@ -137,6 +137,26 @@ struct PvType<false> {  // bf16 V
   }
 };
 
+// Stores of a split part's partial: device-coherent when another workgroup
+// of the same launch merges them (agent-scope relaxed atomic stores, which
+// write through to the device's coherence point), plain otherwise.
+template <bool COHERENT>
+__device__ __forceinline__ void store_f32x2(float* p, float a, float b) {
+  if constexpr (COHERENT) {
+    const uint64_t u = (uint64_t)__builtin_bit_cast(uint32_t, a) | ((uint64_t)__builtin_bit_cast(uint32_t, b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+  }
+}
+template <bool COHERENT>
+__device__ __forceinline__ void store_f32(float* p, float a) {
+  if constexpr (COHERENT)
+    __hip_atomic_store(p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = a;
+}
+
 // Selection (SELECT: from the block scores) and attention of (row, g) for
 // output dims [part * 128 / DSPLIT, (part + 1) * 128 / DSPLIT).  The DSPLIT
 // workgroups of one (row, g) repeat the selection and the softmax (identical,
@@ -146,10 +166,12 @@ struct PvType<false> {  // bf16 V
 // the output, its partial per head: po[pair][p][h][128] = sum over its keys of
 // 2^(z - M) v (K/V tensor scales aside) and pml[pair][p][h] = (M, sum 2^(z - M)),
 // M its largest logit (-inf, with zeros, for a part without keys); a merge
-// launch combines the parts.  Padded rows write nothing but -1 ids.
+// launch, or the last part to finish, combines the parts (COHERENT: the
+// partials are stored device-coherent for the latter).  Padded rows write
+// nothing but -1 ids.
 // With SELECT, mbps must not exceed sel_max_blocks<NT>().  Every thread of the
 // workgroup must call it.
-template <bool FP4, bool SELECT, int DSPLIT, int NT, int SPLIT = 1>
+template <bool FP4, bool SELECT, int DSPLIT, int NT, int SPLIT = 1, bool COHERENT = false>
 __device__ __forceinline__ void attn_workgroup(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -458,13 +480,14 @@ __device__ __forceinline__ void attn_workgroup(
     if (c == 0) {
 #pragma unroll
       for (int i = 0; i < kHeadsPerGroup; ++i) {
-        float4* d4 = reinterpret_cast<float4*>(dst + i * kDim + d0);
-        d4[0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-        d4[1] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+        float* d = dst + i * kDim + d0;
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) store_f32x2<COHERENT>(d + t, acc[t][i], acc[t + 1][i]);
       }
     }
     if (c == 0 && jj == 0)
-      pml[((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + hq] = make_float2(m_w, l_w);
+      store_f32x2<COHERENT>(reinterpret_cast<float*>(pml + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + hq),
+                            m_w, l_w);
     return;
   }
   __syncthreads();  // selection LDS is dead: the merge area reuses it
@@ -501,7 +524,9 @@ __device__ __forceinline__ void attn_workgroup(
     fl += __shfl_xor(fl, 32);
     if (w < kWaves) sm.u.merge.f[w][h] = f;
     if (w == 0) sm.u.merge.inv[h] = SPLIT > 1 ? 1.f : (fl > 0.f ? v_scale / fl : 0.f);
-    if (SPLIT > 1 && w == 0) pml[((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + h] = make_float2(M, fl);
+    if (SPLIT > 1 && w == 0)
+      store_f32x2<COHERENT>(reinterpret_cast<float*>(pml + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + h),
+                            M, fl);
   }
   __syncthreads();
   float* dst = SPLIT > 1 ? po + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup * kDim : out_row;
@@ -511,7 +536,7 @@ __device__ __forceinline__ void attn_workgroup(
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) o = fmaf(sm.u.merge.f[w][h], sm.u.merge.o[w][h][d], o);
-    dst[h * kDim + d] = o * sm.u.merge.inv[h];
+    store_f32<COHERENT>(dst + h * kDim + d, o * sm.u.merge.inv[h]);
   }
 }
 

@@ -27,7 +27,8 @@ __global__ __launch_bounds__(kScanWaves * kWave, 5) void scan_decode_kernel(cons
                                                                           const int32_t* __restrict__ seq_lens,
                                                                           const uint16_t* __restrict__ iq,
                                                                           float* __restrict__ block_scores, int mbps,
-                                                                          int blocks_per_wave, float idx_scale) {
+                                                                          int blocks_per_wave, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+  zero_step_counters(zero, zero_n);
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -48,7 +49,8 @@ template <int S>
 __global__ __launch_bounds__(kScanWaves * kWave) void scan_decode_split_kernel(
     const uint8_t* __restrict__ idx_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int mbps,
-    float idx_scale) {
+    float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+  zero_step_counters(zero, zero_n);
   using Geo = ScanGeom<false>;
   static_assert(kScanWaves % S == 0 && Geo::kLoadsPerBlock % S == 0, "whole pages per workgroup");
   constexpr int kN = Geo::kLoadsPerBlock / S;  // wave-loads per wave
@@ -92,7 +94,8 @@ constexpr int kNvfp4ScanWaves = 4;
 __global__ __launch_bounds__(kNvfp4ScanWaves * kWave, 6) void scan_decode_nvfp4_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int mbps,
-    float idx_scale) {
+    float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+  zero_step_counters(zero, zero_n);
   __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kNvfp4ScanWaves][kBlock * 8];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -113,7 +116,8 @@ __global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_kernel(const
                                                                          const int32_t* __restrict__ seq_lens,
                                                                          const uint16_t* __restrict__ iq,
                                                                          float* __restrict__ block_scores, int q_len,
-                                                                         int mbps, int pages_per_wave, float idx_scale) {
+                                                                         int mbps, int pages_per_wave, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+  zero_step_counters(zero, zero_n);
   __shared__ __attribute__((aligned(16))) uint8_t lds_t[kColsScanWaves][2 * 2048];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -156,7 +160,8 @@ __global__ __launch_bounds__(kColsScanWaves * kWave, MINW) void scan_shared_kern
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores,
     const int32_t* __restrict__ members, const int32_t* __restrict__ shared_blocks,
     const int32_t* __restrict__ seq_shared_blocks, int num_groups, int max_members, int q_len_arg, int mbps,
-    int min_shared, float idx_scale) {
+    int min_shared, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+  zero_step_counters(zero, zero_n);
   const int q_len = Q1 ? 1 : q_len_arg;
   // one flat grid: num_groups x xs workgroups of the shared pass, then
   // num_seqs x xo of the own blocks (which start at block min_shared)
@@ -229,7 +234,8 @@ template <int NT>
 __global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_nvfp4_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ iq, float* __restrict__ block_scores, int q_len,
-    int mbps, int pages_per_wave, float idx_scale) {
+    int mbps, int pages_per_wave, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+  zero_step_counters(zero, zero_n);
   __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kColsScanWaves][kBlock * 8];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -259,18 +265,18 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
   if (a.idx_fmt == kIdxNvfp4) {
     if (q_len <= 4)
       scan_cols_nvfp4_kernel<1><<<grid, block, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
-                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale);
+                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale, a.zero, a.zero_n);
     else
       scan_cols_nvfp4_kernel<2><<<grid, block, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
-                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale);
+                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale, a.zero, a.zero_n);
     return hipGetLastError();
   }
   if (q_len <= 4)
     scan_cols_kernel<1><<<grid, block, 0, stream>>>(pool, a.block_table, a.seq_lens, a.iq, a.block_scores, q_len,
-                                                     a.mbps, ppw, a.idx_scale);
+                                                     a.mbps, ppw, a.idx_scale, a.zero, a.zero_n);
   else
     scan_cols_kernel<2><<<grid, block, 0, stream>>>(pool, a.block_table, a.seq_lens, a.iq, a.block_scores, q_len,
-                                                     a.mbps, ppw, a.idx_scale);
+                                                     a.mbps, ppw, a.idx_scale, a.zero, a.zero_n);
   return hipGetLastError();
 }
 
@@ -289,7 +295,7 @@ hipError_t launch_scan_shared(const ScanArgs& a, const int32_t* members, const i
   const uint8_t* pool = static_cast<const uint8_t*>(a.idx_pool);
 #define MSA_SHARED_ARGS                                                                                      \
   pool, a.idx_sf, a.block_table, a.seq_lens, a.iq, a.block_scores, members, shared_blocks, seq_shared_blocks, \
-      num_groups, max_members, q_len, a.mbps, min_shared, a.idx_scale
+      num_groups, max_members, q_len, a.mbps, min_shared, a.idx_scale, a.zero, a.zero_n
   // at most 32 (member, query, group) columns: one wave per shared page
   const bool wide = max_members * q_len * kGroups > 32;
   if (a.idx_fmt == kIdxNvfp4) {
@@ -345,16 +351,16 @@ hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
     dim3 g2((a.mbps + kNvfp4ScanWaves - 1) / kNvfp4ScanWaves, a.num_seqs);
     scan_decode_nvfp4_kernel<<<g2, dim3(kNvfp4ScanWaves * kWave), 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
                                                        a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
-                                                       a.idx_scale);
+                                                       a.idx_scale, a.zero, a.zero_n);
   } else if ((long long)a.num_seqs * a.mbps <= 2LL * device_cus()) {
     // few pages: 8 waves per page (4 wave-loads, 16 tokens each)
     constexpr int S = kScanWaves;
     dim3 g2((a.mbps + kScanWaves / S - 1) / (kScanWaves / S), a.num_seqs);
     scan_decode_split_kernel<S><<<g2, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, a.idx_scale);
+                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, a.idx_scale, a.zero, a.zero_n);
   } else {
     scan_decode_kernel<false><<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale);
+                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale, a.zero, a.zero_n);
   }
   return hipGetLastError();
 }

@@ -340,16 +340,22 @@ static msa_status decode_impl(const msa_shape* shape, const msa_cache* cache, co
   // its own between them (3 launches), so that the per-workgroup selection
   // latency is not paid once per round.
   float* scores = static_cast<float*>(workspace);
-  hipError_t e = launch_scan_any(shape, scan_args(shape, cache, idx_q, scores), share, stream);
-  if (e != hipSuccess) return hip_status(e, "index scan");
   const long long pairs = (long long)rows_of(shape) * shape->num_kv_heads;
-  if (pairs <= 2LL * msa::device_cus()) {
-    msa::AttnArgs a = attn_args(shape, cache, q, scores, nullptr, sel_blocks, out);
-    if (msa::split_partials_bytes(pairs, a.kv_nvfp4) > 0)  // few pairs, bf16 K/V: the kept-block split
-      a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)) +
-                                            align256(sel_bytes(shape)));
-    return hip_status(msa::launch_sparse_attn(a, stream), "selection + sparse attention");
+  const bool fused = pairs <= 2LL * msa::device_cus();
+  msa::ScanArgs sa = scan_args(shape, cache, idx_q, scores);
+  msa::AttnArgs a = attn_args(shape, cache, q, scores, nullptr, sel_blocks, out);
+  if (fused && msa::split_partials_bytes(pairs, a.kv_nvfp4) > 0) {
+    // few pairs, bf16 K/V: the kept-block split, its partials merged by the
+    // last part of each pair; the scan zeroes the arrival counters
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)) +
+                                          align256(sel_bytes(shape)));
+    a.counters = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.partials) + msa::split_counters_offset(pairs));
+    sa.zero = a.counters;
+    sa.zero_n = (int)pairs;
   }
+  hipError_t e = launch_scan_any(shape, sa, share, stream);
+  if (e != hipSuccess) return hip_status(e, "index scan");
+  if (fused) return hip_status(msa::launch_sparse_attn(a, stream), "selection + sparse attention");
   int32_t* sel = sel_blocks ? sel_blocks
                             : reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(scores_bytes(shape)));
   msa::TopkArgs ta{cache->seq_lens, scores, sel, (int)rows_of(shape), shape->q_len, shape->max_blocks_per_seq};

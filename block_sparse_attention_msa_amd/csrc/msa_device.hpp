@@ -82,6 +82,13 @@ __device__ __forceinline__ float reduce4_permuted(float a0, float a1, float a2, 
 // no range reduction needed; results below 2^-126 flush to 0.
 __device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The scan that opens a decode step zeroes the arrival counters of the
+// attention launch that follows it (n <= 64, by the launch's first
+// workgroup; the kernel boundary orders these stores before the attention).
+__device__ __forceinline__ void zero_step_counters(int32_t* p, int n) {
+  if (p && blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
 __device__ __forceinline__ float wave_max_xor(float m, int from) {
   for (int off = from; off < kWave; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
   return m;

@@ -27,6 +27,10 @@ struct ScanArgs {
   int mbps;
   float idx_scale;
   int idx_fmt;                 // IdxFormat
+  // counters of the attention launch that follows in the same decode step,
+  // zeroed by the scan's first workgroup (at most 64), or nullptr
+  int32_t* zero = nullptr;
+  int zero_n = 0;
 };
 // Decode (one query row per sequence) index scan + block max-pool.
 hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream);
@@ -75,13 +79,22 @@ struct AttnArgs {
   // bf16 K/V with at most kSplitMaxPairs (row, group) pairs: room for the
   // kept-block split's partials (split_partials_bytes), or nullptr
   float* partials = nullptr;
+  // with partials: one arrival counter per (row, group), zero at launch (the
+  // decode step's scan zeroes them); the last part to arrive merges the
+  // partials.  nullptr: a second launch merges them.
+  int32_t* counters = nullptr;
 };
 // Few (row, group) pairs with bf16 K/V: the kept blocks are split over
-// workgroups and the partials merged by a second launch (NVFP4 K/V merge on
-// chip: no partials).
+// workgroups whose partials are merged by the last one to finish, or by a
+// second launch (NVFP4 K/V merge on chip: no partials).  The partials buffer:
+// o [pairs][16][4][128] fp32, (M, sum) [pairs][16][4] float2, then the
+// counters [pairs] int32.
 constexpr int kSplitMaxPairs = 64;
+inline size_t split_counters_offset(long long pairs) {
+  return (size_t)pairs * kTopK * kHeadsPerGroup * (kDim * 4 + 8);
+}
 inline size_t split_partials_bytes(long long pairs, bool kv_nvfp4) {
-  return !kv_nvfp4 && pairs <= kSplitMaxPairs ? (size_t)pairs * kTopK * kHeadsPerGroup * (kDim * 4 + 8) : 0;
+  return !kv_nvfp4 && pairs <= kSplitMaxPairs ? split_counters_offset(pairs) + (size_t)pairs * 4 : 0;
 }
 // Selection (fused path) + attention: one launch.
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);

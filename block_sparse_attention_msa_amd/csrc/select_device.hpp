@@ -355,8 +355,6 @@ __device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt
   constexpr int kWaves = NT / kWave;
   static_assert(NT % kWave == 0 && kWaves >= 1, "whole waves");
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   if (r + 1 <= kTopK) {  // every visible block is kept
     if (tid < kTopK) {
       out[tid] = tid <= r ? tid : -1;

@@ -37,52 +37,42 @@ __global__ __launch_bounds__(NT, 4) void attn_kernel(
                                       pair % kGroups, part, sm);
 }
 
-// Kept blocks split over SPLIT workgroups of NT = 1024 / SPLIT threads, one
-// block per wave; each workgroup writes its partial (o, M, sum) per head.
-template <bool FP4, bool SELECT, int SPLIT>
-__global__ __launch_bounds__(1024 / SPLIT) void attn_split_kernel(
-    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
-    const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
-    int32_t* __restrict__ sel_out, float* __restrict__ po, float2* __restrict__ pml, int rows, int q_len, int mbps,
-    float qk_scale_log2) {
-  constexpr int NT = 1024 / SPLIT;
-  __shared__ AttnSmem<NT> sm;
-  int pair, part;
-  attn_decode_wg<SPLIT>(blockIdx.x, pair, part);
-  if (pair >= rows * kGroups) return;
-  attn_workgroup<FP4, SELECT, 1, NT, SPLIT>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores, sel_in,
-                                           sel_out, nullptr, q_len, mbps, qk_scale_log2, 1.f, pair / kGroups,
-                                           pair % kGroups, part, sm, po, pml);
+// Loads of a split part's partial (COHERENT: device-coherent, for partials
+// stored by other workgroups of the same launch).
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_f32x2(const float* p) {
+  if constexpr (COHERENT) {
+    const uint64_t u =
+        __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__builtin_bit_cast(float, (uint32_t)u), __builtin_bit_cast(float, (uint32_t)(u >> 32)));
+  } else {
+    return *reinterpret_cast<const float2*>(p);
+  }
 }
 
-// Log-sum-exp merge of the SPLIT partials of each (row, group): one wave per
-// pair.  For the factors lane l takes (part l / 4, head l % 4); for the sums
+// Log-sum-exp merge of the SPLIT partials of (row, group) pair `id` by one
+// wave.  For the factors lane l takes (part l / 4, head l % 4); for the sums
 // head l / 16, dims 8 (l % 16) .. + 7.  Every load is issued up front, none
 // waiting on another: each part of a non-padded row writes its partial (zeros
 // and (-inf, 0) without keys); a padded row's partials are never written,
 // are read anyway (inside the buffer) and discarded: its output is 0.
-template <int SPLIT>
-__global__ __launch_bounds__(256) void attn_split_merge_kernel(const int32_t* __restrict__ seq_lens, int pairs,
-                                                               int q_len, const float* __restrict__ po,
-                                                               const float2* __restrict__ pml, float v_scale,
-                                                               float* __restrict__ out) {
+template <int SPLIT, bool COHERENT>
+__device__ __forceinline__ void split_merge_pair(int id, int lane, const int32_t* __restrict__ seq_lens, int q_len,
+                                                 const float* __restrict__ po, const float2* __restrict__ pml,
+                                                 float v_scale, float* __restrict__ out) {
   static_assert(SPLIT * kHeadsPerGroup <= kWave, "one factor per lane");
-  const int lane = threadIdx.x & (kWave - 1);
-  const int id = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (id >= pairs) return;
   const int row = id / kGroups;
   const int h = lane >> 4, d0 = 8 * (lane & 15);
   const int L = seq_lens[row / q_len];
-  const float2 ml = lane < SPLIT * kHeadsPerGroup ? pml[(size_t)id * SPLIT * kHeadsPerGroup + lane]
-                                                  : make_float2(-INFINITY, 0.f);
-  const float4* src = reinterpret_cast<const float4*>(po + ((size_t)id * SPLIT * kHeadsPerGroup + h) * kDim + d0);
-  float4 v[SPLIT][2];
+  const float2 ml = lane < SPLIT * kHeadsPerGroup
+                        ? load_f32x2<COHERENT>(reinterpret_cast<const float*>(pml + (size_t)id * SPLIT * kHeadsPerGroup + lane))
+                        : make_float2(-INFINITY, 0.f);
+  const float* src = po + ((size_t)id * SPLIT * kHeadsPerGroup + h) * kDim + d0;
+  float2 v[SPLIT][4];
 #pragma unroll
-  for (int p = 0; p < SPLIT; ++p) {
-    v[p][0] = src[p * kHeadsPerGroup * kDim / 4];
-    v[p][1] = src[p * kHeadsPerGroup * kDim / 4 + 1];
-  }
+  for (int p = 0; p < SPLIT; ++p)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[p][k] = load_f32x2<COHERENT>(src + p * kHeadsPerGroup * kDim + 2 * k);
   float M = ml.x;
 #pragma unroll
   for (int off = kHeadsPerGroup; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -94,14 +84,11 @@ __global__ __launch_bounds__(256) void attn_split_merge_kernel(const int32_t* __
 #pragma unroll
   for (int p = 0; p < SPLIT; ++p) {
     const float w = __shfl(f, kHeadsPerGroup * p + h);  // 0 for a part without keys (its partial is 0)
-    acc[0] = fmaf(w, v[p][0].x, acc[0]);
-    acc[1] = fmaf(w, v[p][0].y, acc[1]);
-    acc[2] = fmaf(w, v[p][0].z, acc[2]);
-    acc[3] = fmaf(w, v[p][0].w, acc[3]);
-    acc[4] = fmaf(w, v[p][1].x, acc[4]);
-    acc[5] = fmaf(w, v[p][1].y, acc[5]);
-    acc[6] = fmaf(w, v[p][1].z, acc[6]);
-    acc[7] = fmaf(w, v[p][1].w, acc[7]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] = fmaf(w, v[p][k].x, acc[2 * k]);
+      acc[2 * k + 1] = fmaf(w, v[p][k].y, acc[2 * k + 1]);
+    }
   }
   const float flh = __shfl(fl, h);  // lanes 0 .. 3 hold heads 0 .. 3
   const float sc = L > 0 && flh > 0.f ? v_scale / flh : 0.f;
@@ -110,15 +97,69 @@ __global__ __launch_bounds__(256) void attn_split_merge_kernel(const int32_t* __
   dst[1] = L > 0 ? make_float4(acc[4] * sc, acc[5] * sc, acc[6] * sc, acc[7] * sc) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Kept blocks split over SPLIT workgroups of NT = 1024 / SPLIT threads, one
+// block per wave; each workgroup writes its partial (o, M, sum) per head.
+// MERGE: the parts count their arrival on the pair's counter (zero at
+// launch) once their partial stores are complete, and the last one merges
+// the pair's partials and writes the output; otherwise a second launch
+// merges them.
+template <bool FP4, bool SELECT, int SPLIT, bool MERGE>
+__global__ __launch_bounds__(1024 / SPLIT) void attn_split_kernel(
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
+    const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
+    int32_t* __restrict__ sel_out, float* __restrict__ po, float2* __restrict__ pml, int32_t* __restrict__ counters,
+    float* __restrict__ out, int rows, int q_len, int mbps, float qk_scale_log2, float v_scale) {
+  constexpr int NT = 1024 / SPLIT;
+  __shared__ AttnSmem<NT> sm;
+  __shared__ int last;
+  int pair, part;
+  attn_decode_wg<SPLIT>(blockIdx.x, pair, part);
+  if (pair >= rows * kGroups) return;
+  attn_workgroup<FP4, SELECT, 1, NT, SPLIT, MERGE>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores,
+                                                  sel_in, sel_out, nullptr, q_len, mbps, qk_scale_log2, 1.f,
+                                                  pair / kGroups, pair % kGroups, part, sm, po, pml);
+  if constexpr (MERGE) {
+    // this thread's partial stores complete (write-through, device scope)
+    // before the workgroup's arrival is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == SPLIT - 1;
+    __syncthreads();
+    if (last && threadIdx.x < kWave)
+      split_merge_pair<SPLIT, true>(pair, threadIdx.x, seq_lens, q_len, po, pml, v_scale, out);
+  }
+}
+
+// The merge launch: one wave per (row, group) pair.
+template <int SPLIT>
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(const int32_t* __restrict__ seq_lens, int pairs,
+                                                               int q_len, const float* __restrict__ po,
+                                                               const float2* __restrict__ pml, float v_scale,
+                                                               float* __restrict__ out) {
+  const int id = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (id >= pairs) return;
+  split_merge_pair<SPLIT, false>(id, threadIdx.x & (kWave - 1), seq_lens, q_len, po, pml, v_scale, out);
+}
+
 template <bool FP4, bool SELECT, int SPLIT>
 void launch_split(const AttnArgs& a, hipStream_t stream) {
   const long long pairs = (long long)a.rows * kGroups;
   float* po = a.partials;
   float2* pml = reinterpret_cast<float2*>(a.partials + (size_t)pairs * kTopK * kHeadsPerGroup * kDim);
   const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * SPLIT));
-  attn_split_kernel<FP4, SELECT, SPLIT><<<grid, 1024 / SPLIT, 0, stream>>>(
+  if (a.counters) {  // merged by the last part of each pair: one launch
+    attn_split_kernel<FP4, SELECT, SPLIT, true><<<grid, 1024 / SPLIT, 0, stream>>>(
+        static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table,
+        a.seq_lens, a.q, a.block_scores, a.sel, a.sel_out, po, pml, a.counters, a.out, a.rows, a.q_len, a.mbps,
+        a.qk_scale_log2, a.v_scale);
+    return;
+  }
+  attn_split_kernel<FP4, SELECT, SPLIT, false><<<grid, 1024 / SPLIT, 0, stream>>>(
       static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table, a.seq_lens,
-      a.q, a.block_scores, a.sel, a.sel_out, po, pml, a.rows, a.q_len, a.mbps, a.qk_scale_log2);
+      a.q, a.block_scores, a.sel, a.sel_out, po, pml, nullptr, nullptr, a.rows, a.q_len, a.mbps, a.qk_scale_log2,
+      a.v_scale);
   attn_split_merge_kernel<SPLIT><<<dim3((unsigned)((pairs + 3) / 4)), 256, 0, stream>>>(
       a.seq_lens, (int)pairs, a.q_len, po, pml, a.v_scale, a.out);
 }
@@ -194,11 +235,12 @@ int device_cus() {
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
-  // NVFP4 K/V: the on-chip merge (no second launch) also for few pairs; on
-  // the batch-8 x 32K shape 19.2-19.3 us per step against 20.0 us with the
-  // kept blocks split over 16 workgroups, on the batch-4 x 512K shape
-  // 54.9-55.2 us against 55.6 us.  bf16 K/V (a 64 KB block per wave) keep the
-  // split: one workgroup per pair would read all 16 K blocks through one CU.
+  // NVFP4 K/V: the on-chip merge (no partials) also for few pairs; against the
+  // kept blocks split over 16 one-wave workgroups merged by the last of them
+  // (same box): batch 8 x 32K 19.2 us per step against 20.4 us, batch
+  // 4 x 512K 55.5 against 55.0, batch 32 x 128K (128 pairs) 97.6 against
+  // 107.7.  bf16 K/V (a 64 KB block per wave) keep the split: one workgroup
+  // per pair would read all 16 K blocks through one CU.
   if (a.kv_nvfp4) {
     if (a.block_scores)
       launch2<true, true>(a, stream);

@@ -117,8 +117,9 @@ typedef struct {
  * ids [rows][num_kv_heads][16] (used when sel_blocks is NULL and the
  * selection runs as a launch of its own), then, with bf16 K/V and at most 64
  * (row, group) pairs (rows x num_kv_heads), the partial outputs of the
- * kept-block split (2,080 B per (pair, kept block)), each 256-B aligned.  Its
- * contents need no initialisation.  Returns 0 for an invalid shape (see
+ * kept-block split (2,080 B per (pair, kept block)) and one int32 arrival
+ * counter per pair, each part 256-B aligned.  Its contents need no
+ * initialisation: msa_decode's first launch zeroes the counters.  Returns 0 for an invalid shape (see
  * msa_last_error()).  msa_attn_workspace_size(): the stand-alone attention's
  * workspace, the same partials for bf16 K/V and at most 64 pairs (it then
  * splits the kept blocks as msa_decode does), 0 otherwise (it merges its split
@@ -173,8 +174,9 @@ msa_status msa_sparse_attn_decode(const msa_shape* shape, const msa_cache* cache
  * launches).  With bf16 K/V and at most 64 (row, group) pairs the kept blocks
  * of each pair are instead split over 2-16 workgroups ("Decode sparse GQA" of
  * the MiniMax M3 x vLLM post: split work, partial outputs merged), each
- * repeating the selection, and a third launch merges their partials by
- * log-sum-exp.
+ * repeating the selection; the last workgroup of a pair to finish merges the
+ * pair's partials by log-sum-exp (still two launches; msa_sparse_attn_decode
+ * merges them in a second launch of its own, with the same arithmetic).
  * Results are the same in every form up to fp32 summation order (the ids are
  * identical).
  *   out        fp32 [rows][num_q_heads][128], 16-B aligned.

@@ -221,19 +221,25 @@ def test_other_entry_points_validate():
 
 def test_kept_block_split_workspace():
     """bf16 K/V and at most 64 (row, group) pairs: msa_decode's workspace adds
-    the split's partials (2,080 B per (pair, kept block)) after the scores and
-    ids, and the stand-alone attention then needs the same partials as its
-    workspace.  NVFP4 K/V merge on chip: no partials."""
+    the split's partials (2,080 B per (pair, kept block)) and one int32
+    arrival counter per pair after the scores and ids, 256-B aligned, and the
+    stand-alone attention then needs the same region as its workspace.  NVFP4
+    K/V merge on chip: no partials."""
     L = msa.lib()
+
+    def split_region(pairs):
+        return -(-(pairs * 16 * 2080 + pairs * 4) // 256) * 256
+
     nv = _shape(num_seqs=2, max_blocks_per_seq=8)  # NVFP4 K/V, 8 pairs
     assert L.msa_attn_workspace_size(ctypes.byref(nv)) == 0
     assert L.msa_workspace_size(ctypes.byref(nv)) == 256 + 512
     s = _shape(num_seqs=2, max_blocks_per_seq=8, kv_dtype=msa.MSA_KV_BF16)  # 8 pairs
-    parts = 8 * 16 * 2080
+    parts = split_region(8)
+    assert parts == 266496
     assert L.msa_attn_workspace_size(ctypes.byref(s)) == parts
     assert L.msa_workspace_size(ctypes.byref(s)) == 256 + 512 + parts
     s16 = _shape(num_seqs=16, max_blocks_per_seq=8, kv_dtype=msa.MSA_KV_BF16)  # 64 pairs: the largest split batch
-    assert L.msa_attn_workspace_size(ctypes.byref(s16)) == 64 * 16 * 2080
+    assert L.msa_attn_workspace_size(ctypes.byref(s16)) == split_region(64)
     s17 = _shape(num_seqs=17, max_blocks_per_seq=8, kv_dtype=msa.MSA_KV_BF16)
     assert L.msa_attn_workspace_size(ctypes.byref(s17)) == 0
 

@@ -694,15 +694,20 @@ def test_shared_b32_128k_config(dev):
     check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["plain", "shared_fp8", "shared_nvfp4_wide"])
+@pytest.mark.parametrize("case", ["plain", "plain_bf16_split", "shared_fp8", "shared_nvfp4_wide"])
 def test_graph_capture_replays(dev, case):
-    """msa_decode (or msa_decode_shared, whose shared pass is forked onto the
-    library's second stream and joined back with events) captured in a HIP
-    graph: every replay (with eager work and synchronisation in between)
-    equals the eager result bit for bit."""
+    """msa_decode (or msa_decode_shared) captured in a HIP graph: every replay
+    (with eager work and synchronisation in between) equals the eager result
+    bit for bit.  plain_bf16_split: bf16 K/V and few (row, group) pairs, so
+    the kept blocks are split over workgroups whose partials the last one
+    merges; the arrival counters are zeroed by the captured scan, with no
+    memset in the graph."""
     msa = _msa()
     if case == "plain":
         w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", seed=43, device=dev)
+    elif case == "plain_bf16_split":
+        w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", kv_dtype="bf16",
+                                idx_dtype="bf16", seed=45, device=dev)
     else:
         n = 8 if case == "shared_fp8" else 16
         w = synth.make_workload(seq_lens=[9000 + 97 * i for i in range(n)], plant=3, layout="paged", seed=44,
@@ -738,6 +743,37 @@ def test_graph_capture_replays(dev, case):
         assert torch.equal(sel, ref_sel), rep
         call()  # eager call between replays
         torch.cuda.synchronize()
+
+
+def test_split_merge_from_any_workspace(dev):
+    """bf16 K/V with few (row, group) pairs: msa_decode's kept-block split
+    merges each pair's partials in the workgroup that finishes last, counting
+    arrivals on counters in the workspace that the step's scan zeroes.  A
+    workspace left full of nonzero bytes (stale counters included) gives the
+    same bits as a zeroed one and as the stand-alone attention, whose second
+    launch merges the same partials; every row matches the oracle."""
+    msa = _msa()
+    w = synth.make_workload(seq_lens=[3000, 40000, 129, 0, 1000], plant=3, layout="paged", kv_dtype="bf16",
+                            idx_dtype="fp8", seed=46, device=dev)
+    shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+    results = []
+    for fill in (0, 0x7F, 0xFF, 0x01):
+        out, sel = msa.alloc_outputs(w)
+        ws = msa.alloc_workspace(shape, dev)
+        ws.fill_(fill)
+        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)  # counters left by a first call
+        torch.cuda.synchronize()
+        results.append((out.clone(), sel.clone()))
+    for out, sel in results[1:]:
+        assert torch.equal(out, results[0][0]) and torch.equal(sel, results[0][1])
+    out2 = torch.full_like(results[0][0], float("nan"))
+    aws = torch.empty(msa.msa_attn_workspace_size(shape), dtype=torch.uint8, device=dev)
+    msa.msa_sparse_attn_decode(shape, cache, w.q, results[0][1], out2, aws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, results[0][0])
+    P = oracle.Problem.from_workload(w)
+    check_rows(P, results[0][0].cpu().numpy(), results[0][1].cpu().numpy())
 
 
 def test_deterministic(dev):
