@@ -56,13 +56,14 @@ constexpr int kPvSteps = kBlock / 32;   // 32-token MFMA contraction steps per b
 // most 8,192 blocks).  The 512-thread form needs about half the LDS, so two
 // workgroups share a CU and hide each other's load and selection latency.
 // With the kept blocks split over SPLIT workgroups, each takes 16 / SPLIT
-// slots, one per wave (NT = 1024 / SPLIT).
-template <int NT, int SPLIT = 1>
+// slots, one per wave, or, with the tokens of each block split over TS waves
+// (bf16 K/V), one per TS waves (NT = 1024 / SPLIT x TS).
+template <int NT, int SPLIT = 1, int TS = 1>
 struct AttnShape {
   static constexpr int kWaves = NT / kWave;
   static constexpr int kSlots = kTopK / SPLIT;  // kept-block slots of one workgroup
-  static constexpr int kBlocksPerWave = kSlots / kWaves;
-  static_assert(kWaves * kBlocksPerWave * SPLIT == kTopK, "kept blocks split evenly over the waves");
+  static constexpr int kBlocksPerWave = kSlots * TS / kWaves;
+  static_assert(kWaves * kBlocksPerWave * SPLIT == kTopK * TS, "kept blocks split evenly over the waves");
 };
 
 template <int NT>
@@ -169,9 +170,13 @@ __device__ __forceinline__ void store_f32(float* p, float a) {
 // launch, or the last part to finish, combines the parts (COHERENT: the
 // partials are stored device-coherent for the latter).  Padded rows write
 // nothing but -1 ids.
+// TS > 1 (bf16 K/V, kept blocks split): each block's tokens are split over TS
+// waves, wave q of a block taking tokens [q 128 / TS, (q + 1) 128 / TS) (its
+// QK tiles and its PV steps); the waves' partials merge like those of
+// different blocks.
 // With SELECT, mbps must not exceed sel_max_blocks<NT>().  Every thread of the
 // workgroup must call it.
-template <bool FP4, bool SELECT, int DSPLIT, int NT, int SPLIT = 1, bool COHERENT = false>
+template <bool FP4, bool SELECT, int DSPLIT, int NT, int SPLIT = 1, bool COHERENT = false, int TS = 1>
 __device__ __forceinline__ void attn_workgroup(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -180,9 +185,12 @@ __device__ __forceinline__ void attn_workgroup(
     int row, int g, int part, AttnSmem<NT>& sm, float* __restrict__ po = nullptr, float2* __restrict__ pml = nullptr) {
   static_assert(DSPLIT == 1 || DSPLIT == 2 || DSPLIT == 4, "output split");
   static_assert(SPLIT == 1 || DSPLIT == 1, "split either the output dims or the kept blocks");
-  constexpr int kWaves = AttnShape<NT, SPLIT>::kWaves;
-  constexpr int kBpw = AttnShape<NT, SPLIT>::kBlocksPerWave;
-  constexpr int kSlot0Step = AttnShape<NT, SPLIT>::kSlots;  // first slot of part p: p * kSlots
+  static_assert(TS == 1 || (!FP4 && SPLIT > 1 && kPvSteps % TS == 0), "token split: bf16 K/V, kept blocks split");
+  constexpr int kWaves = AttnShape<NT, SPLIT, TS>::kWaves;
+  constexpr int kBpw = AttnShape<NT, SPLIT, TS>::kBlocksPerWave;
+  constexpr int kSlot0Step = AttnShape<NT, SPLIT, TS>::kSlots;  // first slot of part p: p * kSlots
+  constexpr int kTilesPerWave = kQkTiles / TS;  // QK tiles of one wave per block
+  constexpr int kStepsPerWave = kPvSteps / TS;  // PV steps of one wave per block
   // With the kept blocks split (one block per wave, at most 2 waves per SIMD)
   // the V loads go out with the K loads: registers are plentiful and the
   // wave's chain of round trips is what takes the time.
@@ -245,28 +253,31 @@ __device__ __forceinline__ void attn_workgroup(
     }
   }
 
+  const int tq = wave % TS;  // this wave's token part of its blocks
   for (int kb = 0; kb < kBpw; ++kb) {
-    const int slot = (SPLIT > 1 ? part * kSlot0Step : 0) + wave + kWaves * kb;
+    const int slot = (SPLIT > 1 ? part * kSlot0Step : 0) + wave / TS + (kWaves / TS) * kb;
     const int j = sm.sel[slot];
     // ids outside the row's visible blocks or the table contribute nothing
     if (j < 0 || j >= mbps || j * kBlock > pos) continue;  // wave-uniform
     const int64_t page = SELECT ? sm.page[slot] : block_table[(size_t)b * mbps + j];
     const int64_t row0 = (page * kGroups + g) * kBlock;  // first (token, head) row of this page/head
     const int nvis = min(pos - j * kBlock + 1, kBlock);   // keys: tokens 0..nvis-1 (>= 1)
+    if (tq * (kBlock / TS) >= nvis) continue;  // wave-uniform: no key in this wave's tokens
     const uint8_t* kbase = kpool + row0 * kRowBytes;
     const uint8_t* vbase = vpool + row0 * kRowBytes;
 
     [[maybe_unused]] uint32_t vw[kPvSteps][8];
     [[maybe_unused]] uint4 vq[FP4 ? kLaneDims : 1];  // NVFP4 V: dim d0 + t, tokens 32c .. 32c + 31
     [[maybe_unused]] uint4 vb[FP4 ? 1 : 8];
-    [[maybe_unused]] uint4 vbe[(!FP4 && kVEarly) ? kPvSteps : 1][8];  // bf16 V, loaded early
+    [[maybe_unused]] uint4 vbe[(!FP4 && kVEarly) ? kStepsPerWave : 1][8];  // bf16 V, loaded early
     auto load_v = [&]() {
       if constexpr (!FP4 && kVEarly) {
 #pragma unroll
-        for (int s = 0; s < kPvSteps; ++s)
+        for (int u = 0; u < kStepsPerWave; ++u)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            vbe[s][e] = *reinterpret_cast<const uint4*>(vbase + (size_t)(32 * s + 8 * c + e) * kRowBytes + 2 * d0);
+            vbe[u][e] = *reinterpret_cast<const uint4*>(
+                vbase + (size_t)(32 * (tq * kStepsPerWave + u) + 8 * c + e) * kRowBytes + 2 * d0);
       } else if constexpr (!FP4 && kLaneDims == 2) {  // bf16 V, 2 dims per lane: all 4 steps' words fit 32 VGPRs
 #pragma unroll
         for (int s = 0; s < kPvSteps; ++s)
@@ -302,10 +313,11 @@ __device__ __forceinline__ void attn_workgroup(
       wave_sync_lds();
     }
 
-    // ---- QK: z[T] = logit (log2 domain) of token 16T + 4c + jj, head hq
-    float z[kQkTiles];
+    // ---- QK: z[t] = logit (log2 domain) of token 16T + 4c + jj, head hq, T = tq kTilesPerWave + t
+    float z[kTilesPerWave];
 #pragma unroll
-    for (int T = 0; T < kQkTiles; ++T) {
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int T = tq * kTilesPerWave + t;
       f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FP4) {
         const uint32_t w[4] = {kv[T].x, kv[T].y, kv[T].z, kv[T].w};
@@ -353,7 +365,7 @@ __device__ __forceinline__ void attn_workgroup(
       y1 += dpp<kDppXor2>(x1);
       const float keep = b0 ? y1 : y0, send = b0 ? y0 : y1;
       const float dot = keep + dpp<kDppXor1>(send);
-      z[T] = 16 * T + 4 * c + jj < nvis ? dot * qk_scale_log2 : -INFINITY;
+      z[t] = 16 * T + 4 * c + jj < nvis ? dot * qk_scale_log2 : -INFINITY;
     }
 
     // ---- issue the V loads (here, or with the K loads): lane (c, n) takes
@@ -363,7 +375,7 @@ __device__ __forceinline__ void attn_workgroup(
     // ---- softmax over the block; with two blocks per wave, online across them
     float mx = z[0];
 #pragma unroll
-    for (int T = 1; T < kQkTiles; ++T) mx = fmaxf(mx, z[T]);
+    for (int t = 1; t < kTilesPerWave; ++t) mx = fmaxf(mx, z[t]);
     mx = fmaxf(mx, dpp<kDppXor1>(mx));
     mx = fmaxf(mx, dpp<kDppXor2>(mx));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -383,8 +395,9 @@ __device__ __forceinline__ void attn_workgroup(
     m_w = mx;
     float ls = 0.f;
 #pragma unroll
-    for (int T = 0; T < kQkTiles; ++T) {
-      const float p = exp2_nonpos(z[T] - mx);
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int T = tq * kTilesPerWave + t;
+      const float p = exp2_nonpos(z[t] - mx);
       ls += p;
       const uint16_t ph = PV::pack(p);
       sm.p[wave][hq][16 * T + 4 * c + jj] = ph;
@@ -399,7 +412,8 @@ __device__ __forceinline__ void attn_workgroup(
 
     // ---- PV
 #pragma unroll
-    for (int s = 0; s < kPvSteps; ++s) {
+    for (int u = 0; u < kStepsPerWave; ++u) {
+      const int s = tq * kStepsPerWave + u;
       // A: p of head n (rows 4..15 zero); the contraction's K index 8c + e is
       // token 32c + 8s + e with NVFP4 V (a lane's V bytes of one dim are then
       // one 16-B run), token 32s + 8c + e with bf16 V
@@ -441,7 +455,7 @@ __device__ __forceinline__ void attn_workgroup(
           const int tok = 32 * s + 8 * c + e;
           [[maybe_unused]] const uint8_t* src = vbase + (size_t)tok * kRowBytes + 2 * d0;
           if constexpr (kVEarly) {
-            vb[e] = vbe[s][e];
+            vb[e] = vbe[u][e];
           } else if constexpr (kLaneDims == 8) {
             vb[e] = *reinterpret_cast<const uint4*>(src);
           } else if constexpr (kLaneDims == 4) {

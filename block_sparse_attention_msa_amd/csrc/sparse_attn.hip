@@ -97,26 +97,27 @@ __device__ __forceinline__ void split_merge_pair(int id, int lane, const int32_t
   dst[1] = L > 0 ? make_float4(acc[4] * sc, acc[5] * sc, acc[6] * sc, acc[7] * sc) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// Kept blocks split over SPLIT workgroups of NT = 1024 / SPLIT threads, one
-// block per wave; each workgroup writes its partial (o, M, sum) per head.
+// Kept blocks split over SPLIT workgroups of NT = 1024 / SPLIT x TS threads,
+// each block's tokens over TS waves; each workgroup writes its partial
+// (o, M, sum) per head.
 // MERGE: the parts count their arrival on the pair's counter (zero at
 // launch) once their partial stores are complete, and the last one merges
 // the pair's partials and writes the output; otherwise a second launch
 // merges them.
-template <bool FP4, bool SELECT, int SPLIT, bool MERGE>
-__global__ __launch_bounds__(1024 / SPLIT) void attn_split_kernel(
+template <bool FP4, bool SELECT, int SPLIT, bool MERGE, int TS>
+__global__ __launch_bounds__(1024 / SPLIT * TS) void attn_split_kernel(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const uint8_t* __restrict__ k_sf,
     const uint8_t* __restrict__ v_sf, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ block_scores, const int32_t* __restrict__ sel_in,
     int32_t* __restrict__ sel_out, float* __restrict__ po, float2* __restrict__ pml, int32_t* __restrict__ counters,
     float* __restrict__ out, int rows, int q_len, int mbps, float qk_scale_log2, float v_scale) {
-  constexpr int NT = 1024 / SPLIT;
+  constexpr int NT = 1024 / SPLIT * TS;
   __shared__ AttnSmem<NT> sm;
   __shared__ int last;
   int pair, part;
   attn_decode_wg<SPLIT>(blockIdx.x, pair, part);
   if (pair >= rows * kGroups) return;
-  attn_workgroup<FP4, SELECT, 1, NT, SPLIT, MERGE>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores,
+  attn_workgroup<FP4, SELECT, 1, NT, SPLIT, MERGE, TS>(kpool, vpool, k_sf, v_sf, block_table, seq_lens, q, block_scores,
                                                   sel_in, sel_out, nullptr, q_len, mbps, qk_scale_log2, 1.f,
                                                   pair / kGroups, pair % kGroups, part, sm, po, pml);
   if constexpr (MERGE) {
@@ -143,20 +144,28 @@ __global__ __launch_bounds__(256) void attn_split_merge_kernel(const int32_t* __
   split_merge_pair<SPLIT, false>(id, threadIdx.x & (kWave - 1), seq_lens, q_len, po, pml, v_scale, out);
 }
 
+// bf16 K/V: each kept block's 128 tokens over TS = 4 waves, so that no wave
+// streams a whole 64 KB block through its own outstanding loads; the 8-block
+// parts (SPLIT = 2) keep one wave per block (16 waves would exceed 128 VGPRs).
+template <bool FP4, int SPLIT>
+constexpr int split_token_waves() { return !FP4 && SPLIT >= 4 ? 4 : 1; }
+
 template <bool FP4, bool SELECT, int SPLIT>
 void launch_split(const AttnArgs& a, hipStream_t stream) {
+  constexpr int TS = split_token_waves<FP4, SPLIT>();
+  constexpr int NT = 1024 / SPLIT * TS;
   const long long pairs = (long long)a.rows * kGroups;
   float* po = a.partials;
   float2* pml = reinterpret_cast<float2*>(a.partials + (size_t)pairs * kTopK * kHeadsPerGroup * kDim);
   const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * SPLIT));
   if (a.counters) {  // merged by the last part of each pair: one launch
-    attn_split_kernel<FP4, SELECT, SPLIT, true><<<grid, 1024 / SPLIT, 0, stream>>>(
+    attn_split_kernel<FP4, SELECT, SPLIT, true, TS><<<grid, NT, 0, stream>>>(
         static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table,
         a.seq_lens, a.q, a.block_scores, a.sel, a.sel_out, po, pml, a.counters, a.out, a.rows, a.q_len, a.mbps,
         a.qk_scale_log2, a.v_scale);
     return;
   }
-  attn_split_kernel<FP4, SELECT, SPLIT, false><<<grid, 1024 / SPLIT, 0, stream>>>(
+  attn_split_kernel<FP4, SELECT, SPLIT, false, TS><<<grid, NT, 0, stream>>>(
       static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.k_sf, a.v_sf, a.block_table, a.seq_lens,
       a.q, a.block_scores, a.sel, a.sel_out, po, pml, nullptr, nullptr, a.rows, a.q_len, a.mbps, a.qk_scale_log2,
       a.v_scale);

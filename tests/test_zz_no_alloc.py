@@ -51,6 +51,25 @@ def test_noalloc_matches_decode_two_calls_second_smaller():
         check_rows(P, out.cpu().numpy(), sel.cpu().numpy())
 
 
+def test_noalloc_bf16_split_counters_in_scratch():
+    """bf16 K/V with few (row, group) pairs: the kept blocks are split over
+    workgroups whose arrival counters sit in the static scratch after the
+    partials.  The scratch keeps the previous call's bytes (counters left at
+    their final counts included); each call's scan zeroes them, so two calls
+    in a row, the second smaller, both match msa_decode bit for bit."""
+    from block_sparse_attention_msa_amd import msa
+    dev = torch.device("cuda:0")
+    a = synth.make_workload(seq_lens=[5000, 128 * 9, 0, 700, 20000], plant=3, layout="paged", kv_dtype="bf16",
+                            idx_dtype="bf16", seed=123, device=dev)
+    b = synth.make_workload(seq_lens=[3000, 129], plant=2, layout="paged", kv_dtype="bf16", idx_dtype="fp8",
+                            seed=124, device=dev)
+    for label, w in (("bf16 split, 5 rows", a), ("bf16 split, 2 rows", b)):
+        _say(f"[noalloc] {label}")
+        out, sel = _both(msa, w)
+        P = oracle.Problem.from_workload(w)
+        check_rows(P, out.cpu().numpy(), sel.cpu().numpy())
+
+
 def test_noalloc_selection_launch_ids_in_scratch():
     """160 decode rows: more (row, group) pairs than two per compute unit, so
     the selection runs as its own launch; with no sel_blocks output its ids
