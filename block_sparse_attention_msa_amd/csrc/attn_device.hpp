@@ -487,23 +487,6 @@ __device__ __forceinline__ void attn_workgroup(
     }
     wave_sync_lds();  // the next block rewrites this wave's LDS
   }
-  if constexpr (SPLIT > 1 && kWaves == 1) {
-    // a one-wave part: its registers are the partial (lanes 0..15 hold heads
-    // 0..3 x dims d0 .. d0 + 7; lane 4 h holds head h's (m, l))
-    float* dst = po + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup * kDim;
-    if (c == 0) {
-#pragma unroll
-      for (int i = 0; i < kHeadsPerGroup; ++i) {
-        float* d = dst + i * kDim + d0;
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) store_f32x2<COHERENT>(d + t, acc[t][i], acc[t + 1][i]);
-      }
-    }
-    if (c == 0 && jj == 0)
-      store_f32x2<COHERENT>(reinterpret_cast<float*>(pml + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + hq),
-                            m_w, l_w);
-    return;
-  }
   __syncthreads();  // selection LDS is dead: the merge area reuses it
 
   // ---- per-wave partials to LDS: lanes 0..15 hold heads 0..3 (acc rows) x dims d0 + t
