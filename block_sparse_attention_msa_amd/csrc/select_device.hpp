@@ -169,10 +169,14 @@ __device__ __forceinline__ uint32_t wave_sort_desc32(uint32_t v, int lane) {
 template <int E, bool PAGES>
 __device__ __forceinline__ void sel_append(const uint64_t (&keys)[E], const int32_t (&pages)[E], uint64_t thr,
                                            uint64_t (&ballot)[E], int total, int lane, uint64_t* cand,
-                                           int32_t* cand_page, int* count) {
+                                           int32_t* cand_page, int* count, bool solo) {
   int base = 0;
-  if (lane == 0) base = atomicAdd(count, total);
-  base = __shfl(base, 0);
+  if (solo) {  // the only wave with candidates: they start at 0
+    if (lane == 0) *count = total;
+  } else {
+    if (lane == 0) base = atomicAdd(count, total);
+    base = __shfl(base, 0);
+  }
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -254,15 +258,24 @@ __device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* _
 
   // 2. T0 = max over active waves of the wave's 15th best lane-best score (wave
   //    0 always has at least 16 lanes holding keys, so T0 > 0 and absent keys,
-  //    0, never qualify)
+  //    0, never qualify).  With one active wave (solo, workgroup-uniform) T0
+  //    stays in its registers and no workgroup barrier is needed until the
+  //    winners are written.
+  const bool solo = active == 1;
+  uint32_t t0 = 0;
   if (wave < active) {
     const uint32_t sorted = wave_sort_desc32(best, lane);
-    if (lane == kTopK - 2) sm.wave_t0[wave] = sorted;
+    if (solo)
+      t0 = (uint32_t)__builtin_amdgcn_readlane((int)sorted, kTopK - 2);
+    else if (lane == kTopK - 2)
+      sm.wave_t0[wave] = sorted;
   }
-  if (tid == 0) sm.count = 0;
-  __syncthreads();
-  uint32_t t0 = sm.wave_t0[0];
-  for (int w = 1; w < active; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
+  if (!solo) {
+    if (tid == 0) sm.count = 0;
+    __syncthreads();
+    t0 = sm.wave_t0[0];
+    for (int w = 1; w < active; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
+  }
 
   // 3. candidates: score >= T0, or, in a wave with too many ties at T0, key >=
   //    the wave's exact 15th-best lane key
@@ -280,9 +293,12 @@ __device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* _
       thr = tw > thr ? tw : thr;
       total = sel_ballots(keys, thr, ballot);
     }
-    sel_append<E, PAGES>(keys, pages, thr, ballot, total, lane, sm.cand, sm.cand_page, &sm.count);
+    sel_append<E, PAGES>(keys, pages, thr, ballot, total, lane, sm.cand, sm.cand_page, &sm.count, solo);
   }
-  __syncthreads();
+  if (solo)
+    wave_sync_lds();  // wave 0 reads back what it wrote
+  else
+    __syncthreads();
 
   if (wave == 0) {
     // 4. the 15 best candidates -> lanes 0..14 (any order): (myj, mypage)
