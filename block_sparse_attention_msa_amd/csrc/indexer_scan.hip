@@ -307,9 +307,9 @@ hipError_t launch_scan_shared(const ScanArgs& a, const int32_t* members, const i
       else
         scan_shared_kernel<true, 2, 4, false, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
     } else if (q_len == 1) {
-      // 5 waves per SIMD (at most 102 VGPRs: the wide shared body takes 96, the
-      // own rows' NVFP4 decode body 80; 6 per SIMD spilled 38)
-      scan_shared_kernel<true, 0, 5, true, true><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
+      // the wide forms' two 32 KB page buffers leave room for two workgroups
+      // per CU: 4 waves per SIMD whatever the registers
+      scan_shared_kernel<true, 0, 4, true, true><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
     } else if (q_len <= 4) {
       scan_shared_kernel<true, 1, 4, true, false><<<grid, block, 0, stream>>>(MSA_SHARED_ARGS);
     } else {
