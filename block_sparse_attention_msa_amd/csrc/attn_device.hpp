@@ -521,9 +521,10 @@ __device__ __forceinline__ void attn_workgroup(
     fl += __shfl_xor(fl, 32);
     if (w < kWaves) sm.u.merge.f[w][h] = f;
     if (w == 0) sm.u.merge.inv[h] = SPLIT > 1 ? 1.f : (fl > 0.f ? v_scale / fl : 0.f);
-    if (SPLIT > 1 && w == 0)
-      store_f32x2<COHERENT>(reinterpret_cast<float*>(pml + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + h),
-                            M, fl);
+    if (SPLIT > 1 && w == 0) {
+      float2* ml_dst = pml + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup + h;
+      store_f32x2<COHERENT>(reinterpret_cast<float*>(ml_dst), M, fl);
+    }
   }
   __syncthreads();
   float* dst = SPLIT > 1 ? po + ((size_t)(row * kGroups + g) * SPLIT + part) * kHeadsPerGroup * kDim : out_row;

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
                                                              const int32_t* __restrict__ seq_lens,
                                                              const uint16_t* __restrict__ iq,
                                                              float* __restrict__ block_scores, int q_len, int mbps,
-                                                             int nchunks, int wgs, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+                                                             int nchunks, int wgs, float idx_scale,
+                                                             int32_t* __restrict__ zero, int zero_n) {
   zero_step_counters(zero, zero_n);
   // bytes per token of an index-key page: E4M3, bf16, or E2M1 codes (NVFP4,
   // whose 8 group scales per token sit in idx_sf, 1 KB per page)
@@ -274,13 +275,16 @@ hipError_t launch_scan_mq(const ScanArgs& a, int q_len, hipStream_t stream) {
   const uint8_t* pool = static_cast<const uint8_t*>(a.idx_pool);
   if (a.idx_fmt == kIdxFp8)
     scan_mq_kernel<kIdxFp8><<<grid, kMqThreads, 0, stream>>>(pool, nullptr, a.block_table, a.seq_lens, a.iq,
-                                                              a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale, a.zero, a.zero_n);
+                                                              a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale,
+                                                              a.zero, a.zero_n);
   else if (a.idx_fmt == kIdxNvfp4)
     scan_mq_kernel<kIdxNvfp4><<<grid, kMqThreads, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
-                                                                a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale, a.zero, a.zero_n);
+                                                                a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale,
+                                                                a.zero, a.zero_n);
   else
     scan_mq_kernel<kIdxBf16><<<grid, kMqThreads, 0, stream>>>(pool, nullptr, a.block_table, a.seq_lens, a.iq,
-                                                               a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale, a.zero, a.zero_n);
+                                                               a.block_scores, q_len, a.mbps, nchunks, wgs, a.idx_scale,
+                                                               a.zero, a.zero_n);
   return hipGetLastError();
 }
 

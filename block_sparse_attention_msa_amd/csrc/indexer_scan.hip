@@ -27,7 +27,8 @@ __global__ __launch_bounds__(kScanWaves * kWave, 5) void scan_decode_kernel(cons
                                                                           const int32_t* __restrict__ seq_lens,
                                                                           const uint16_t* __restrict__ iq,
                                                                           float* __restrict__ block_scores, int mbps,
-                                                                          int blocks_per_wave, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+                                                                          int blocks_per_wave, float idx_scale,
+                                                                          int32_t* __restrict__ zero, int zero_n) {
   zero_step_counters(zero, zero_n);
   const int b = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(kColsScanWaves * kWave) void scan_cols_kernel(const
                                                                          const int32_t* __restrict__ seq_lens,
                                                                          const uint16_t* __restrict__ iq,
                                                                          float* __restrict__ block_scores, int q_len,
-                                                                         int mbps, int pages_per_wave, float idx_scale, int32_t* __restrict__ zero, int zero_n) {
+                                                                         int mbps, int pages_per_wave, float idx_scale,
+                                                                         int32_t* __restrict__ zero, int zero_n) {
   zero_step_counters(zero, zero_n);
   __shared__ __attribute__((aligned(16))) uint8_t lds_t[kColsScanWaves][2 * 2048];
   const int b = blockIdx.y;
@@ -265,10 +267,12 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
   if (a.idx_fmt == kIdxNvfp4) {
     if (q_len <= 4)
       scan_cols_nvfp4_kernel<1><<<grid, block, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
-                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale, a.zero, a.zero_n);
+                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale,
+                                                             a.zero, a.zero_n);
     else
       scan_cols_nvfp4_kernel<2><<<grid, block, 0, stream>>>(pool, a.idx_sf, a.block_table, a.seq_lens, a.iq,
-                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale, a.zero, a.zero_n);
+                                                             a.block_scores, q_len, a.mbps, ppw, a.idx_scale,
+                                                             a.zero, a.zero_n);
     return hipGetLastError();
   }
   if (q_len <= 4)
@@ -349,18 +353,20 @@ hipError_t launch_scan_decode(const ScanArgs& a, hipStream_t stream) {
   dim3 block(waves_per_wg * kWave);
   if (a.idx_fmt == kIdxNvfp4) {
     dim3 g2((a.mbps + kNvfp4ScanWaves - 1) / kNvfp4ScanWaves, a.num_seqs);
-    scan_decode_nvfp4_kernel<<<g2, dim3(kNvfp4ScanWaves * kWave), 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.idx_sf,
-                                                       a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
-                                                       a.idx_scale, a.zero, a.zero_n);
+    scan_decode_nvfp4_kernel<<<g2, dim3(kNvfp4ScanWaves * kWave), 0, stream>>>(
+        static_cast<const uint8_t*>(a.idx_pool), a.idx_sf, a.block_table, a.seq_lens, a.iq, a.block_scores, a.mbps,
+        a.idx_scale, a.zero, a.zero_n);
   } else if ((long long)a.num_seqs * a.mbps <= 2LL * device_cus()) {
     // few pages: 8 waves per page (4 wave-loads, 16 tokens each)
     constexpr int S = kScanWaves;
     dim3 g2((a.mbps + kScanWaves / S - 1) / (kScanWaves / S), a.num_seqs);
     scan_decode_split_kernel<S><<<g2, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, a.idx_scale, a.zero, a.zero_n);
+                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, a.idx_scale,
+                                                           a.zero, a.zero_n);
   } else {
     scan_decode_kernel<false><<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(a.idx_pool), a.block_table,
-                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale, a.zero, a.zero_n);
+                                                           a.seq_lens, a.iq, a.block_scores, a.mbps, bpw, a.idx_scale,
+                                                           a.zero, a.zero_n);
   }
   return hipGetLastError();
 }

@@ -64,9 +64,8 @@ __device__ __forceinline__ void split_merge_pair(int id, int lane, const int32_t
   const int row = id / kGroups;
   const int h = lane >> 4, d0 = 8 * (lane & 15);
   const int L = seq_lens[row / q_len];
-  const float2 ml = lane < SPLIT * kHeadsPerGroup
-                        ? load_f32x2<COHERENT>(reinterpret_cast<const float*>(pml + (size_t)id * SPLIT * kHeadsPerGroup + lane))
-                        : make_float2(-INFINITY, 0.f);
+  const float* ml_src = reinterpret_cast<const float*>(pml + (size_t)id * SPLIT * kHeadsPerGroup + lane);
+  const float2 ml = lane < SPLIT * kHeadsPerGroup ? load_f32x2<COHERENT>(ml_src) : make_float2(-INFINITY, 0.f);
   const float* src = po + ((size_t)id * SPLIT * kHeadsPerGroup + h) * kDim + d0;
   float2 v[SPLIT][4];
 #pragma unroll
