@@ -841,3 +841,52 @@ def test_kv_insert_matches_oracle(dev, kv, idx, q_len, scales):
         changed += int(np.count_nonzero(got != old))
     assert changed > 0
     check_workload(w, label=f"decode after insert {kv}/{idx} q_len={q_len}")
+
+
+@pytest.mark.parametrize("kv,idx", [("nvfp4", "fp8"), ("bf16", "bf16"), ("nvfp4", "nvfp4")])
+def test_multi_step_decode_with_inserts(dev, kv, idx):
+    """Decode steps as a serving loop runs them: each step appends one token
+    per sequence (its row of the block table gets a fresh page when the token
+    opens a new block), inserts the token's K/V/index key with msa_kv_insert,
+    draws new queries and decodes over the grown cache.  After every insert
+    the pools equal the oracle's bytes; every decode matches the oracle on
+    every row.  Lengths start just below, on and past page boundaries; one
+    row is padded and stays so."""
+    msa = _msa()
+    lens = [127, 0, 128 * 5 - 2, 1000, 128 * 2]
+    steps = 4
+    w = synth.make_workload(seq_lens=lens, kv_dtype=kv, idx_dtype=idx, plant=2, layout="paged", seed=61,
+                            spare_pages=8, max_blocks_per_seq=max((L + steps - 1) // 128 + 1 for L in lens),
+                            device=dev)
+    bt0, L0 = w.block_table.cpu(), w.seq_lens.cpu().tolist()
+    used = {int(bt0[b, j]) for b, n in enumerate(L0) for j in range((n + 127) // 128)}
+    spare = sorted(set(range(w.num_pages)) - used)
+    assert len(spare) == 8
+    g = torch.Generator(device="cpu").manual_seed(17)
+    for step in range(steps):
+        L = w.seq_lens.cpu().tolist()
+        bt = w.block_table.cpu()
+        for b, n in enumerate(L):
+            if n == 0:
+                continue
+            if n % 128 == 0:  # the new token opens block n / 128
+                bt[b, n // 128] = spare.pop(0)
+            L[b] = n + 1
+        w.block_table.copy_(bt.to(dev))
+        w.seq_lens.copy_(torch.tensor(L, dtype=torch.int32).to(dev))
+        w.q.copy_(torch.randn(w.q.shape, generator=g).to(torch.bfloat16).to(dev))
+        w.iq.copy_(torch.randn(w.iq.shape, generator=g).to(torch.bfloat16).to(dev))
+        k_new = torch.randn(w.rows, 4, 128, generator=g).to(torch.bfloat16)
+        v_new = torch.randn(w.rows, 4, 128, generator=g).to(torch.bfloat16)
+        x_new = torch.randn(w.rows, 128, generator=g).to(torch.bfloat16)
+        P = oracle.Problem.from_workload(w)  # the grown metadata, the pools before the insert
+        shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+        msa.msa_kv_insert(shape, cache, k_new.to(dev), v_new.to(dev), x_new.to(dev))
+        torch.cuda.synchronize()
+        P.kv_insert(_bits(k_new), _bits(v_new), _bits(x_new))
+        h = w.host_arrays()
+        for name in ("k", "v", "k_sf", "v_sf", "idx_k", "idx_sf"):
+            if h.get(name) is not None:
+                assert np.array_equal(h[name], P.arrays[name]), f"step {step}: {name} differs after the insert"
+        check_workload(w, label=f"decode step {step} {kv}/{idx}")
+
