@@ -259,7 +259,12 @@ hipError_t launch_scan_cols(const ScanArgs& a, int q_len, hipStream_t stream) {
   // shape: q_len 1 80.6 us with one page per wave (81.3-81.8 us with 2 or 4),
   // q_len 4 88 us with two (91.5 us with one, 88 us with four); 4- and 16-wave
   // workgroups 1-10 % slower, 5 waves per SIMD (at most 102 VGPRs) 11-13 %.
-  const int ppw = q_len == 1 ? 1 : 2;
+  // NVFP4 keys (q_len 2-8) on the same shape: 53.0-53.7 us with four pages
+  // per wave against 54.8-54.9 with two, 61.6-62.2 with one and 63.5 / 70.2
+  // with eight / sixteen (too few workgroups to fill the GPU), so four where
+  // the batch has at least 128 pages per CU (1,024 workgroups at 256 CUs).
+  const bool deep = a.idx_fmt == kIdxNvfp4 && (long long)a.num_seqs * a.mbps >= 128LL * device_cus();
+  const int ppw = q_len == 1 ? 1 : deep ? 4 : 2;
   const int per_wg = kColsScanWaves * ppw;
   dim3 grid((a.mbps + per_wg - 1) / per_wg, a.num_seqs);
   dim3 block(kColsScanWaves * kWave);
