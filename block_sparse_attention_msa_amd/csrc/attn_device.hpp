@@ -207,7 +207,7 @@ __device__ __forceinline__ void attn_workgroup(
   const int L = seq_lens[b];
   [[maybe_unused]] SelLoads ld;  // the selection's loads, issued before the row length arrives
   if constexpr (SELECT)
-    select_load<true>(block_scores + ((size_t)row * kGroups + g) * mbps, block_table + (size_t)b * mbps, mbps, ld);
+    select_load<NT, true>(block_scores + ((size_t)row * kGroups + g) * mbps, block_table + (size_t)b * mbps, mbps, ld);
   const int head0 = g * kHeadsPerGroup;
   const int dbase = SPLIT > 1 ? 0 : part * kDims;
   float* out_row = out + ((size_t)row * (kGroups * kHeadsPerGroup) + head0) * kDim;
@@ -222,7 +222,7 @@ __device__ __forceinline__ void attn_workgroup(
   const int pos = L - q_len + row % q_len;
   if constexpr (SELECT) {
     const int r = min(pos / kBlock, mbps - 1);
-    select_blocks<NT, true>(ld, block_table + (size_t)b * mbps, r, sm.u.sel, sm.sel, sm.page);
+    select_blocks<NT, true>(ld, block_table + (size_t)b * mbps, r, mbps, sm.u.sel, sm.sel, sm.page);
     if (sel_row && tid < kTopK) sel_row[tid] = sm.sel[tid];
   } else {
     if (tid < kTopK) sm.sel[tid] = sel_in[((size_t)row * kGroups + g) * kTopK + tid];

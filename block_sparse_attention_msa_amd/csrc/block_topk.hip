@@ -22,7 +22,7 @@ __global__ __launch_bounds__(NT) void block_topk_kernel(const int32_t* __restric
   const int b = row / q_len;
   const int L = seq_lens[b];
   SelLoads ld;  // issued before the row length arrives
-  select_load<false>(block_scores + ((size_t)row * kGroups + g) * mbps, nullptr, mbps, ld);
+  select_load<NT, false>(block_scores + ((size_t)row * kGroups + g) * mbps, nullptr, mbps, ld);
   int32_t* out = sel + ((size_t)row * kGroups + g) * kTopK;
   if (L <= 0) {
     if (threadIdx.x < kTopK) out[threadIdx.x] = -1;
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(NT) void block_topk_kernel(const int32_t* __restric
   }
   const int pos = L - q_len + row % q_len;
   const int r = min(pos / kBlock, mbps - 1);  // recent block (clamped: never read past the row)
-  select_blocks<NT, false>(ld, nullptr, r, sm, out, nullptr);
+  select_blocks<NT, false>(ld, nullptr, r, mbps, sm, out, nullptr);
 }
 
 template <int NT>

@@ -10,44 +10,64 @@
 // lower block index (total order: score descending, index ascending), which
 // makes the selection exact under any split of the candidates.
 //
-// Algorithm (one active wave per 1,024 candidate blocks, 16 keys per lane):
-//  1. wave w takes blocks j = 1024 w + lane + 64 e (e < 16; coalesced loads,
+// Algorithm (A selection waves: one for tables of up to 256 blocks, else the
+// waves the row needs at 1,024 keys each, but at least four, one per SIMD,
+// when the workgroup has them; E <= 16 keys per lane):
+//  1. wave w < A takes blocks j = 64 (A e + w) + lane (e < E; coalesced loads,
 //     all issued before use, and before the row length is known) as 64-bit
 //     keys (ordered score << 32 | ~j), and, for the attention, the blocks'
 //     page ids from the block table;
-//  2. each active wave sorts its 64 lane-best scores (32-bit bitonic, DPP lane
-//     moves where they exist); the wave's 15th best score T_w bounds the 15th
-//     best key overall from below (15 distinct blocks reach it), and so does
-//     T0 = max_w T_w;
+//  2. lane l's best score over its keys in all selection waves (the blocks
+//     j = l mod 64) is gathered through LDS; every active wave sorts the 64
+//     lane-bests (32-bit bitonic, DPP lane moves where they exist), and their
+//     15th best T0 bounds the 15th best key overall from below (15 distinct
+//     blocks reach it);
 //  3. keys whose score is >= T0 (every true top-15 key among them) are
 //     compacted into LDS with ballots, one LDS atomic per wave; a wave whose
-//     count exceeds 15 lanes x 16 keys (many scores tied at T0) uses its exact
+//     count exceeds 15 lanes x E keys (many scores tied at T0) uses its exact
 //     64-bit 15th-best lane key instead, which bounds its count again;
 //  4. wave 0 ranks up to 64 candidates by counting larger keys (broadcast LDS
-//     reads); more candidates are merged 49 at a time into a running top-15
-//     with a 64-bit bitonic sort;
+//     reads); more are merged 49 at a time into a running top-15 with a 64-bit
+//     bitonic sort;
 //  5. the 15 ids plus the recent block are written in ascending order, with
 //     their page ids when asked for.
+// One wave issues about 40 instructions per key per lane in steps 1-3, so the
+// keys are spread over a wave of each SIMD rather than held by one wave.
 #pragma once
 
 #include "msa_device.hpp"
 
 namespace msa {
 
-constexpr int kSelKeysPerLane = 16;                               // keys per lane of an active wave
+constexpr int kSelKeysPerLane = 16;                               // keys per lane of an active wave, at most
 constexpr int kSelBlocksPerWave = kWave * kSelKeysPerLane;         // 1,024
 constexpr int kSelWaveCap = (kTopK - 1) * kSelKeysPerLane;         // candidates per active wave, at most
+constexpr int kSelMinWaves = 4;                                    // one wave per SIMD
+constexpr int kSelSoloBlocks = 4 * kWave;                          // up to here one wave, no barrier
 
 // A workgroup of NT threads selects among at most (NT / 64) x 1,024 blocks.
 template <int NT>
 constexpr int sel_max_blocks() { return NT / kWave * kSelBlocksPerWave; }
+
+// The selection waves A for rows of at most cap blocks (cap <= sel_max_blocks):
+// one wave up to 256 blocks (4 keys per lane cost less than the workgroup
+// barrier and the exchange of lane-bests), else the waves that 1,024 keys each
+// need, at least kSelMinWaves when the workgroup has them.  Wave w < A holds
+// blocks 64 (A e + w) + lane.
+template <int NT>
+__device__ __forceinline__ int sel_waves(int cap) {
+  constexpr int kWaves = NT / kWave;
+  if (cap <= kSelSoloBlocks) return 1;
+  const int need = (cap + kSelBlocksPerWave - 1) / kSelBlocksPerWave;
+  return min(kWaves, max(need, kSelMinWaves));
+}
 
 template <int NT>
 struct SelectSmem {
   static constexpr int kCandCap = kSelWaveCap * (NT / kWave) + kWave;  // at most 15 x 16 keys per active wave
   uint64_t cand[kCandCap];
   int32_t cand_page[kCandCap];
-  uint32_t wave_t0[NT / kWave];
+  uint32_t lane_best[NT / kWave][kWave];  // each selection wave's lane-best scores
   int32_t win[kTopK];
   int32_t win_page[kTopK];
   int count;
@@ -206,38 +226,41 @@ struct SelLoads {
   int32_t pages[kSelKeysPerLane];
 };
 
-// Issues this wave's loads of blocks 1,024 w + lane + 64 e (e < 16), clamped
-// to the row's cap entries, so that they need not wait for the row length:
-// the scores s[] and, when PAGES, the block-table entries (read, never
-// followed).  Waves that start past the row load nothing.  Entries past the
+// Issues this wave's loads of its blocks 64 (A e + w) + lane (A =
+// sel_waves(cap)), clamped to the row's cap entries, so that they need not
+// wait for the row length: the scores s[] and, when PAGES, the block-table
+// entries (read, never followed).  Waves past A load nothing.  Entries past the
 // candidates are discarded by select_blocks, so they may hold anything.
-template <bool PAGES>
+template <int NT, bool PAGES>
 __device__ __forceinline__ void select_load(const float* __restrict__ s, const int32_t* __restrict__ bt_row, int cap,
                                             SelLoads& ld) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  if (wave * kSelBlocksPerWave >= cap) return;  // wave-uniform
-  const int j0 = wave * kSelBlocksPerWave + lane;
+  const int A = sel_waves<NT>(cap);
+  if (wave >= A) return;  // wave-uniform
 #pragma unroll
   for (int e = 0; e < kSelKeysPerLane; ++e) {
-    const int idx = min(j0 + e * kWave, cap - 1);
+    // keys per lane: the power of two that covers cap (select_blocks uses a
+    // power of two covering the row length, never more)
+    if (e > 0 && (e & (e - 1)) == 0 && kWave * A * e >= cap) break;  // wave-uniform
+    const int idx = min(kWave * (A * e + wave) + lane, cap - 1);
     ld.sv[e] = s[idx];
     ld.pages[e] = PAGES ? bt_row[idx] : 0;
   }
 }
 
-// The selection proper for n >= 16 candidates (blocks 0 .. n - 1, n = r), with
-// E of the 16 loaded keys per lane in use: 1 for n <= 64, 4 for n <= 256,
-// else 16 (the candidates beyond a lane's first E keys are past the row).
+// The selection proper for n >= 16 candidates (blocks 0 .. n - 1, n = r) held
+// by A selection waves, with E of the loaded keys per lane in use, 64 A E >= n
+// (the blocks beyond a lane's first E keys are past the row).
 template <int NT, bool PAGES, int E>
-__device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r,
+__device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r, int A,
                                             SelectSmem<NT>& sm, int32_t* out, int32_t* out_page) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int n = r;
-  const int active = (n + kSelBlocksPerWave - 1) / kSelBlocksPerWave;
-  const int j0 = wave * kSelBlocksPerWave + lane;
+  // waves holding candidates: with one key per lane, the first n / 64
+  const int active = E == 1 ? min(A, (n + kWave - 1) / kWave) : A;
   int32_t recent_page = 0;
   if (PAGES && tid == kTopK - 1) recent_page = bt_row[r];
 
@@ -245,37 +268,35 @@ __device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* _
   uint64_t keys[E];
   int32_t pages[E];
   uint32_t best = 0;
-  if (wave < active) {  // loaded: 1,024 w < n < cap
+  if (wave < active) {  // loaded: these blocks are below cap
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int j = j0 + e * kWave;
+      const int j = kWave * (A * e + wave) + lane;
       pages[e] = ld.pages[e];
-      keys[e] = j < n ? block_key(ld.sv[e], j) : 0;
+      const uint64_t k = block_key(ld.sv[e], j);
+      keys[e] = j < n ? k : 0;
       const uint32_t hi = (uint32_t)(keys[e] >> 32);
       best = hi > best ? hi : best;
     }
   }
 
-  // 2. T0 = max over active waves of the wave's 15th best lane-best score (wave
-  //    0 always has at least 16 lanes holding keys, so T0 > 0 and absent keys,
-  //    0, never qualify).  With one active wave (solo, workgroup-uniform) T0
-  //    stays in its registers and no workgroup barrier is needed until the
-  //    winners are written.
+  // 2. T0 = the 15th best of the 64 lane-best scores, lane l's best taken over
+  //    its keys in every active wave (blocks j = l mod 64; the waves' bests
+  //    meet in LDS), so 15 distinct blocks reach T0 and every top-15 key
+  //    scores at least T0 (wave 0 always has at least 16 lanes holding keys,
+  //    so T0 > 0 and absent keys, 0, never qualify).  Every active wave sorts
+  //    the same 64 values.  With one active wave (solo, workgroup-uniform) no
+  //    workgroup barrier is needed until the winners are written.
   const bool solo = active == 1;
-  uint32_t t0 = 0;
-  if (wave < active) {
-    const uint32_t sorted = wave_sort_desc32(best, lane);
-    if (solo)
-      t0 = (uint32_t)__builtin_amdgcn_readlane((int)sorted, kTopK - 2);
-    else if (lane == kTopK - 2)
-      sm.wave_t0[wave] = sorted;
-  }
   if (!solo) {
+    if (wave < active) sm.lane_best[wave][lane] = best;
     if (tid == 0) sm.count = 0;
     __syncthreads();
-    t0 = sm.wave_t0[0];
-    for (int w = 1; w < active; ++w) t0 = sm.wave_t0[w] > t0 ? sm.wave_t0[w] : t0;
+    if (wave < active)
+      for (int w = 0; w < active; ++w) best = sm.lane_best[w][lane] > best ? sm.lane_best[w][lane] : best;
   }
+  uint32_t t0 = 0;
+  if (wave < active) t0 = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort_desc32(best, lane), kTopK - 2);
 
   // 3. candidates: score >= T0, or, in a wave with too many ties at T0, key >=
   //    the wave's exact 15th-best lane key
@@ -356,18 +377,18 @@ __device__ __forceinline__ void select_core(const SelLoads& ld, const int32_t* _
   __syncthreads();
 }
 
-// Selection for one (row, group) by a workgroup of NT threads; r must be below
-// sel_max_blocks<NT>() so that every candidate fits the active waves'
-// registers (1,024 per wave).
-// ld: the wave's select_load of the row/group's scores, with a cap above r;
+// Selection for one (row, group) by a workgroup of NT threads; cap must not
+// exceed sel_max_blocks<NT>() so that every candidate fits the selection
+// waves' registers (1,024 per wave).
+// ld: the wave's select_load of the row/group's scores with this cap (r < cap);
 // bt_row: its block table row (read only when PAGES); r: the recent block
 // (0 <= r < row length).  Writes 16 ids (ascending, -1 padded) to out[] and,
 // when PAGES, their page ids to out_page[] (0 for padding), then synchronises
 // the workgroup so LDS outputs are readable by every thread.  Every thread of
 // the workgroup must call it.
 template <int NT, bool PAGES>
-__device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r, SelectSmem<NT>& sm,
-                              int32_t* out, int32_t* out_page) {
+__device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt_row, int r, int cap,
+                              SelectSmem<NT>& sm, int32_t* out, int32_t* out_page) {
   constexpr int kWaves = NT / kWave;
   static_assert(NT % kWave == 0 && kWaves >= 1, "whole waves");
   const int tid = threadIdx.x;
@@ -381,12 +402,18 @@ __device__ void select_blocks(const SelLoads& ld, const int32_t* __restrict__ bt
   }
   // candidates: blocks 0 .. r-1 (n = r >= 16); the keys per lane in use
   // follow the row length (a workgroup-uniform choice)
-  if (r <= kWave)
-    select_core<NT, PAGES, 1>(ld, bt_row, r, sm, out, out_page);
-  else if (r <= 4 * kWave)
-    select_core<NT, PAGES, 4>(ld, bt_row, r, sm, out, out_page);
+  const int A = sel_waves<NT>(cap);
+  const int per = (r + kWave * A - 1) / (kWave * A);
+  if (per <= 1)
+    select_core<NT, PAGES, 1>(ld, bt_row, r, A, sm, out, out_page);
+  else if (per <= 2)
+    select_core<NT, PAGES, 2>(ld, bt_row, r, A, sm, out, out_page);
+  else if (per <= 4)
+    select_core<NT, PAGES, 4>(ld, bt_row, r, A, sm, out, out_page);
+  else if (per <= 8)
+    select_core<NT, PAGES, 8>(ld, bt_row, r, A, sm, out, out_page);
   else
-    select_core<NT, PAGES, kSelKeysPerLane>(ld, bt_row, r, sm, out, out_page);
+    select_core<NT, PAGES, kSelKeysPerLane>(ld, bt_row, r, A, sm, out, out_page);
 }
 
 }  // namespace msa
