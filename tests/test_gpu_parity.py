@@ -194,6 +194,50 @@ def test_selection_kernel_exact_on_ties(dev):
             assert np.array_equal(got[b, g], ref), (b, g, got[b, g], ref)
 
 
+@pytest.mark.parametrize("mb,blocks", [
+    (256, (16, 64, 65, 200, 255)),                  # one wave, 1, 2 and 4 keys per lane
+    (257, (16, 64, 65, 256)),                       # one wave (64 threads) past the one-wave table limit
+    (1500, (100, 130, 300, 600, 1200, 1499)),       # two waves (128 threads), 1 to 16 keys per lane
+    (3000, (16, 200, 257, 600, 1100, 2100, 2999)),  # four waves, 1, 2, 4, 8 and 16 keys per lane
+    (8192, (300, 2100, 4097, 8191)),                # eight waves
+])
+def test_selection_waves_and_keys_per_lane(dev, mb, blocks):
+    """msa_block_topk alone across the selection's layouts (its workgroup has
+    one wave per 1,024 blocks of the table): the waves that hold the keys and
+    the keys per lane follow the table width and the row length.
+    Integer-valued scores (ties, -0 and +0) and a row of equal scores; ids must
+    equal the oracle's selection of the same fp32 values bit for bit."""
+    msa = _msa()
+    rng = np.random.default_rng(mb)
+    lens = [128 * n + 1 for n in blocks] + [0]
+    S = len(lens)
+    bs = rng.integers(-3, 3, size=(S, 4, mb)).astype(np.float32)
+    bs[0, 1, ::3] = -0.0
+    bs[-2, 2, :] = 1.0  # all equal: the lowest ids win
+    shape = msa.MsaShape(S, 1, 16, 4, mb, 1, 1, 1, 0.1, 1.0, 1.0, 1.0)
+    d_bs = torch.from_numpy(bs).to(dev)
+    d_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+    d_sel = torch.empty(S, 4, 16, dtype=torch.int32, device=dev)
+    _say(f"[select] table {mb} blocks, rows {list(blocks)}")
+    msa.msa_block_topk(shape, d_len, d_bs, d_sel)
+    got = d_sel.cpu().numpy()
+    for b, L in enumerate(lens):
+        nbv = (L - 1) // 128 + 1 if L else 0
+        for g in range(4):
+            ref = oracle.select(bs[b, g].astype(np.float64), nbv)
+            assert np.array_equal(got[b, g], ref), (mb, b, g, got[b, g], ref)
+
+
+@pytest.mark.parametrize("mb,blocks", [(257, (17, 200, 256)), (3000, (300, 700, 1500, 2999))])
+def test_fused_selection_waves(dev, mb, blocks):
+    """The fused selection of the attention launch on the same layouts (a table
+    just past the one-wave limit; four selection waves with 2, 4, 8 and 16 keys
+    per lane), every row against the oracle and bit-equal to the unfused trio."""
+    w = synth.make_workload(seq_lens=[128 * n + 5 for n in blocks], max_blocks_per_seq=mb, plant=4, zipf=1.1,
+                            layout="paged", seed=mb, device=dev)
+    check_workload(w, label=f"fused selection, table {mb} blocks")
+
+
 def test_fused_selection_on_ties(dev):
     """All index queries zero: every block score is 0 (ties everywhere, -0 and
     +0 alike), so the fused path must keep blocks 0..14 plus the recent block
@@ -216,9 +260,9 @@ def test_fused_selection_on_ties(dev):
 def test_max_context_fused(dev, idx):
     """The largest supported row: 16,384 blocks (2M tokens) next to a short
     one, with FP8 or NVFP4 index keys.  The fused selection then runs 16
-    active waves, takes the maximum of their thresholds and ranks the merged
-    candidates; checked on every row against the oracle (block scores, ids,
-    outputs)."""
+    selection waves of 16 keys per lane, which exchange their lane-bests for
+    the threshold, and ranks the merged candidates; checked on every row
+    against the oracle (block scores, ids, outputs)."""
     w = synth.make_workload(seq_lens=[16384 * 128 - 5, 3000], max_blocks_per_seq=16384, plant=8, zipf=1.1,
                             layout="paged", idx_dtype=idx, seed=45, device=dev)
     check_workload(w, label=f"max context 16,384 blocks, {idx} index keys")
