@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kMqThreads) void scan_mq_kernel(const uint8_t* __re
   constexpr int kKeyRow = FMT == kIdxFp8 ? kDim : FMT == kIdxBf16 ? kDim * 2 : kDim / 2;
   constexpr int kPage = kBlock * kKeyRow;             // 16, 32 or 8 KB
   constexpr int kLoads = kPage / 1024 / kMqWaves;     // 1 KB wave-loads per wave and block (2, 4 or 1)
+  static_assert(FMT != kIdxNvfp4 || kLoads == 1, "NVFP4: one wave-load, so one pair of group scales, per wave");
   constexpr int kRowB = kDim * 2;                     // bytes per token of a bf16 key row in LDS
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[kRowChunk * kLdsRow];     // 68 KB
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kBlock * kRowB];       // 2 x 32 KB, bf16 keys
