@@ -738,31 +738,44 @@ def test_shared_b32_128k_config(dev):
     check_rows(P, out2.cpu().numpy(), sel2.cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["plain", "plain_bf16_split", "shared_fp8", "shared_nvfp4_wide"])
+@pytest.mark.parametrize("case", ["plain", "plain_bf16_split", "shared_fp8", "shared_nvfp4_wide", "multi_query",
+                                  "block_major"])
 def test_graph_capture_replays(dev, case):
     """msa_decode (or msa_decode_shared) captured in a HIP graph: every replay
     (with eager work and synchronisation in between) equals the eager result
     bit for bit.  plain_bf16_split: bf16 K/V and few (row, group) pairs, so
     the kept blocks are split over workgroups whose partials the last one
     merges; the arrival counters are zeroed by the captured scan, with no
-    memset in the graph."""
+    memset in the graph.  multi_query: 192 rows of 64 query tokens, more
+    (row, group) pairs than two per compute unit, so the step is three launches
+    (scan, selection, attention); block_major: msa_decode_block_major on the
+    same shape (inversion, block-major partials, merge)."""
     msa = _msa()
     if case == "plain":
         w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", seed=43, device=dev)
     elif case == "plain_bf16_split":
         w = synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", kv_dtype="bf16",
                                 idx_dtype="bf16", seed=45, device=dev)
+    elif case in ("multi_query", "block_major"):
+        w = synth.make_workload(seq_lens=[20000, 9000, 4000], q_len=64, plant=3, layout="paged", seed=47,
+                                shared_bias_iq=True, device=dev)
+        assert w.rows * 4 > 2 * torch.cuda.get_device_properties(0).multi_processor_count
     else:
         n = 8 if case == "shared_fp8" else 16
         w = synth.make_workload(seq_lens=[9000 + 97 * i for i in range(n)], plant=3, layout="paged", seed=44,
                                 idx_dtype="fp8" if case == "shared_fp8" else "nvfp4", share=(n, 40), device=dev)
     shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
-    share = msa.MsaPrefixShare.from_workload(w) if case != "plain" else None
+    share = msa.MsaPrefixShare.from_workload(w) if case.startswith("shared") else None
     out, sel = msa.alloc_outputs(w)
-    ws = msa.alloc_workspace(shape, dev)
+    if case == "block_major":
+        ws = torch.empty(msa.msa_block_major_workspace_size(shape), dtype=torch.uint8, device=dev)
+    else:
+        ws = msa.alloc_workspace(shape, dev)
 
     def call(stream=None):
-        if share is None:
+        if case == "block_major":
+            msa.msa_decode_block_major(shape, cache, w.q, w.iq, out, sel, ws, stream=stream)
+        elif share is None:
             msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws, stream=stream)
         else:
             msa.msa_decode_shared(shape, cache, share, w.q, w.iq, out, sel, ws, stream=stream)
