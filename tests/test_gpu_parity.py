@@ -802,6 +802,44 @@ def test_graph_capture_replays(dev, case):
         torch.cuda.synchronize()
 
 
+def test_concurrent_streams(dev):
+    """Two steps in flight at once on two streams (default priority), each with
+    its own workspace: a batch-4 decode with NVFP4 K/V (two launches), a bf16
+    batch whose kept blocks are split and merged through arrival counters, and
+    a 64-token chunk (three launches).  The library holds no device state of
+    its own on this path, so every result equals the eager, one-at-a-time
+    result bit for bit."""
+    msa = _msa()
+    ws_ = [
+        synth.make_workload(seq_lens=[12000, 5000, 300, 0], plant=3, layout="paged", seed=50, device=dev),
+        synth.make_workload(seq_lens=[9000, 700], plant=2, layout="paged", kv_dtype="bf16", idx_dtype="bf16",
+                            seed=51, device=dev),
+        synth.make_workload(seq_lens=[20000, 9000, 4000], q_len=64, plant=3, layout="paged", seed=52,
+                            device=dev),
+    ]
+    runs = []
+    for w in ws_:
+        shape, cache = msa.MsaShape.from_workload(w), msa.MsaCache.from_workload(w)
+        out, sel = msa.alloc_outputs(w)
+        ws = msa.alloc_workspace(shape, dev)
+        msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws)
+        torch.cuda.synchronize()
+        runs.append((w, shape, cache, out, sel, ws, out.clone(), sel.clone()))
+    streams = [torch.cuda.Stream() for _ in runs]
+    for rep in range(3):
+        for (w, shape, cache, out, sel, ws, _, _) in runs:
+            out.fill_(float("nan"))
+            sel.fill_(-7)
+        torch.cuda.synchronize()
+        for s, (w, shape, cache, out, sel, ws, _, _) in zip(streams, runs):
+            s.wait_stream(torch.cuda.current_stream())
+            msa.msa_decode(shape, cache, w.q, w.iq, out, sel, ws, stream=s)
+        torch.cuda.synchronize()
+        for (w, shape, cache, out, sel, ws, ref_out, ref_sel) in runs:
+            assert torch.equal(out, ref_out), (w.name, rep)
+            assert torch.equal(sel, ref_sel), (w.name, rep)
+
+
 def test_split_merge_from_any_workspace(dev):
     """bf16 K/V with few (row, group) pairs: msa_decode's kept-block split
     merges each pair's partials in the workgroup that finishes last, counting
