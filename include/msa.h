@@ -60,6 +60,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* hipStream_t.  C callers compile with ROCm's include directory and
+ * -D__HIP_PLATFORM_AMD__ (hipcc sets both); the header is C99. */
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus

@@ -305,3 +305,44 @@ def test_binding_constants_match_header():
                  "MSA_ERR_INVALID_ARGUMENT", "MSA_ERR_UNSUPPORTED", "MSA_ERR_WORKSPACE_TOO_SMALL", "MSA_ERR_HIP"):
         m = re.search(name + r" = (\d+)", hdr)
         assert m and int(m.group(1)) == getattr(msa, name), name
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/msa.h as a C99 caller sees it: a C program that includes it
+    compiles with warnings as errors, links against libmsa.so and gets the
+    same workspace size as the binding for the headline shape (host-only
+    entry points: no GPU is touched)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "msa.h"
+int main(void) {
+  msa_shape s = {32, 1, MSA_NUM_Q_HEADS, MSA_NUM_KV_HEADS, 1024, 32768, MSA_KV_NVFP4, MSA_IDX_FP8_E4M3,
+                 0.08838834764831845f, 1.0f, 1.0f, 1.0f};
+  size_t ws = msa_workspace_size(&s);
+  msa_shape bad = s;
+  bad.num_q_heads = 3;
+  size_t none = msa_workspace_size(&bad);
+  printf("%zu %zu %s %s\n", ws, none, msa_status_string(MSA_OK), msa_status_string(MSA_ERR_INVALID_ARGUMENT));
+  return ws > 0 && none == 0 ? 0 : 1;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(msa.LIB_PATH)
+    include = os.path.join(os.path.dirname(libdir), "include")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    # the header takes hipStream_t from the HIP runtime API header, which a C
+    # compiler reads with the platform macro set
+    subprocess.check_call([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", include,
+                           "-I", os.path.join(rocm, "include"), str(src), "-o", str(exe), msa.LIB_PATH,
+                           f"-Wl,-rpath,{libdir}"])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    shape = msa.MsaShape(32, 1, 16, 4, 1024, 32768, msa.MSA_KV_NVFP4, msa.MSA_IDX_FP8_E4M3, 0.08838834764831845,
+                         1.0, 1.0, 1.0)
+    assert int(out[0]) == msa.msa_workspace_size(shape)
+    assert out[1:] == ["0", "MSA_OK", "MSA_ERR_INVALID_ARGUMENT"]
