@@ -1,5 +1,6 @@
-"""CPU checks of the benchmark's committed measurement records: the traffic
-records match the scan sources as checked out, on any machine."""
+"""CPU checks of the benchmark: its committed measurement records (the
+traffic records match the scan sources as checked out, on any machine) and
+its refusal of runs on several GPUs."""
 import json
 import os
 import sys
@@ -37,3 +38,15 @@ def test_committed_traffic_records():
             stale.append(f)
     if stale:
         pytest.skip(f"records taken before the last scan change (bench reports traffic null): {stale}")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: asked for several it exits with status 2 and
+    says why, before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "more than one GPU" in (r.stdout + r.stderr)
